@@ -1,0 +1,422 @@
+"""Pins of the FP64 oracle against what the pages and the mathematics fix.
+
+No GPU.  Each pin is independent of the oracle's own code: printed values,
+closed forms, library routines (torch float64), brute force on tiny inputs and
+finite differences.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import HParams
+from tests.common import clone_inputs, oracle_inputs, tiny_inputs
+from workloads import get_workload, make_inputs
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- printed values
+
+def _disjoint_inputs(g, K=7):
+    """One block of K slots, every slot a pair of disjoint saturated distributions."""
+    V = g["vocab"]
+    s = g["saturation_logit"]
+    z = np.zeros((K, V)); z[:, g["draft_hot"]] = s
+    t = np.zeros((K, V)); t[:, g["teacher_hot"]] = s
+    return oracle.Inputs(B=1, N=1, K=K, z=z, target_ids=np.full(K, g["draft_hot"]),
+                         eval_mask=np.ones(K), aligned=t)
+
+
+def test_disjoint_saturated_raw_l1_is_two():
+    g = _gold("disjoint_saturated.json")
+    inp = _disjoint_inputs(g)
+    fw = oracle.forward(inp, HParams())
+    assert np.allclose(fw.l1, g["expected"]["raw_l1"], atol=1e-12)
+    assert np.allclose(0.5 * fw.l1, g["expected"]["total_variation"], atol=1e-12)
+    assert np.allclose(fw.accept, g["expected"]["accept"], atol=1e-12)
+    tau_num, tau_den = fw.pairs["dspark tau"]
+    assert tau_den == 1 and tau_num == pytest.approx(g["expected"]["tau_first_slot_rejected"])
+    # the trained term is the raw L1 at weight 0.9 (not 1.8 x TV, not 0.9 x TV)
+    hp = HParams(ce_alpha=0.0, l1_alpha=0.9, confidence_alpha=0.0, loss_decay_gamma=None)
+    fw = oracle.forward(inp, hp)
+    assert fw.loss == pytest.approx(0.9 * 2.0 * 7, rel=1e-12)
+
+
+def test_recipe_constants_match_workloads():
+    g = _gold("qwen3_8b_recipe.json")
+    for idx in (2, 3):
+        wl = get_workload(idx)
+        assert wl.K == g["block_size"] and wl.gamma == g["loss_decay_gamma"]
+        assert wl.r == g["markov_rank"] and wl.Vd == g["vocab_size"] == wl.Vt
+    assert HParams().loss_decay_gamma == g["loss_decay_gamma"]
+
+
+def test_loss_defaults_match_page():
+    g = _gold("loss_defaults.json")
+    hp = HParams()
+    assert (hp.ce_alpha, hp.l1_alpha, hp.confidence_alpha, hp.loss_decay_gamma) == \
+        (g["ce_alpha"], g["l1_alpha"], g["confidence_alpha"], g["loss_decay_gamma"])
+
+
+def test_probability_tensor_size_pins_vocab_layout():
+    g = _gold("probability_tensor_size.json")
+    V = get_workload(3).Vd
+    gib = g["batch"] * g["num_blocks"] * g["block_size"] * V * g["bytes_per_element"] / 2**30
+    assert round(gib, 2) == g["gib_printed"]
+
+
+# ----------------------------------------------------------------- closed forms
+
+def test_identical_distributions_accept_one_tau_k_plus_one():
+    inp = tiny_inputs(V=40)
+    t = inp.H_t @ inp.LM.T
+    e = inp.W1[inp.prev_ids.astype(int)]
+    same = clone_inputs(inp, aligned=t.copy(), z=t - e @ inp.W2.T, H_t=None, LM=None)
+    fw = oracle.forward(same, HParams())
+    assert np.max(np.abs(fw.l1)) < 1e-12
+    assert np.allclose(fw.accept, 1.0)
+    tau_num, tau_den = fw.pairs["dspark tau"]
+    assert tau_num / tau_den == pytest.approx(inp.K + 1, abs=1e-9)
+
+
+@pytest.mark.parametrize("a,expected", [(0.8, 4.1611392), (0.5, 1.9921875), (0.0, 1.0), (1.0, 8.0)])
+def test_tau_constant_accept_geometric_series(a, expected):
+    K = 7
+    closed = 1.0 + sum(a ** k for k in range(1, K + 1))       # geometric series
+    assert closed == pytest.approx(expected, abs=1e-7)
+    acc_num, acc_den, tau_num, tau_den = oracle.accept_report(np.full(K, a), np.ones(K), None, 1, 1, K)
+    assert tau_den == 1 and tau_num == pytest.approx(closed, abs=1e-12)
+    assert acc_den == K and acc_num == pytest.approx(K * a)
+
+
+def test_decay_weights_properties():
+    K, gamma = 7, 4.0
+    w = oracle.decay_weights(K, gamma)
+    assert w[0] == 1.0
+    ratios = w[1:] / w[:-1]
+    assert np.allclose(ratios, math.exp(-1.0 / gamma), rtol=1e-15)
+    assert w[4] == pytest.approx(1.0 / math.e, rel=1e-15)      # k = gamma
+    assert w.sum() == pytest.approx((1 - math.exp(-K / gamma)) / (1 - math.exp(-1 / gamma)), rel=1e-14)
+    assert np.all(oracle.decay_weights(K, None) == 1.0)
+    assert np.all(oracle.decay_weights(K, 0.0) == 1.0)
+    # the weights the loss actually applies: w_k / w_0 = exp(-k / gamma) within each block
+    fw = oracle.forward(tiny_inputs(V=16, N=2), HParams(loss_decay_gamma=gamma))
+    wb = fw.w.reshape(-1, K)
+    assert np.allclose(wb[:, 1:] / wb[:, :-1], math.exp(-1.0 / gamma), rtol=1e-15)
+
+
+def test_l1_range_and_accept_relation():
+    inp = tiny_inputs(V=50, N=4)
+    fw = oracle.forward(inp, HParams())
+    v = fw.m != 0
+    assert np.all(fw.l1[v] >= 0) and np.all(fw.l1[v] <= 2.0)
+    assert np.allclose(fw.accept[v], 1 - 0.5 * fw.l1[v])
+    assert np.all(np.abs(fw.S[v]) <= 1.0 + 1e-12)
+
+
+def test_softmax_gradient_rows_sum_to_zero():
+    inp = tiny_inputs(V=30)
+    gr = oracle.backward(inp, HParams(), grad_scale=0.37)
+    assert np.max(np.abs(gr.dz.sum(axis=1))) < 1e-14
+
+
+def test_loss_decomposition_into_pairs():
+    inp = tiny_inputs(V=30, N=4)
+    hp = HParams(ce_alpha=0.3, l1_alpha=0.6, confidence_alpha=0.7)
+    fw = oracle.forward(inp, hp)
+    ce, l1, cf = (fw.pairs[k][0] for k in ("dspark ce", "dspark l1", "dspark confidence"))
+    assert fw.loss == pytest.approx(0.3 * ce + 0.6 * l1 + 0.7 * cf, rel=1e-14)
+    for k in ("dspark ce", "dspark l1", "dspark confidence"):
+        assert fw.pairs[k][1] == fw.num_tokens
+
+
+# ----------------------------------------------------------------- masks and invariants
+
+def test_cumprod_mask_example():
+    # [1,1,0,1,1,1,1] -> [1,1,0,0,0,0,0]: the supervised part is a contiguous prefix
+    m = oracle.effective_mask(np.array([1, 1, 0, 1, 1, 1, 1]), None, 1, 1, 7)
+    assert m.tolist() == [1, 1, 0, 0, 0, 0, 0]
+    m = oracle.effective_mask(np.array([1, 1, 1, 1, 1, 1, 1, 0.5, 0, 0, 0, 0, 0, 0]),
+                              np.array([0, 1]), 1, 2, 7)
+    assert m.tolist() == [0] * 7 + [1] + [0] * 6
+
+
+def test_all_masked_gives_zero_loss_and_tokens():
+    inp = tiny_inputs(V=20)
+    inp = clone_inputs(inp, eval_mask=np.zeros_like(inp.eval_mask))
+    fw = oracle.forward(inp, HParams())
+    assert fw.loss == 0.0 and fw.num_tokens == 0
+    gr = oracle.backward(inp, HParams())
+    assert not np.any(gr.dz) and not np.any(gr.dW1) and not np.any(gr.dW2)
+
+
+def test_garbage_in_masked_rows_changes_nothing():
+    prefix = np.array([1, 1, 1, 0, 1, 0, 0] + [1] * 7 + [0] * 7)
+    inp = tiny_inputs(V=24, prefix=prefix)
+    fw = oracle.forward(inp, HParams())
+    gr = oracle.backward(inp, HParams())
+    m = fw.m
+    bad = clone_inputs(inp)
+    bad.z[m == 0] = np.nan
+    bad.z[np.nonzero(m == 0)[0][::2]] = np.inf
+    bad.prev_ids[m == 0] = -1
+    bad.target_ids[m == 0] = -1
+    bad.h_d[m == 0] = np.nan
+    fw2 = oracle.forward(bad, HParams())
+    gr2 = oracle.backward(bad, HParams())
+    assert fw2.loss == fw.loss and fw2.pairs == fw.pairs
+    assert np.array_equal(gr2.dz, gr.dz) and np.array_equal(gr2.dW1, gr.dW1)
+    assert np.array_equal(gr2.dW2, gr.dW2) and np.array_equal(gr2.dW_c, gr.dW_c)
+    assert fw2.conf_logit[m == 0].tolist() == [0.0] * int((m == 0).sum())
+
+
+def test_data_parallel_split_is_additive():
+    inp = tiny_inputs(V=24, B=2, N=2)
+    hp = HParams()
+    fw = oracle.forward(inp, hp)
+    gr = oracle.backward(inp, hp, grad_scale=0.5)
+    half = inp.R // 2
+    parts = []
+    for sl, bsl in ((slice(0, half), slice(0, 2)), (slice(half, None), slice(2, None))):
+        p = clone_inputs(inp, B=1, z=inp.z[sl], target_ids=inp.target_ids[sl],
+                         eval_mask=inp.eval_mask[sl], block_keep=inp.block_keep[bsl],
+                         prev_ids=inp.prev_ids[sl], H_t=inp.H_t[sl], h_d=inp.h_d[sl])
+        parts.append((oracle.forward(p, hp), oracle.backward(p, hp, grad_scale=0.5)))
+    assert fw.loss == pytest.approx(sum(f.loss for f, _ in parts), rel=1e-13)
+    assert fw.num_tokens == sum(f.num_tokens for f, _ in parts)
+    for k in fw.pairs:
+        assert fw.pairs[k][0] == pytest.approx(sum(f.pairs[k][0] for f, _ in parts), rel=1e-13)
+        assert fw.pairs[k][1] == sum(f.pairs[k][1] for f, _ in parts)
+    assert np.allclose(gr.dW2, sum(g.dW2 for _, g in parts), rtol=1e-12, atol=1e-15)
+    assert np.allclose(gr.dW1, sum(g.dW1 for _, g in parts), rtol=1e-12, atol=1e-15)
+    assert np.allclose(gr.dW_c, sum(g.dW_c for _, g in parts), rtol=1e-12, atol=1e-15)
+
+
+def test_row_chunking_does_not_change_result():
+    inp = tiny_inputs(V=24, N=4)
+    a = oracle.forward(inp, HParams(), row_chunk=1)
+    b = oracle.forward(inp, HParams(), row_chunk=1000)
+    assert a.loss == pytest.approx(b.loss, rel=1e-14)
+
+
+def test_teacher_free_mode():
+    inp = tiny_inputs(V=24)
+    nt = clone_inputs(inp, H_t=None, LM=None, h_d=None, W_c=None, b_c=None)
+    with pytest.raises(ValueError):
+        oracle.forward(nt, HParams())                       # l1_alpha defaults to 0.9
+    fw = oracle.forward(nt, HParams(l1_alpha=0.0))
+    assert not np.any(fw.l1)
+    with pytest.raises(ValueError):                          # confidence head without teacher
+        oracle.forward(clone_inputs(inp, H_t=None, LM=None), HParams(l1_alpha=0.0))
+
+
+# ----------------------------------------------------------------- library routines
+
+def _t(x):
+    return torch.tensor(x, dtype=torch.float64)
+
+
+def test_ce_bce_l1_bias_against_torch_library():
+    inp = tiny_inputs(V=45, N=4)
+    fw = oracle.forward(inp, HParams())
+    v = np.nonzero(fw.m)[0]
+    e = inp.W1[inp.prev_ids[v].astype(int)]
+    # Markov bias == W2(W1[prev]) -- TorchSpec #132 "Testing"
+    bias = F.linear(_t(e), _t(inp.W2))
+    zp = _t(inp.z[v]) + bias
+    ce = F.cross_entropy(zp, torch.tensor(inp.target_ids[v].astype(np.int64)), reduction="none")
+    assert np.allclose(fw.ce[v], ce.numpy(), rtol=1e-13)
+    t = F.linear(_t(inp.H_t[v]), _t(inp.LM))
+    l1 = (F.softmax(zp, -1) - F.softmax(t, -1)).abs().sum(-1)
+    assert np.allclose(fw.l1[v], l1.numpy(), rtol=1e-12)
+    acc = (1 - 0.5 * l1).clamp(0, 1)
+    c = F.linear(torch.cat([_t(inp.h_d[v]), _t(e)], 1), _t(inp.W_c), _t(inp.b_c)).squeeze(1)
+    assert np.allclose(fw.conf_logit[v], c.numpy(), rtol=1e-12)
+    bce = F.binary_cross_entropy_with_logits(c, acc, reduction="none")
+    assert np.allclose(fw.bce[v], bce.numpy(), rtol=1e-12)
+
+
+def test_reduces_to_plain_cross_entropy():
+    inp = tiny_inputs(V=33, N=2)
+    plain = clone_inputs(inp, W1=None, W2=None, prev_ids=None, h_d=None, W_c=None, b_c=None)
+    fw = oracle.forward(plain, HParams(ce_alpha=1.0, l1_alpha=0.0, confidence_alpha=0.0,
+                                       loss_decay_gamma=None))
+    ref = F.cross_entropy(_t(inp.z), torch.tensor(inp.target_ids.astype(np.int64)), reduction="sum")
+    assert fw.loss == pytest.approx(float(ref), rel=1e-13)
+
+
+def _torch_loss(inp, hp, grad_scale):
+    """The objective assembled from torch float64 library ops, for autograd."""
+    B, N, K = inp.B, inp.N, inp.K
+    m = torch.cumprod(torch.tensor(inp.eval_mask != 0, dtype=torch.float64).view(B, N, K), 2)
+    if inp.block_keep is not None:
+        m = m * torch.tensor(inp.block_keep != 0, dtype=torch.float64).view(B, N, 1)
+    m = m.reshape(-1)
+    z = _t(inp.z).requires_grad_(); W1 = _t(inp.W1).requires_grad_(); W2 = _t(inp.W2).requires_grad_()
+    Wc = _t(inp.W_c).requires_grad_(); bc = _t(inp.b_c).requires_grad_(); hd = _t(inp.h_d).requires_grad_()
+    e = W1[torch.tensor(inp.prev_ids.astype(np.int64))]
+    zp = z + F.linear(e, W2)
+    tl = F.linear(_t(inp.H_t), _t(inp.LM))
+    ce = F.cross_entropy(zp, torch.tensor(inp.target_ids.astype(np.int64)), reduction="none")
+    l1 = (F.softmax(zp, -1) - F.softmax(tl, -1)).abs().sum(-1)
+    acc = (1 - 0.5 * l1).clamp(0, 1).detach()
+    c = F.linear(torch.cat([hd, e], 1), Wc, bc).squeeze(1)
+    bce = F.binary_cross_entropy_with_logits(c, acc, reduction="none")
+    w = m * torch.exp(-(torch.arange(inp.R) % K).double() / hp.loss_decay_gamma)
+    loss = (w * (hp.ce_alpha * ce + hp.l1_alpha * l1 + hp.confidence_alpha * bce)).sum()
+    (loss * grad_scale).backward()
+    return loss, dict(dz=z.grad, dW1=W1.grad, dW2=W2.grad, dW_c=Wc.grad, db_c=bc.grad, dh_d=hd.grad)
+
+
+def test_gradients_against_torch_autograd():
+    inp = tiny_inputs(V=37, N=4, prefix=np.array([1] * 7 + [1, 1, 1, 0, 0, 0, 0] + [1] * 7 + [1] * 7))
+    hp = HParams(ce_alpha=0.2, l1_alpha=0.8, confidence_alpha=0.9)
+    loss, ref = _torch_loss(inp, hp, 0.25)
+    fw = oracle.forward(inp, hp)
+    assert fw.loss == pytest.approx(float(loss.detach()), rel=1e-13)
+    gr = oracle.backward(inp, hp, grad_scale=0.25)
+    for k in ref:
+        mine = getattr(gr, k)
+        assert np.allclose(mine, ref[k].numpy().reshape(mine.shape), rtol=1e-10, atol=1e-14), k
+
+
+# ----------------------------------------------------------------- brute force
+
+def _brute_row(z_row, t_row, y, e, W2, hd, Wc, bc):
+    V = len(z_row)
+    zp = [z_row[v] + sum(W2[v][j] * e[j] for j in range(len(e))) for v in range(V)]
+    mz = max(zp); mt = max(t_row)
+    sz = sum(math.exp(x - mz) for x in zp); st = sum(math.exp(x - mt) for x in t_row)
+    p = [math.exp(x - mz) / sz for x in zp]; q = [math.exp(x - mt) / st for x in t_row]
+    ce = -math.log(p[y])
+    l1 = sum(abs(p[v] - q[v]) for v in range(V))
+    acc = min(1.0, max(0.0, 1 - l1 / 2))
+    feat = list(hd) + list(e)
+    c = sum(Wc[i] * feat[i] for i in range(len(feat))) + bc
+    sg = 1 / (1 + math.exp(-c))
+    bce = -(acc * math.log(sg) + (1 - acc) * math.log(1 - sg))
+    return ce, l1, acc, c, bce
+
+
+def test_brute_force_tiny_vocab():
+    inp = tiny_inputs(V=12, H=4, r=3, N=2)
+    fw = oracle.forward(inp, HParams())
+    T = inp.H_t @ inp.LM.T
+    for row in range(inp.R):
+        if not fw.m[row]:
+            continue
+        e = inp.W1[int(inp.prev_ids[row])]
+        ce, l1, acc, c, bce = _brute_row(inp.z[row], T[row], int(inp.target_ids[row]), e,
+                                         inp.W2, inp.h_d[row], inp.W_c[0], inp.b_c[0])
+        assert fw.ce[row] == pytest.approx(ce, rel=1e-12)
+        assert fw.l1[row] == pytest.approx(l1, rel=1e-12)
+        assert fw.accept[row] == pytest.approx(acc, rel=1e-12)
+        assert fw.conf_logit[row] == pytest.approx(c, rel=1e-12)
+        assert fw.bce[row] == pytest.approx(bce, rel=1e-10)
+    # tau by explicit loops over each block
+    K = inp.K
+    tau_sum = 0.0
+    for blk in range(inp.B * inp.N):
+        run, tau = 1.0, 1.0
+        for k in range(K):
+            r = blk * K + k
+            run *= fw.accept[r] if fw.m[r] else 0.0
+            tau += run
+        tau_sum += tau
+    assert fw.pairs["dspark tau"][0] == pytest.approx(tau_sum, rel=1e-13)
+
+
+def test_finite_differences_every_element():
+    """Central differences of the forward loss match the backward, element by element.
+
+    The BCE label (accept) is detached (reading R6), so the differenced loss
+    holds the label fixed at its unperturbed value.
+    """
+    inp = tiny_inputs(V=10, H=4, r=3, N=1, K=4, B=1)
+    hp = HParams(ce_alpha=0.3, l1_alpha=0.7, confidence_alpha=0.5)
+    hp_nc = HParams(ce_alpha=0.3, l1_alpha=0.7, confidence_alpha=0.0)
+    gs = 0.8
+    gr = oracle.backward(inp, hp, grad_scale=gs)
+    accept0 = oracle.forward(inp, hp).accept.copy()
+
+    def loss_of(x):
+        f = oracle.forward(x, hp)
+        frozen = np.sum(f.w * oracle.bce_with_logits(f.conf_logit, accept0))
+        return gs * (oracle.forward(x, hp_nc).loss + hp.confidence_alpha * frozen)
+
+    h = 1e-6
+    for name in ("z", "W1", "W2", "W_c", "b_c", "h_d"):
+        base = getattr(inp, name)
+        fd = np.zeros_like(base, dtype=np.float64)
+        for idx in np.ndindex(base.shape):
+            xp = clone_inputs(inp); getattr(xp, name)[idx] += h
+            xm = clone_inputs(inp); getattr(xm, name)[idx] -= h
+            fd[idx] = (loss_of(xp) - loss_of(xm)) / (2 * h)
+        ana = {"z": gr.dz, "W1": gr.dW1, "W2": gr.dW2, "W_c": gr.dW_c, "b_c": gr.db_c,
+               "h_d": gr.dh_d}[name]
+        assert np.allclose(ana, fd, rtol=1e-5, atol=1e-8), name
+
+
+# ----------------------------------------------------------------- planted mistakes
+
+@pytest.mark.parametrize("mutation", ["tv_half", "no_decay", "sign_flip", "no_cumprod", "label_grad"])
+def test_pins_catch_planted_oracle_mistakes(monkeypatch, mutation):
+    """Each plausible mistake planted in the oracle makes at least one pin fail."""
+    import oracle.dspark_oracle as od
+    if mutation == "tv_half":
+        orig = od._row_terms
+        def bad(inp, rows):
+            t = orig(inp, rows); t["l1"] = 0.5 * t["l1"]; return t
+        monkeypatch.setattr(od, "_row_terms", bad)
+        pin = test_disjoint_saturated_raw_l1_is_two
+    elif mutation == "no_decay":
+        monkeypatch.setattr(od, "decay_weights", lambda K, g: np.ones(K))
+        pin = test_decay_weights_properties
+    elif mutation == "sign_flip":
+        orig = od._row_terms
+        def bad(inp, rows):
+            t = orig(inp, rows); t["s"] = -t["s"]; t["S"] = -t["S"]; return t
+        monkeypatch.setattr(od, "_row_terms", bad)
+        pin = test_gradients_against_torch_autograd
+    elif mutation == "no_cumprod":
+        def bad_mask(ev, keep, B, N, K):
+            m = (np.asarray(ev).reshape(B, N, K) != 0).astype(np.int64)
+            if keep is not None:
+                m = m * (np.asarray(keep).reshape(B, N, 1) != 0)
+            return m.reshape(-1)
+        monkeypatch.setattr(od, "effective_mask", bad_mask)
+        monkeypatch.setattr(oracle, "effective_mask", bad_mask)
+        pin = test_cumprod_mask_example
+    else:
+        orig_sig = od.sigmoid
+        monkeypatch.setattr(od, "sigmoid", lambda c: orig_sig(c) + 0.01)
+        pin = test_finite_differences_every_element
+    with pytest.raises(AssertionError):
+        pin()
+
+
+# ----------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_small_workloads_run_in_oracle(idx):
+    wl = get_workload(idx)
+    d = make_inputs(wl, "cpu")
+    inp = oracle_inputs(d)
+    fw = oracle.forward(inp, HParams())
+    assert np.isfinite(fw.loss) and fw.num_tokens == int(fw.m.sum()) > 0
+    v = fw.m != 0
+    assert np.all(fw.l1[v] <= 2) and np.all(fw.accept[v] >= 0)
