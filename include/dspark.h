@@ -1,0 +1,173 @@
+/*
+ * dspark.h -- C ABI of the fused DSpark draft-training loss for AMD gfx950.
+ *
+ * What is computed (the pages, cited by title and section):
+ *   Megatron-Bridge API page "bridge.training.post_training.dspark.loss",
+ *   module docstring and `dspark_loss`: the draft is trained with three
+ *   position-weighted terms -- cross-entropy against the teacher-forced next
+ *   token, the raw probability L1 ||p_draft - p_target||_1 (no 1/2), and a
+ *   confidence BCE against the label 1 - 0.5 * L1 -- each weighted by
+ *   exp(-k / loss_decay_gamma); acceptance is accept = 1 - 0.5 * L1 and
+ *   tau = sum_k cumprod(accept)_k + 1.  The loss is an unnormalised numerator,
+ *   returned with the supervised token count and [numerator, denominator]
+ *   report pairs (section "Return contract").
+ *   NeMo-RL design doc "DSpark Auxiliary Heads": the draft logits are first
+ *   corrected by the Markov head, bias = markov_w2 . markov_w1[prev_id] on
+ *   valid slots ("Inputs and Outputs"); the confidence head is a linear
+ *   projection of [hidden ; markov embedding] plus a bias ("Checkpoint
+ *   Contract" shapes).  TorchSpec pull request #132, PR description: the
+ *   teacher is the target lm_head applied to the target's final hidden state.
+ *
+ * Conventions shared by every entry point:
+ *   - R = batch * num_blocks * block_size rows, in (b, n, k) order; the vocab
+ *     axis is innermost.  All tensors are dense row-major.
+ *   - Every pointer in the structs below is DEVICE memory owned by the caller.
+ *     The library allocates nothing and keeps no pointer after a call returns.
+ *   - Every device pointer must be 16-byte aligned (DSPARK_ERR_ALIGN).
+ *   - Validation is on the host and synchronous; after it the work is enqueued
+ *     on `stream` (a hipStream_t; NULL = the legacy default stream) and the
+ *     call returns without synchronising.  Data-dependent problems (ids out of
+ *     range on a supervised slot, a non-finite loss term) set bits in the
+ *     device word `flags` instead of failing.
+ *   - Supervised slot mask m = block_keep_mask[b,n] * cumprod_k(eval_mask != 0)
+ *     (API page, `DSparkForwardOutput.eval_mask`: a block supervises a
+ *     contiguous prefix; TorchSpec #132: realised as a cumprod).  Rows with
+ *     m = 0 are never read beyond their mask and ids: NaN/Inf there changes
+ *     nothing (Megatron-Bridge PR #5241, merge note: scrub before reducing).
+ *   - Calls on one workspace must not overlap; distinct workspaces are
+ *     independent.  dspark_loss_bwd must follow dspark_loss_fwd on the same
+ *     workspace, same stream order, with the inputs unchanged.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t, passed as an opaque pointer so this header needs no HIP headers. */
+typedef void *dspark_stream_t;
+
+/* Element types of the float inputs / of the draft-logit gradient. */
+enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
+
+/* Status codes (0 = success).  dspark_status_string() describes each. */
+enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_NULL = -1,       /* a pointer the call needs is NULL */
+  DSPARK_ERR_SHAPE = -2,      /* a dimension is <= 0, not a multiple of 8 where required, or inconsistent */
+  DSPARK_ERR_DTYPE = -3,      /* dtype / grad_dtype not DSPARK_F32 or DSPARK_BF16 */
+  DSPARK_ERR_NO_TARGET = -4,  /* L1 term or confidence head requested without a teacher */
+  DSPARK_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than dspark_workspace_size() */
+  DSPARK_ERR_ALIGN = -6,      /* a device pointer is not 16-byte aligned */
+  DSPARK_ERR_HIP = -7         /* a HIP launch failed; see dspark_last_hip_error() */
+};
+
+/* Bits of the device word dspark_fwd_out.flags (OR-ed, never cleared by bwd). */
+enum {
+  DSPARK_FLAG_TARGET_ID_RANGE = 1u, /* a supervised slot has target id outside [0, draft_vocab) */
+  DSPARK_FLAG_PREV_ID_RANGE = 2u,   /* a supervised slot has prev id outside [0, target_vocab) */
+  DSPARK_FLAG_NONFINITE = 4u,       /* a supervised slot produced a non-finite loss term */
+  DSPARK_FLAG_NO_TEACHER = 8u       /* CE-only call: L1 is zero by definition, so accept = 1 */
+};
+
+typedef struct {
+  int64_t batch;          /* B */
+  int64_t num_blocks;     /* N: sampled anchor blocks per sample */
+  int64_t block_size;     /* K: draft positions per anchor */
+  int64_t draft_vocab;    /* Vd: logits, L1 and target ids live here; multiple of 8 */
+  int64_t target_vocab;   /* Vt: rows of markov_w1, range of prev ids (may differ from Vd) */
+  int64_t hidden;         /* H: inner size of lm_head / target_hidden; multiple of 8 (0 if unused) */
+  int64_t conf_hidden;    /* Hd: confidence-head hidden size; 0 = no confidence head */
+  int64_t markov_rank;    /* r: multiple of 8; 0 = no Markov head */
+  int32_t with_markov_conf; /* 1: confidence input is [hidden ; markov embedding] (proj [1, Hd + r]) */
+  int32_t dtype;          /* DSPARK_F32 or DSPARK_BF16: type of every float input */
+  int32_t grad_dtype;     /* type written to d_draft_logits */
+  int32_t reserved;
+} dspark_shape;
+
+/* `dspark_loss` keyword arguments (API page, defaults 0.1 / 0.9 / 1.0 / 4.0). */
+typedef struct {
+  float ce_alpha;
+  float l1_alpha;          /* weight of the RAW L1 (no 1/2) */
+  float confidence_alpha;
+  float loss_decay_gamma;  /* <= 0 disables the decay (the page's None) */
+} dspark_hparams;
+
+/* Forward inputs; shapes use R = B*N*K.  Pointers not needed by the shape may be NULL. */
+typedef struct {
+  const void *draft_logits;          /* [R, Vd] dtype, required */
+  const int32_t *target_ids;         /* [R], required; read on supervised slots only */
+  const uint8_t *eval_mask;          /* [R] nonzero = loss-enabled, required */
+  const uint8_t *block_keep_mask;    /* [B*N] nonzero = kept, or NULL = all kept */
+  const int32_t *prev_ids;           /* [R] ids into markov_w1 rows; required when r > 0 */
+  const void *markov_w1;             /* [Vt, r] dtype (markov_head.markov_w1.weight) */
+  const void *markov_w2;             /* [Vd, r] dtype (markov_head.markov_w2.weight) */
+  const void *target_hidden;         /* [R, H] dtype, target final hidden AFTER its final norm */
+  const void *lm_head;               /* [Vd, H] dtype, target lm_head rows of the draft vocab */
+  const void *aligned_target_logits; /* [R, Vd] dtype: teacher logits given directly (wins over the two above) */
+  const void *conf_hidden;           /* [R, Hd] dtype: confidence-head hidden input */
+  const void *conf_w;                /* [1, Hd (+ r)] dtype (confidence_head.proj.weight) */
+  const void *conf_b;                /* [1] dtype (confidence_head.proj.bias) */
+} dspark_inputs;
+
+typedef struct {
+  double *loss;          /* [1] unnormalised weighted numerator (required) */
+  int64_t *num_tokens;   /* [1] supervised slot count (required) */
+  double *pairs;         /* [10] (num, den) x {ce, l1, confidence, accept rate, tau}; every
+                            den is an exact integer (required) */
+  float *accept_rate;    /* [R] per-slot accept, 1 on unsupervised slots, or NULL */
+  float *row_terms;      /* [R, 4] (ce, l1, bce, confidence logit) per slot, 0 when unsupervised, or NULL */
+  uint32_t *flags;       /* [1] DSPARK_FLAG_* bits, OR-ed in (required; caller zeroes it) */
+} dspark_fwd_out;
+
+typedef struct {
+  void *d_draft_logits;  /* [R, Vd] grad_dtype, required; 0 on unsupervised slots */
+  float *d_markov_w1;    /* [Vt, r], required when r > 0 */
+  float *d_markov_w2;    /* [Vd, r], required when r > 0 */
+  float *d_conf_w;       /* [1, Hd (+ r)], required with a confidence head */
+  float *d_conf_b;       /* [1], required with a confidence head */
+  float *d_conf_hidden;  /* [R, Hd] or NULL */
+} dspark_bwd_out;
+
+/* Bytes of device workspace fwd + bwd need for `shape` (0 on an invalid shape).
+ * It holds the fp32 teacher logits, the fp32 Markov-corrected draft logits,
+ * per-tile softmax statistics, per-row state and the backward scratch. */
+size_t dspark_workspace_size(const dspark_shape *shape);
+
+/* Forward: loss numerator, token count, report pairs, optional per-row terms.
+ * Teacher: aligned_target_logits if non-NULL, else target_hidden x lm_head^T
+ * if both are non-NULL (and H > 0), else none -- then only CE is allowed
+ * (l1_alpha == 0 and no confidence head, else DSPARK_ERR_NO_TARGET), the L1
+ * output is zeros (API page, `_ce_and_l1_per_token`) and FLAG_NO_TEACHER is set.
+ * The workspace must stay untouched until the matching dspark_loss_bwd. */
+int dspark_loss_fwd(const dspark_shape *shape, const dspark_hparams *hp, const dspark_inputs *in,
+                    void *workspace, size_t workspace_bytes, dspark_fwd_out *out,
+                    dspark_stream_t stream);
+
+/* Backward of `loss` with upstream gradient `grad_scale` (Megatron-Core scales
+ * by 1 / global num_tokens).  Outputs are overwritten, not accumulated.  The
+ * teacher gets no gradient (API page: the teacher is "already detached"), and
+ * the BCE label is treated as a constant. */
+int dspark_loss_bwd(const dspark_shape *shape, const dspark_hparams *hp, const dspark_inputs *in,
+                    void *workspace, size_t workspace_bytes, float grad_scale,
+                    dspark_bwd_out *out, dspark_stream_t stream);
+
+/* Acceptance report alone (API page, `_acceptance_report`): from per-slot
+ * accept rates [R] (fp32), eval_mask [R] and block_keep_mask [B*N] (or NULL),
+ * writes out4 = {sum m*accept, sum m, sum over kept blocks of
+ * (1 + sum_k prod_{j<=k} m_j accept_j), number of kept blocks} as doubles. */
+int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,
+                         const float *accept_rate, const uint8_t *eval_mask,
+                         const uint8_t *block_keep_mask, double *out4, dspark_stream_t stream);
+
+const char *dspark_status_string(int status);
+const char *dspark_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */

@@ -1,0 +1,331 @@
+// C ABI of the DSpark loss library: host-side validation, workspace layout and
+// the launch sequences of the forward, backward and acceptance report.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dspark.h"
+#include "internal.h"
+#include "rowwise.h"
+
+namespace dspark {
+namespace {
+
+thread_local char g_hip_err[256] = "";
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Dims {
+  int64_t B, N, K, R, Vd, Vt, H, Hd, r, nstat, splits, conf_chunks, F;
+  int dtype, gdtype, esize;
+  bool markov, conf, conf_markov;
+};
+
+struct Layout {
+  size_t Zp, T, sz, st, E, mask, rowf, ghi, glo, g32, dEpart, dE, confpart, total;
+};
+
+constexpr int kRowArrays = 10;  // float row arrays of RowState (w .. dcoef)
+
+int make_dims(const dspark_shape* sh, Dims* d) {
+  if (!sh) return DSPARK_ERR_NULL;
+  if (sh->dtype != DSPARK_F32 && sh->dtype != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (sh->grad_dtype != DSPARK_F32 && sh->grad_dtype != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (sh->batch <= 0 || sh->num_blocks <= 0 || sh->block_size <= 0) return DSPARK_ERR_SHAPE;
+  if (sh->draft_vocab <= 0 || sh->draft_vocab % 8) return DSPARK_ERR_SHAPE;
+  if (sh->markov_rank < 0 || sh->markov_rank % 8) return DSPARK_ERR_SHAPE;
+  if (sh->hidden < 0 || sh->hidden % 8) return DSPARK_ERR_SHAPE;
+  if (sh->conf_hidden < 0) return DSPARK_ERR_SHAPE;
+  if (sh->markov_rank > 0 && sh->target_vocab <= 0) return DSPARK_ERR_SHAPE;
+  if (sh->draft_vocab > (int64_t{1} << 26) || sh->hidden > (int64_t{1} << 20) ||
+      sh->markov_rank > 4096)
+    return DSPARK_ERR_SHAPE;  // keeps every tile's byte offsets below 2^31
+  d->B = sh->batch; d->N = sh->num_blocks; d->K = sh->block_size;
+  d->R = d->B * d->N * d->K;
+  if (d->R > (int64_t{1} << 31) - 1) return DSPARK_ERR_SHAPE;
+  d->Vd = sh->draft_vocab; d->Vt = sh->target_vocab; d->H = sh->hidden;
+  d->Hd = sh->conf_hidden; d->r = sh->markov_rank;
+  d->dtype = sh->dtype; d->gdtype = sh->grad_dtype;
+  d->esize = d->dtype == DSPARK_BF16 ? 2 : 4;
+  d->markov = d->r > 0;
+  d->conf = d->Hd > 0;
+  d->conf_markov = d->conf && d->markov && sh->with_markov_conf != 0;
+  d->nstat = (d->Vd + 255) / 256;
+  const int64_t nM = (d->R + 255) / 256;
+  int64_t sp = 640 / nM;
+  const int64_t kmax = 2 * gemm_kpad(d->Vd, d->esize) / (8 * 64);  // at least 8 K-tiles per split
+  if (sp > kmax) sp = kmax;
+  if (sp > 32) sp = 32;
+  if (sp < 1) sp = 1;
+  d->splits = d->markov ? sp : 0;
+  d->conf_chunks = d->R < 256 ? static_cast<int>(d->R) : 256;
+  d->F = d->Hd + (d->conf_markov ? d->r : 0);
+  return DSPARK_OK;
+}
+
+Layout make_layout(const Dims& d) {
+  Layout L{};
+  size_t o = 0;
+  const size_t RV = static_cast<size_t>(d.R) * d.Vd;
+  L.Zp = o; o = up(o + RV * 4);
+  L.T = o; o = up(o + RV * 4);
+  L.sz = o; o = up(o + static_cast<size_t>(d.R) * d.nstat * 8);
+  L.st = o; o = up(o + static_cast<size_t>(d.R) * d.nstat * 8);
+  L.E = o; o = up(o + static_cast<size_t>(d.R) * d.r * d.esize);
+  L.mask = o; o = up(o + d.R);
+  L.rowf = o; o = up(o + static_cast<size_t>(d.R) * 4 * kRowArrays);
+  L.ghi = L.glo = L.g32 = 0;
+  if (d.dtype == DSPARK_BF16) {
+    if (d.gdtype != DSPARK_BF16) { L.ghi = o; o = up(o + RV * 2); }
+    L.glo = o; o = up(o + RV * 2);
+  } else if (d.gdtype != DSPARK_F32) {
+    L.g32 = o; o = up(o + RV * 4);
+  }
+  L.dEpart = o; o = up(o + static_cast<size_t>(d.splits) * d.R * d.r * 4);
+  L.dE = o; o = up(o + static_cast<size_t>(d.R) * d.r * 4);
+  L.confpart = o; o = up(o + static_cast<size_t>(d.conf_chunks) * (d.F + 1) * 4);
+  L.total = o;
+  return L;
+}
+
+RowState row_state(char* ws, const Layout& L, const Dims& d) {
+  RowState s;
+  float* f = reinterpret_cast<float*>(ws + L.rowf);
+  s.mask = reinterpret_cast<uint8_t*>(ws + L.mask);
+  s.w = f + 0 * d.R; s.lse_z = f + 1 * d.R; s.lse_t = f + 2 * d.R; s.l1 = f + 3 * d.R;
+  s.S = f + 4 * d.R; s.ce = f + 5 * d.R; s.accept = f + 6 * d.R; s.conf = f + 7 * d.R;
+  s.bce = f + 8 * d.R; s.dcoef = f + 9 * d.R;
+  return s;
+}
+
+inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return DSPARK_OK;
+  std::snprintf(g_hip_err, sizeof(g_hip_err), "%s", hipGetErrorString(e));
+  return DSPARK_ERR_HIP;
+}
+
+#define DSPARK_TRY(expr)                          \
+  do {                                            \
+    const hipError_t e_ = (expr);                 \
+    if (e_ != hipSuccess) return hip_status(e_);  \
+  } while (0)
+
+enum Teacher { kNone = 0, kHidden = 1, kAligned = 2 };
+
+int check_inputs(const Dims& d, const dspark_hparams* hp, const dspark_inputs* in, Teacher* t) {
+  if (!hp || !in) return DSPARK_ERR_NULL;
+  if (!in->draft_logits || !in->target_ids || !in->eval_mask) return DSPARK_ERR_NULL;
+  if (d.markov && (!in->prev_ids || !in->markov_w1 || !in->markov_w2)) return DSPARK_ERR_NULL;
+  if (d.conf && (!in->conf_hidden || !in->conf_w || !in->conf_b)) return DSPARK_ERR_NULL;
+  if (in->aligned_target_logits) *t = kAligned;
+  else if (in->target_hidden && in->lm_head && d.H > 0) *t = kHidden;
+  else *t = kNone;
+  if (*t == kNone && (hp->l1_alpha != 0.f || d.conf)) return DSPARK_ERR_NO_TARGET;
+  const void* ptrs[] = {in->draft_logits, in->target_ids, in->eval_mask, in->block_keep_mask,
+                        in->prev_ids, in->markov_w1, in->markov_w2, in->target_hidden,
+                        in->lm_head, in->aligned_target_logits, in->conf_hidden, in->conf_w,
+                        in->conf_b};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+}  // namespace
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+size_t dspark_workspace_size(const dspark_shape* shape) {
+  Dims d;
+  if (make_dims(shape, &d) != DSPARK_OK) return 0;
+  return make_layout(d).total;
+}
+
+const char* dspark_status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_NULL: return "a required pointer is NULL";
+    case DSPARK_ERR_SHAPE: return "invalid or inconsistent dimensions";
+    case DSPARK_ERR_DTYPE: return "dtype must be DSPARK_F32 or DSPARK_BF16";
+    case DSPARK_ERR_NO_TARGET: return "L1 term or confidence head requested without a teacher";
+    case DSPARK_ERR_WORKSPACE: return "workspace NULL or smaller than dspark_workspace_size()";
+    case DSPARK_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case DSPARK_ERR_HIP: return "HIP launch failure (see dspark_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+const char* dspark_last_hip_error(void) { return g_hip_err; }
+
+int dspark_loss_fwd(const dspark_shape* shape, const dspark_hparams* hp, const dspark_inputs* in,
+                    void* workspace, size_t workspace_bytes, dspark_fwd_out* out,
+                    dspark_stream_t stream) {
+  Dims d;
+  int st = make_dims(shape, &d);
+  if (st) return st;
+  Teacher teacher;
+  st = check_inputs(d, hp, in, &teacher);
+  if (st) return st;
+  if (!out || !out->loss || !out->num_tokens || !out->pairs || !out->flags) return DSPARK_ERR_NULL;
+  if (misaligned(workspace) || misaligned(out->accept_rate) || misaligned(out->row_terms))
+    return DSPARK_ERR_ALIGN;
+  const Layout L = make_layout(d);
+  if (!workspace || workspace_bytes < L.total) return DSPARK_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const RowState rs = row_state(ws, L, d);
+  float* Zp = reinterpret_cast<float*>(ws + L.Zp);
+  float* T = reinterpret_cast<float*>(ws + L.T);
+  float2* sz = reinterpret_cast<float2*>(ws + L.sz);
+  float2* stt = reinterpret_cast<float2*>(ws + L.st);
+  void* E = ws + L.E;
+
+  DSPARK_TRY(launch_prep_rows(d.R, static_cast<int>(d.K), in->eval_mask, in->block_keep_mask,
+                              in->target_ids, in->prev_ids, d.Vd, d.Vt, d.markov,
+                              hp->loss_decay_gamma, teacher == kNone ? DSPARK_FLAG_NO_TEACHER : 0u,
+                              rs.mask, rs.w, out->flags, s));
+  if (d.markov)
+    DSPARK_TRY(launch_gather_embed(d.dtype, d.R, d.r, d.Vt, in->prev_ids, rs.mask, in->markov_w1,
+                                   E, s));
+
+  // corrected draft logits z' = z + E W2^T (fp32) with per-tile softmax statistics
+  {
+    Operand A{}, B{};
+    A.seg[0] = A.seg[1] = E; A.kseg = d.r; A.kpad = gemm_kpad(d.r, d.esize); A.ld = d.r;
+    A.mcontig = 0; A.nseg = 1;
+    B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.r; B.kpad = A.kpad; B.ld = d.r;
+    B.mcontig = 0; B.nseg = 1;
+    EpiParams ep{};
+    ep.C = Zp; ep.ldc = d.Vd; ep.X = in->draft_logits; ep.ldx = d.Vd; ep.stats = sz;
+    ep.nstat = d.nstat;
+    DSPARK_TRY(launch_gemm(d.dtype, EPI_STATS, d.R, d.Vd, A, B, 1, ep, s));
+  }
+  // teacher logits T (fp32) with the same statistics
+  if (teacher != kNone) {
+    Operand A{}, B{};
+    EpiParams ep{};
+    ep.C = T; ep.ldc = d.Vd; ep.stats = stt; ep.nstat = d.nstat;
+    if (teacher == kHidden) {
+      A.seg[0] = A.seg[1] = in->target_hidden; A.kseg = d.H; A.kpad = gemm_kpad(d.H, d.esize);
+      A.ld = d.H; A.nseg = 1;
+      B.seg[0] = B.seg[1] = in->lm_head; B.kseg = d.H; B.kpad = A.kpad; B.ld = d.H; B.nseg = 1;
+    } else {
+      A.nseg = B.nseg = 1;  // K = 0: T = aligned logits
+      ep.X = in->aligned_target_logits; ep.ldx = d.Vd;
+    }
+    DSPARK_TRY(launch_gemm(d.dtype, EPI_STATS, d.R, d.Vd, A, B, 1, ep, s));
+  }
+  DSPARK_TRY(launch_l1_sweep(d.R, d.Vd, Zp, T, sz, stt, d.nstat, rs.mask, in->target_ids,
+                             teacher != kNone, rs, s));
+  DSPARK_TRY(launch_finalize_rows(d.dtype, d.R, d.Hd, d.r, d.conf_markov, d.conf,
+                                  in->conf_hidden, E, in->conf_w, in->conf_b, rs,
+                                  out->accept_rate, out->row_terms, out->flags, hp->ce_alpha,
+                                  hp->l1_alpha, hp->confidence_alpha, s));
+  DSPARK_TRY(launch_reduce_fwd(d.R, d.B * d.N, static_cast<int>(d.K), rs, in->eval_mask,
+                               in->block_keep_mask, hp->ce_alpha, hp->l1_alpha,
+                               d.conf ? hp->confidence_alpha : 0.f, out->loss, out->num_tokens,
+                               out->pairs, s));
+  return DSPARK_OK;
+}
+
+int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const dspark_inputs* in,
+                    void* workspace, size_t workspace_bytes, float grad_scale,
+                    dspark_bwd_out* out, dspark_stream_t stream) {
+  Dims d;
+  int st = make_dims(shape, &d);
+  if (st) return st;
+  Teacher teacher;
+  st = check_inputs(d, hp, in, &teacher);
+  if (st) return st;
+  if (!out || !out->d_draft_logits) return DSPARK_ERR_NULL;
+  if (d.markov && (!out->d_markov_w1 || !out->d_markov_w2)) return DSPARK_ERR_NULL;
+  if (d.conf && (!out->d_conf_w || !out->d_conf_b)) return DSPARK_ERR_NULL;
+  if (misaligned(workspace) || misaligned(out->d_draft_logits) || misaligned(out->d_markov_w1) ||
+      misaligned(out->d_markov_w2) || misaligned(out->d_conf_hidden))
+    return DSPARK_ERR_ALIGN;
+  const Layout L = make_layout(d);
+  if (!workspace || workspace_bytes < L.total) return DSPARK_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const RowState rs = row_state(ws, L, d);
+  const float* Zp = reinterpret_cast<const float*>(ws + L.Zp);
+  const float* T = reinterpret_cast<const float*>(ws + L.T);
+  void* E = ws + L.E;
+  const float g = grad_scale;
+  const float c_a = d.conf ? hp->confidence_alpha : 0.f;
+
+  // G = dloss/dz' (also dloss/dz); operand copies for the MFMA products
+  bf16_t* ghi = nullptr;
+  bf16_t* glo = nullptr;
+  float* g32 = nullptr;
+  const void* gA = nullptr;  // first K segment of the G operand
+  if (d.dtype == DSPARK_BF16) {
+    ghi = d.gdtype == DSPARK_BF16 ? nullptr : reinterpret_cast<bf16_t*>(ws + L.ghi);
+    glo = reinterpret_cast<bf16_t*>(ws + L.glo);
+    gA = ghi ? static_cast<const void*>(ghi) : out->d_draft_logits;
+  } else {
+    g32 = d.gdtype == DSPARK_F32 ? nullptr : reinterpret_cast<float*>(ws + L.g32);
+    gA = g32 ? static_cast<const void*>(g32) : out->d_draft_logits;
+  }
+  DSPARK_TRY(launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs, teacher != kNone,
+                               g, hp->ce_alpha, hp->l1_alpha, out->d_draft_logits, ghi, glo, g32,
+                               s));
+  const int nseg = d.dtype == DSPARK_BF16 ? 2 : 1;
+  if (d.markov) {
+    float* dEpart = reinterpret_cast<float*>(ws + L.dEpart);
+    float* dE = reinterpret_cast<float*>(ws + L.dE);
+    {  // dE partials = G . W2 over vocabulary splits
+      Operand A{}, B{};
+      A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.Vd; A.kpad = gemm_kpad(d.Vd, d.esize);
+      A.ld = d.Vd; A.mcontig = 0; A.nseg = nseg;
+      B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.Vd; B.kpad = A.kpad; B.ld = d.r;
+      B.mcontig = 1; B.nseg = nseg;
+      EpiParams ep{};
+      ep.C = dEpart; ep.ldc = d.r;
+      DSPARK_TRY(launch_gemm(d.dtype, EPI_PARTIAL, d.R, d.r, A, B, static_cast<int>(d.splits), ep,
+                             s));
+    }
+    DSPARK_TRY(launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits), dEpart, rs,
+                                d.conf_markov, in->conf_w, d.Hd, g, c_a, dE, s));
+    DSPARK_TRY(launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
+    DSPARK_TRY(launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE, out->d_markov_w1, s));
+    {  // dW2 = G^T . E (reduction over rows)
+      Operand A{}, B{};
+      A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.R; A.kpad = gemm_kpad(d.R, d.esize);
+      A.ld = d.Vd; A.mcontig = 1; A.nseg = nseg;
+      B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = A.kpad; B.ld = d.r; B.mcontig = 1;
+      B.nseg = nseg;
+      EpiParams ep{};
+      ep.C = out->d_markov_w2; ep.ldc = d.r;
+      DSPARK_TRY(launch_gemm(d.dtype, EPI_STORE, d.Vd, d.r, A, B, 1, ep, s));
+    }
+  }
+  if (d.conf) {
+    float* part = reinterpret_cast<float*>(ws + L.confpart);
+    DSPARK_TRY(launch_conf_bwd(d.dtype, d.R, d.Hd, d.r, d.conf_markov, in->conf_hidden, E,
+                               in->conf_w, rs, g, c_a, part, d.conf_chunks, out->d_conf_w,
+                               out->d_conf_b, out->d_conf_hidden, s));
+  }
+  return DSPARK_OK;
+}
+
+int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,
+                         const float* accept_rate, const uint8_t* eval_mask,
+                         const uint8_t* block_keep_mask, double* out4, dspark_stream_t stream) {
+  if (!accept_rate || !eval_mask || !out4) return DSPARK_ERR_NULL;
+  if (batch <= 0 || num_blocks <= 0 || block_size <= 0) return DSPARK_ERR_SHAPE;
+  if (misaligned(accept_rate) || misaligned(eval_mask) || misaligned(out4) ||
+      misaligned(block_keep_mask))
+    return DSPARK_ERR_ALIGN;
+  return hip_status(launch_accept_report(batch * num_blocks, static_cast<int>(block_size),
+                                         accept_rate, eval_mask, block_keep_mask, out4,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

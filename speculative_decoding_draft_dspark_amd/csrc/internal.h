@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (capi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// One operand of C[M,N] = A[M,K] . B[N,K]^T, possibly made of two K segments.
+// The K axis is padded: segment s covers k in [s*kpad, s*kpad + kseg), and
+// k in [s*kpad + kseg, (s+1)*kpad) reads as zero.  kpad must be a multiple of
+// the GEMM's BK (64 for bf16, 32 for fp32) and equal for A and B.
+//   kcontig: element (i, k) of segment s at seg[s][i * ld + k]  (row i K-contiguous)
+//   mcontig: element (i, k) of segment s at seg[s][k * ld + i]  (row i strided)
+// Byte offsets i*ld + k (resp. k*ld + i) within one 256-row tile must stay below 2^31.
+struct Operand {
+  const void* seg[2];
+  int64_t kseg;
+  int64_t kpad;
+  int64_t ld;
+  int mcontig;
+  int nseg;
+};
+
+// Padded K extent of an operand segment for the GEMM of element size `esize`.
+inline int64_t gemm_kpad(int64_t k, int esize) {
+  const int64_t bk = esize == 2 ? 64 : 32;
+  return (k + bk - 1) / bk * bk;
+}
+
+enum Epilogue { EPI_STATS = 0, EPI_STORE = 1, EPI_PARTIAL = 2 };
+
+struct EpiParams {
+  float* C;            // fp32 [M, ldc] (EPI_PARTIAL: [splits, M, ldc])
+  int64_t ldc;
+  const void* X;       // EPI_STATS: optional addend [M, ldx] of the operand dtype
+  int64_t ldx;
+  float2* stats;       // EPI_STATS: [M, nstat] (tile max, tile sum of exp(x - max))
+  int64_t nstat;
+};
+
+// dtype: 0 = fp32, 1 = bf16.  splits > 1 only with EPI_PARTIAL.
+hipError_t launch_gemm(int dtype, int epi, int64_t M, int64_t N, const Operand& A,
+                       const Operand& B, int splits, const EpiParams& ep, hipStream_t s);
+
+}  // namespace dspark

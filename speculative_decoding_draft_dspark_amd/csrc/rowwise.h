@@ -1,0 +1,60 @@
+// Launchers of the row-wise DSpark loss kernels (see rowwise.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef uint16_t bf16_t;
+
+// Per-row state saved by the forward pass for the backward pass.
+struct RowState {
+  uint8_t* mask;   // supervised slot (prefix rule x block keep)
+  float* w;        // decay weight exp(-k / gamma) on supervised slots, else 0
+  float* lse_z;    // log-sum-exp of the corrected draft logits
+  float* lse_t;    // log-sum-exp of the teacher logits
+  float* l1;       // sum |p - q|
+  float* S;        // sum p sign(p - q)
+  float* ce;       // lse_z - z'_y
+  float* accept;   // clamp(1 - l1 / 2, 0, 1); 1 on unsupervised slots
+  float* conf;     // confidence logit
+  float* bce;      // BCE(conf, accept)
+  float* dcoef;    // sigmoid(conf) - accept
+};
+
+hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t s);
+hipError_t launch_prep_rows(int64_t R, int K, const uint8_t* eval, const uint8_t* keep,
+                            const int32_t* tid, const int32_t* prev, int64_t Vd, int64_t Vt,
+                            int has_markov, float gamma, uint32_t set_bits, uint8_t* mask, float* w,
+                            uint32_t* flags, hipStream_t s);
+hipError_t launch_gather_embed(int dtype, int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
+                               const uint8_t* mask, const void* W1, void* E, hipStream_t s);
+hipError_t launch_l1_sweep(int64_t R, int64_t V, const float* Zp, const float* Tt,
+                           const float2* sz, const float2* st, int64_t nstat, const uint8_t* mask,
+                           const int32_t* tid, int has_teacher, RowState rs, hipStream_t s);
+hipError_t launch_finalize_rows(int dtype, int64_t R, int64_t Hd, int64_t rank,
+                                int with_markov_conf, int has_conf, const void* hd, const void* E,
+                                const void* Wc, const void* bc, RowState rs, float* accept_out,
+                                float* row_terms, uint32_t* flags, float ce_a, float l1_a,
+                                float c_a, hipStream_t s);
+hipError_t launch_reduce_fwd(int64_t R, int64_t nblk, int K, RowState rs, const uint8_t* eval,
+                             const uint8_t* keep, float ce_a, float l1_a, float c_a, double* loss,
+                             int64_t* num_tokens, double* pairs, hipStream_t s);
+hipError_t launch_accept_report(int64_t nblk, int K, const float* accept, const uint8_t* eval,
+                                const uint8_t* keep, double* out4, hipStream_t s);
+hipError_t launch_grad_sweep(int grad_dtype, int64_t R, int64_t V, const float* Zp,
+                             const float* Tt, const int32_t* tid, RowState rs, int has_teacher,
+                             float g, float ce_a, float l1_a, void* dz, bf16_t* ghi, bf16_t* glo,
+                             float* g32, hipStream_t s);
+hipError_t launch_de_reduce(int dtype, int64_t R, int64_t rank, int splits, const float* part,
+                            RowState rs, int conf_markov, const void* Wc, int64_t Hd, float g,
+                            float c_a, float* dE, hipStream_t s);
+hipError_t launch_dw1_scatter(int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
+                              const uint8_t* mask, const float* dE, float* dW1, hipStream_t s);
+hipError_t launch_conf_bwd(int dtype, int64_t R, int64_t Hd, int64_t rank, int conf_markov,
+                           const void* hd, const void* E, const void* Wc, RowState rs, float g,
+                           float c_a, float* part, int chunks, float* dWc, float* db, float* dh,
+                           hipStream_t s);
+
+}  // namespace dspark

@@ -1,0 +1,578 @@
+// Row-wise kernels of the DSpark loss (gfx950): masks, softmax/L1 sweeps,
+// per-row terms, deterministic reductions and the backward helpers.
+//
+// Definitions (cited by page title and section):
+//   Megatron-Bridge API page "bridge.training.post_training.dspark.loss":
+//     module docstring (ce, raw L1 without 1/2, confidence BCE against the
+//     label 1 - 0.5 L1, decay exp(-k / gamma), accept = 1 - 0.5 L1,
+//     tau = sum_k cumprod(accept)_k + 1), `DSparkForwardOutput.eval_mask`
+//     (contiguous supervised prefix), `_acceptance_report`, `_pair`.
+//   Megatron-Bridge pull request #5241, merge note: masked rows are selected
+//     away before any reduction and accept is clamped to [0, 1].
+//   TorchSpec pull request #132, PR description: prefix mask as a cumprod.
+//   NeMo-RL "DSpark Auxiliary Heads": Markov embedding W1[prev], confidence
+//     logit = proj([hidden ; embedding]) + bias, zero on invalid slots.
+#include "common.h"
+#include "rowwise.h"
+
+namespace dspark {
+
+// ---------------------------------------------------------------- fill
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
+                     static_cast<uint32_t*>(p), n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- masks
+
+// m_r = keep[b,n] * prod_{j<=k} [eval_j != 0]; w_r = m_r * exp(-k / gamma).
+__device__ __forceinline__ bool slot_supervised(const uint8_t* eval, const uint8_t* keep, int64_t r,
+                                                int K) {
+  const int64_t blk = r / K;
+  const int k = static_cast<int>(r - blk * K);
+  if (keep && !keep[blk]) return false;
+  for (int j = 0; j <= k; ++j)
+    if (!eval[blk * K + j]) return false;
+  return true;
+}
+
+__global__ void prep_rows_kernel(int64_t R, int K, const uint8_t* eval, const uint8_t* keep,
+                                 const int32_t* tid, const int32_t* prev, int64_t Vd, int64_t Vt,
+                                 int has_markov, float gamma, uint32_t set_bits, uint8_t* mask,
+                                 float* w, uint32_t* flags) {
+  const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (r >= R) return;
+  if (r == 0 && set_bits) atomicOr(flags, set_bits);
+  const bool m = slot_supervised(eval, keep, r, K);
+  const int k = static_cast<int>(r % K);
+  mask[r] = m ? 1 : 0;
+  w[r] = m ? (gamma > 0.f ? expf(-static_cast<float>(k) / gamma) : 1.f) : 0.f;
+  if (m) {
+    uint32_t f = 0;
+    const int32_t y = tid[r];
+    if (y < 0 || y >= Vd) f |= 1u;
+    if (has_markov) {
+      const int32_t pv = prev[r];
+      if (pv < 0 || pv >= Vt) f |= 2u;
+    }
+    if (f) atomicOr(flags, f);
+  }
+}
+
+hipError_t launch_prep_rows(int64_t R, int K, const uint8_t* eval, const uint8_t* keep,
+                            const int32_t* tid, const int32_t* prev, int64_t Vd, int64_t Vt,
+                            int has_markov, float gamma, uint32_t set_bits, uint8_t* mask, float* w,
+                            uint32_t* flags, hipStream_t s) {
+  hipLaunchKernelGGL(prep_rows_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)), dim3(256), 0,
+                     s, R, K, eval, keep, tid, prev, Vd, Vt, has_markov, gamma, set_bits, mask, w, flags);
+  return hipGetLastError();
+}
+
+// E[r, :] = W1[prev_r, :] on supervised slots with an in-range id, else 0.
+// One thread per 16-byte chunk.
+template <typename T>
+__global__ void gather_embed_kernel(int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
+                                    const uint8_t* mask, const T* W1, T* E) {
+  constexpr int KPC = Elem<T>::kPerChunk;
+  const int64_t chunks = rank / KPC;
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= R * chunks) return;
+  const int64_t r = i / chunks, c = i - r * chunks;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (mask[r]) {
+    const int32_t pv = prev[r];
+    if (pv >= 0 && pv < Vt) v = reinterpret_cast<const uint4*>(W1 + pv * rank)[c];
+  }
+  reinterpret_cast<uint4*>(E + r * rank)[c] = v;
+}
+
+hipError_t launch_gather_embed(int dtype, int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
+                               const uint8_t* mask, const void* W1, void* E, hipStream_t s) {
+  const int kpc = dtype == 1 ? 8 : 4;
+  const int64_t n = R * (rank / kpc);
+  if (n <= 0) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>((n + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(gather_embed_kernel<bf16_t>, grid, dim3(256), 0, s, R, rank, Vt, prev, mask,
+                       static_cast<const bf16_t*>(W1), static_cast<bf16_t*>(E));
+  else
+    hipLaunchKernelGGL(gather_embed_kernel<float>, grid, dim3(256), 0, s, R, rank, Vt, prev, mask,
+                       static_cast<const float*>(W1), static_cast<float*>(E));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- L1 sweep
+
+constexpr int kSweepThreads = 256;
+
+// log-sum-exp of a row from its per-tile (max, sum exp(x - max)) statistics.
+// The same routine (same order) is used for the draft and the teacher row, so
+// equal statistics give bitwise-equal results.
+__device__ float merge_lse(const float2* st, int64_t n, float* fscr, double* dscr) {
+  float m = -INFINITY;
+  for (int64_t i = threadIdx.x; i < n; i += kSweepThreads) m = fmaxf(m, st[i].x);
+  const float M = block_max<kSweepThreads>(m, fscr);
+  double acc = 0.0;
+  if (M != -INFINITY)
+    for (int64_t i = threadIdx.x; i < n; i += kSweepThreads) {
+      const float2 t = st[i];
+      if (t.x != -INFINITY) acc += static_cast<double>(t.y) * static_cast<double>(dexp(t.x - M));
+    }
+  const double L = block_sum<kSweepThreads>(acc, dscr);
+  return M + static_cast<float>(log(L));
+}
+
+// Per supervised row: lse of the corrected draft logits and of the teacher
+// logits, then L1 = sum |p - q|, S = sum p sign(p - q) and CE = lse_z - z'_y.
+__global__ __launch_bounds__(kSweepThreads) void l1_sweep_kernel(
+    int64_t V, const float* Zp, const float* Tt, const float2* sz, const float2* st, int64_t nstat,
+    const uint8_t* mask, const int32_t* tid, int has_teacher, float* lse_z, float* lse_t,
+    float* l1, float* S, float* ce) {
+  __shared__ float fscr[kSweepThreads / kWave];
+  __shared__ double dscr[kSweepThreads / kWave];
+  const int64_t r = blockIdx.x;
+  if (!mask[r]) {
+    if (threadIdx.x == 0) { lse_z[r] = 0.f; lse_t[r] = 0.f; l1[r] = 0.f; S[r] = 0.f; ce[r] = 0.f; }
+    return;
+  }
+  const float lz = merge_lse(sz + r * nstat, nstat, fscr, dscr);
+  float lt = 0.f;
+  double sum_l1 = 0.0, sum_s = 0.0;
+  if (has_teacher) {
+    lt = merge_lse(st + r * nstat, nstat, fscr, dscr);
+    const float4* z4 = reinterpret_cast<const float4*>(Zp + r * V);
+    const float4* t4 = reinterpret_cast<const float4*>(Tt + r * V);
+    const int64_t n4 = V / 4;
+    float a1 = 0.f, a2 = 0.f;
+#pragma unroll 4
+    for (int64_t c = threadIdx.x; c < n4; c += kSweepThreads) {
+      const float4 zz = z4[c], tt = t4[c];
+      const float p0 = dexp(zz.x - lz), q0 = dexp(tt.x - lt);
+      const float p1 = dexp(zz.y - lz), q1 = dexp(tt.y - lt);
+      const float p2 = dexp(zz.z - lz), q2 = dexp(tt.z - lt);
+      const float p3 = dexp(zz.w - lz), q3 = dexp(tt.w - lt);
+      a1 += fabsf(p0 - q0) + fabsf(p1 - q1) + fabsf(p2 - q2) + fabsf(p3 - q3);
+      a2 += p0 * sgnf(p0 - q0) + p1 * sgnf(p1 - q1) + p2 * sgnf(p2 - q2) + p3 * sgnf(p3 - q3);
+    }
+    sum_l1 = a1;
+    sum_s = a2;
+  }
+  sum_l1 = block_sum<kSweepThreads>(sum_l1, dscr);
+  sum_s = block_sum<kSweepThreads>(sum_s, dscr);
+  if (threadIdx.x == 0) {
+    int32_t y = tid[r];
+    y = y < 0 ? 0 : (y >= V ? static_cast<int32_t>(V - 1) : y);
+    lse_z[r] = lz;
+    lse_t[r] = lt;
+    l1[r] = static_cast<float>(sum_l1);
+    S[r] = static_cast<float>(sum_s);
+    ce[r] = lz - Zp[r * V + y];
+  }
+}
+
+hipError_t launch_l1_sweep(int64_t R, int64_t V, const float* Zp, const float* Tt,
+                           const float2* sz, const float2* st, int64_t nstat, const uint8_t* mask,
+                           const int32_t* tid, int has_teacher, RowState rs, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(l1_sweep_kernel, dim3(static_cast<uint32_t>(R)), dim3(kSweepThreads), 0, s, V,
+                     Zp, Tt, sz, st, nstat, mask, tid, has_teacher, rs.lse_z, rs.lse_t, rs.l1, rs.S,
+                     rs.ce);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- per-row finalize
+
+// One wave per row: confidence logit c = W_c . [h ; e] + b (0 on invalid
+// slots), accept = clamp(1 - L1/2, 0, 1) (1 on invalid slots), BCE(c, accept)
+// with the label held constant, and the outputs the caller asked for.
+template <typename T>
+__global__ __launch_bounds__(256) void finalize_rows_kernel(
+    int64_t R, int64_t Hd, int64_t rank, int with_markov_conf, int has_conf, const T* hd,
+    const T* E, const T* Wc, const T* bc, RowState rs, float* accept_out, float* row_terms,
+    uint32_t* flags, float ce_a, float l1_a, float c_a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const bool m = rs.mask[r] != 0;
+  float c = 0.f;
+  if (m && has_conf) {
+    float acc = 0.f;
+    const T* h = hd + r * Hd;
+    for (int64_t i = lane; i < Hd; i += 64) acc += Elem<T>::to_f32(h[i]) * Elem<T>::to_f32(Wc[i]);
+    if (with_markov_conf) {
+      const T* e = E + r * rank;
+      for (int64_t j = lane; j < rank; j += 64)
+        acc += Elem<T>::to_f32(e[j]) * Elem<T>::to_f32(Wc[Hd + j]);
+    }
+    c = wave_sumf(acc) + Elem<T>::to_f32(bc[0]);
+  }
+  if (lane != 0) return;
+  float accept = 1.f, bce = 0.f, ce = 0.f, l1 = 0.f, dco = 0.f;
+  if (m) {
+    ce = rs.ce[r];
+    l1 = rs.l1[r];
+    accept = fminf(fmaxf(1.f - 0.5f * l1, 0.f), 1.f);
+    if (has_conf) {
+      bce = fmaxf(c, 0.f) - c * accept + log1pf(expf(-fabsf(c)));
+      dco = 1.f / (1.f + expf(-c)) - accept;
+    }
+    const float lr = rs.w[r] * (ce_a * ce + l1_a * l1 + c_a * bce);
+    if (!isfinite(lr)) atomicOr(flags, 4u);
+  }
+  rs.accept[r] = accept;
+  rs.conf[r] = c;
+  rs.bce[r] = bce;
+  rs.dcoef[r] = dco;
+  if (accept_out) accept_out[r] = accept;
+  if (row_terms) {
+    float4 t = make_float4(ce, l1, bce, c);
+    reinterpret_cast<float4*>(row_terms)[r] = t;
+  }
+}
+
+hipError_t launch_finalize_rows(int dtype, int64_t R, int64_t Hd, int64_t rank,
+                                int with_markov_conf, int has_conf, const void* hd, const void* E,
+                                const void* Wc, const void* bc, RowState rs, float* accept_out,
+                                float* row_terms, uint32_t* flags, float ce_a, float l1_a,
+                                float c_a, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>((R + 3) / 4));
+  if (dtype == 1)
+    hipLaunchKernelGGL(finalize_rows_kernel<bf16_t>, grid, dim3(256), 0, s, R, Hd, rank,
+                       with_markov_conf, has_conf, static_cast<const bf16_t*>(hd),
+                       static_cast<const bf16_t*>(E), static_cast<const bf16_t*>(Wc),
+                       static_cast<const bf16_t*>(bc), rs, accept_out, row_terms, flags, ce_a,
+                       l1_a, c_a);
+  else
+    hipLaunchKernelGGL(finalize_rows_kernel<float>, grid, dim3(256), 0, s, R, Hd, rank,
+                       with_markov_conf, has_conf, static_cast<const float*>(hd),
+                       static_cast<const float*>(E), static_cast<const float*>(Wc),
+                       static_cast<const float*>(bc), rs, accept_out, row_terms, flags, ce_a, l1_a,
+                       c_a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- reductions
+
+constexpr int kRedThreads = 1024;
+
+// accept pair (sum m*accept, sum m) and tau pair (sum over kept blocks of
+// 1 + sum_k prod_{j<=k} m_j accept_j, number of kept blocks) for this thread's
+// share, with m from the prefix rule.
+__device__ void accept_tau_share(int64_t nblk, int K, const float* accept, const uint8_t* eval,
+                                 const uint8_t* keep, double* acc_num, double* acc_den,
+                                 double* tau_num, double* tau_den) {
+  for (int64_t b = threadIdx.x; b < nblk; b += kRedThreads) {
+    const bool kept = keep == nullptr || keep[b] != 0;
+    double run = 1.0, tau = 1.0;
+    bool alive = kept;
+    for (int k = 0; k < K; ++k) {
+      const int64_t r = b * K + k;
+      alive = alive && eval[r] != 0;
+      const double a = alive ? static_cast<double>(accept[r]) : 0.0;
+      if (alive) { *acc_num += a; *acc_den += 1.0; }
+      run *= a;
+      tau += run;
+    }
+    if (kept) { *tau_num += tau; *tau_den += 1.0; }
+  }
+}
+
+__device__ void block_sum_many(double* v, int n, double* scr) {
+  // fixed-order reduction of n values per thread over the block
+  for (int i = 0; i < n; ++i) v[i] = wave_sum(v[i]);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  constexpr int NW = kRedThreads / kWave;
+  __syncthreads();
+  if (l == 0)
+    for (int i = 0; i < n; ++i) scr[i * NW + w] = v[i];
+  __syncthreads();
+  for (int i = 0; i < n; ++i) {
+    double r = 0.0;
+    for (int j = 0; j < NW; ++j) r += scr[i * NW + j];
+    v[i] = r;
+  }
+}
+
+__global__ __launch_bounds__(kRedThreads) void reduce_fwd_kernel(
+    int64_t R, int64_t nblk, int K, RowState rs, const uint8_t* eval, const uint8_t* keep,
+    float ce_a, float l1_a, float c_a, double* loss, int64_t* num_tokens, double* pairs) {
+  __shared__ double scr[8 * (kRedThreads / kWave)];
+  double v[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // ce, l1, bce, tokens, acc_num, acc_den, tau_num, tau_den
+  for (int64_t r = threadIdx.x; r < R; r += kRedThreads) {
+    if (!rs.mask[r]) continue;
+    const double w = rs.w[r];
+    v[0] += w * static_cast<double>(rs.ce[r]);
+    v[1] += w * static_cast<double>(rs.l1[r]);
+    v[2] += w * static_cast<double>(rs.bce[r]);
+    v[3] += 1.0;
+  }
+  accept_tau_share(nblk, K, rs.accept, eval, keep, &v[4], &v[5], &v[6], &v[7]);
+  block_sum_many(v, 8, scr);
+  if (threadIdx.x == 0) {
+    *loss = static_cast<double>(ce_a) * v[0] + static_cast<double>(l1_a) * v[1] +
+            static_cast<double>(c_a) * v[2];
+    *num_tokens = static_cast<int64_t>(v[3]);
+    pairs[0] = v[0]; pairs[1] = v[3];
+    pairs[2] = v[1]; pairs[3] = v[3];
+    pairs[4] = v[2]; pairs[5] = v[3];
+    pairs[6] = v[4]; pairs[7] = v[5];
+    pairs[8] = v[6]; pairs[9] = v[7];
+  }
+}
+
+hipError_t launch_reduce_fwd(int64_t R, int64_t nblk, int K, RowState rs, const uint8_t* eval,
+                             const uint8_t* keep, float ce_a, float l1_a, float c_a, double* loss,
+                             int64_t* num_tokens, double* pairs, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_fwd_kernel, dim3(1), dim3(kRedThreads), 0, s, R, nblk, K, rs, eval,
+                     keep, ce_a, l1_a, c_a, loss, num_tokens, pairs);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kRedThreads) void accept_report_kernel(int64_t nblk, int K,
+                                                                    const float* accept,
+                                                                    const uint8_t* eval,
+                                                                    const uint8_t* keep,
+                                                                    double* out4) {
+  __shared__ double scr[4 * (kRedThreads / kWave)];
+  double v[4] = {0, 0, 0, 0};
+  accept_tau_share(nblk, K, accept, eval, keep, &v[0], &v[1], &v[2], &v[3]);
+  block_sum_many(v, 4, scr);
+  if (threadIdx.x == 0)
+    for (int i = 0; i < 4; ++i) out4[i] = v[i];
+}
+
+hipError_t launch_accept_report(int64_t nblk, int K, const float* accept, const uint8_t* eval,
+                                const uint8_t* keep, double* out4, hipStream_t s) {
+  hipLaunchKernelGGL(accept_report_kernel, dim3(1), dim3(kRedThreads), 0, s, nblk, K, accept, eval,
+                     keep, out4);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- gradient sweep
+
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+  uint2 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+__device__ __forceinline__ float bf16_round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+
+// G_v = g w [ce_a (p_v - [v = y]) + l1_a p_v (s_v - S)], s = sign(p - q).
+// Writes dz (grad dtype); for bf16 operands also G as hi + lo bf16 parts (hi
+// may alias dz) for the MFMA products dE = G W2 and dW2 = G^T E; for fp32
+// operands G in fp32 (may alias dz).
+template <typename GT>
+__global__ __launch_bounds__(kSweepThreads) void grad_sweep_kernel(
+    int64_t V, const float* Zp, const float* Tt, const int32_t* tid, RowState rs, int has_teacher,
+    float g, float ce_a, float l1_a, GT* dz, bf16_t* ghi, bf16_t* glo, float* g32) {
+  const int64_t r = blockIdx.x;
+  const int64_t n4 = V / 4;
+  const bool m = rs.mask[r] != 0;
+  GT* dzr = dz + r * V;
+  bf16_t* hir = ghi ? ghi + r * V : nullptr;
+  bf16_t* lor = glo ? glo + r * V : nullptr;
+  float* g32r = g32 ? g32 + r * V : nullptr;
+  if (!m) {
+    for (int64_t c = threadIdx.x; c < n4; c += kSweepThreads) {
+      store4(dzr + 4 * c, 0.f, 0.f, 0.f, 0.f);
+      if (hir) store4(hir + 4 * c, 0.f, 0.f, 0.f, 0.f);
+      if (lor) store4(lor + 4 * c, 0.f, 0.f, 0.f, 0.f);
+      if (g32r) store4(g32r + 4 * c, 0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  const float gw = g * rs.w[r];
+  const float cc = gw * ce_a, cl = gw * l1_a;
+  const float Sr = rs.S[r];
+  const float lz = rs.lse_z[r], lt = rs.lse_t[r];
+  int32_t y = tid[r];
+  y = y < 0 ? 0 : (y >= V ? static_cast<int32_t>(V - 1) : y);
+  const float4* z4 = reinterpret_cast<const float4*>(Zp + r * V);
+  const float4* t4 = reinterpret_cast<const float4*>(Tt + r * V);
+#pragma unroll 2
+  for (int64_t c = threadIdx.x; c < n4; c += kSweepThreads) {
+    const float4 zz = z4[c];
+    float p[4] = {dexp(zz.x - lz), dexp(zz.y - lz), dexp(zz.z - lz), dexp(zz.w - lz)};
+    float G[4];
+    if (has_teacher) {
+      const float4 tt = t4[c];
+      const float q[4] = {dexp(tt.x - lt), dexp(tt.y - lt), dexp(tt.z - lt), dexp(tt.w - lt)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) G[e] = p[e] * (cc + cl * (sgnf(p[e] - q[e]) - Sr));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) G[e] = p[e] * cc;
+    }
+    const int64_t v0 = 4 * c;
+    if (y >= v0 && y < v0 + 4) G[y - v0] -= cc;
+    store4(dzr + v0, G[0], G[1], G[2], G[3]);
+    if (hir) store4(hir + v0, G[0], G[1], G[2], G[3]);
+    if (lor) {
+      store4(lor + v0, G[0] - bf16_round(G[0]), G[1] - bf16_round(G[1]), G[2] - bf16_round(G[2]),
+             G[3] - bf16_round(G[3]));
+    }
+    if (g32r) store4(g32r + v0, G[0], G[1], G[2], G[3]);
+  }
+}
+
+hipError_t launch_grad_sweep(int grad_dtype, int64_t R, int64_t V, const float* Zp,
+                             const float* Tt, const int32_t* tid, RowState rs, int has_teacher,
+                             float g, float ce_a, float l1_a, void* dz, bf16_t* ghi, bf16_t* glo,
+                             float* g32, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>(R));
+  if (grad_dtype == 1)
+    hipLaunchKernelGGL(grad_sweep_kernel<bf16_t>, grid, dim3(kSweepThreads), 0, s, V, Zp, Tt, tid,
+                       rs, has_teacher, g, ce_a, l1_a, static_cast<bf16_t*>(dz), ghi, glo, g32);
+  else
+    hipLaunchKernelGGL(grad_sweep_kernel<float>, grid, dim3(kSweepThreads), 0, s, V, Zp, Tt, tid,
+                       rs, has_teacher, g, ce_a, l1_a, static_cast<float*>(dz), ghi, glo, g32);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- backward helpers
+
+// dE[r, j] = sum_s part[s, r, j] + dc_r W_c[Hd + j]  (dc_r = g w_r c_a (sigmoid(c_r) - accept_r)),
+// zero on unsupervised rows.
+template <typename T>
+__global__ void de_reduce_kernel(int64_t R, int64_t rank, int splits, const float* part,
+                                 RowState rs, int conf_markov, const T* Wc, int64_t Hd, float g,
+                                 float c_a, float* dE) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= R * rank) return;
+  const int64_t r = i / rank, j = i - r * rank;
+  float v = 0.f;
+  if (rs.mask[r]) {
+    for (int s = 0; s < splits; ++s) v += part[s * R * rank + i];
+    if (conf_markov) v += g * rs.w[r] * c_a * rs.dcoef[r] * Elem<T>::to_f32(Wc[Hd + j]);
+  }
+  dE[i] = v;
+}
+
+hipError_t launch_de_reduce(int dtype, int64_t R, int64_t rank, int splits, const float* part,
+                            RowState rs, int conf_markov, const void* Wc, int64_t Hd, float g,
+                            float c_a, float* dE, hipStream_t s) {
+  const int64_t n = R * rank;
+  if (n <= 0) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>((n + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(de_reduce_kernel<bf16_t>, grid, dim3(256), 0, s, R, rank, splits, part, rs,
+                       conf_markov, static_cast<const bf16_t*>(Wc), Hd, g, c_a, dE);
+  else
+    hipLaunchKernelGGL(de_reduce_kernel<float>, grid, dim3(256), 0, s, R, rank, splits, part, rs,
+                       conf_markov, static_cast<const float*>(Wc), Hd, g, c_a, dE);
+  return hipGetLastError();
+}
+
+// dW1[prev_r, :] += dE[r, :] on supervised rows with an in-range id.
+__global__ void dw1_scatter_kernel(int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
+                                   const uint8_t* mask, const float* dE, float* dW1) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= R * rank) return;
+  const int64_t r = i / rank, j = i - r * rank;
+  if (!mask[r]) return;
+  const int32_t pv = prev[r];
+  if (pv < 0 || pv >= Vt) return;
+  atomicAdd(dW1 + pv * rank + j, dE[i]);
+}
+
+hipError_t launch_dw1_scatter(int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
+                              const uint8_t* mask, const float* dE, float* dW1, hipStream_t s) {
+  const int64_t n = R * rank;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dw1_scatter_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256),
+                     0, s, R, rank, Vt, prev, mask, dE, dW1);
+  return hipGetLastError();
+}
+
+// Confidence-head gradients.  Column f of the feature [h ; e] (f < F = Hd (+ r))
+// and the bias (column F) are reduced over row chunks into part[chunk, F + 1];
+// dh[r, i] = dc_r W_c[i].
+template <typename T>
+__global__ void conf_bwd_partial_kernel(int64_t R, int64_t Hd, int64_t rank, int64_t F,
+                                        int64_t rows_per, const T* hd, const T* E, RowState rs,
+                                        float g, float c_a, float* part) {
+  const int64_t f = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int64_t r0 = blockIdx.y * rows_per;
+  const int64_t r1 = (r0 + rows_per) < R ? (r0 + rows_per) : R;
+  if (f > F) return;
+  float acc = 0.f;
+  for (int64_t r = r0; r < r1; ++r) {
+    if (!rs.mask[r]) continue;
+    const float dc = g * rs.w[r] * c_a * rs.dcoef[r];
+    float x;
+    if (f < Hd) x = Elem<T>::to_f32(hd[r * Hd + f]);
+    else if (f < F) x = Elem<T>::to_f32(E[r * rank + (f - Hd)]);
+    else x = 1.f;
+    acc += dc * x;
+  }
+  part[blockIdx.y * (F + 1) + f] = acc;
+}
+
+__global__ void conf_bwd_final_kernel(int64_t F, int chunks, const float* part, float* dWc,
+                                      float* db) {
+  const int64_t f = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (f > F) return;
+  double acc = 0.0;
+  for (int c = 0; c < chunks; ++c) acc += part[c * (F + 1) + f];
+  if (f < F) dWc[f] = static_cast<float>(acc);
+  else *db = static_cast<float>(acc);
+}
+
+template <typename T>
+__global__ void conf_dh_kernel(int64_t R, int64_t Hd, const T* Wc, RowState rs, float g, float c_a,
+                               float* dh) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= R * Hd) return;
+  const int64_t r = i / Hd, f = i - r * Hd;
+  dh[i] = rs.mask[r] ? g * rs.w[r] * c_a * rs.dcoef[r] * Elem<T>::to_f32(Wc[f]) : 0.f;
+}
+
+hipError_t launch_conf_bwd(int dtype, int64_t R, int64_t Hd, int64_t rank, int conf_markov,
+                           const void* hd, const void* E, const void* Wc, RowState rs, float g,
+                           float c_a, float* part, int chunks, float* dWc, float* db, float* dh,
+                           hipStream_t s) {
+  const int64_t F = Hd + (conf_markov ? rank : 0);
+  const int64_t rows_per = (R + chunks - 1) / chunks;
+  dim3 grid(static_cast<uint32_t>((F + 1 + 255) / 256), static_cast<uint32_t>(chunks));
+  if (dtype == 1)
+    hipLaunchKernelGGL(conf_bwd_partial_kernel<bf16_t>, grid, dim3(256), 0, s, R, Hd, rank, F,
+                       rows_per, static_cast<const bf16_t*>(hd), static_cast<const bf16_t*>(E), rs,
+                       g, c_a, part);
+  else
+    hipLaunchKernelGGL(conf_bwd_partial_kernel<float>, grid, dim3(256), 0, s, R, Hd, rank, F,
+                       rows_per, static_cast<const float*>(hd), static_cast<const float*>(E), rs, g,
+                       c_a, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(conf_bwd_final_kernel, dim3(static_cast<uint32_t>((F + 1 + 255) / 256)),
+                     dim3(256), 0, s, F, chunks, part, dWc, db);
+  e = hipGetLastError();
+  if (e != hipSuccess || dh == nullptr || R * Hd == 0) return e;
+  dim3 g2(static_cast<uint32_t>((R * Hd + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(conf_dh_kernel<bf16_t>, g2, dim3(256), 0, s, R, Hd,
+                       static_cast<const bf16_t*>(Wc), rs, g, c_a, dh);
+  else
+    hipLaunchKernelGGL(conf_dh_kernel<float>, g2, dim3(256), 0, s, R, Hd,
+                       static_cast<const float*>(Wc), rs, g, c_a, dh);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

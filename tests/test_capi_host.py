@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI: exports, validation codes, loud failures.
+
+No GPU: every call here is rejected by host validation before any HIP call.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+from speculative_decoding_draft_dspark_amd import _capi as capi
+from speculative_decoding_draft_dspark_amd import DSparkBatch, DSparkError, dspark_loss_fwd
+
+PKG = os.path.dirname(capi.__file__)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return capi.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = capi.declared_functions()
+    assert set(names) >= {"dspark_loss_fwd", "dspark_loss_bwd", "dspark_accept_report",
+                          "dspark_workspace_size", "dspark_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _shape(**kw):
+    d = dict(batch=2, num_blocks=3, block_size=7, draft_vocab=512, target_vocab=600, hidden=64,
+             conf_hidden=32, markov_rank=16, with_markov_conf=1, dtype=1, grad_dtype=1,
+             reserved=0)
+    d.update(kw)
+    return capi.Shape(**d)
+
+
+def test_workspace_size(L):
+    s = _shape()
+    n = L.dspark_workspace_size(C.byref(s))
+    R, V = 42, 512
+    assert n >= 2 * R * V * 4            # fp32 teacher + corrected draft logits
+    assert n % 256 == 0
+    for bad in (dict(batch=0), dict(draft_vocab=1001), dict(markov_rank=12), dict(dtype=7),
+                dict(hidden=-8), dict(target_vocab=0)):
+        assert L.dspark_workspace_size(C.byref(_shape(**bad))) == 0, bad
+    assert L.dspark_workspace_size(None) == 0
+
+
+FAKE = 0x10000  # aligned host address; never dereferenced (validation fails first)
+
+
+def _inputs(**over):
+    d = {n: FAKE for n, _ in capi.InputsC._fields_}
+    d["aligned_target_logits"] = None
+    d.update(over)
+    return capi.InputsC(**d)
+
+
+def _fwd(L, shape=None, inp=None, ws=FAKE, wsbytes=1 << 40, out=None, hp=None):
+    shape = shape or _shape()
+    hp = hp or capi.HParamsC(0.1, 0.9, 1.0, 4.0)
+    inp = inp or _inputs()
+    out = out or capi.FwdOutC(FAKE, FAKE, FAKE, None, None, FAKE)
+    return L.dspark_loss_fwd(C.byref(shape), C.byref(hp), C.byref(inp), ws, wsbytes,
+                             C.byref(out), None)
+
+
+def test_validation_codes(L):
+    assert _fwd(L, inp=_inputs(draft_logits=None)) == -1
+    assert _fwd(L, inp=_inputs(prev_ids=None)) == -1
+    assert _fwd(L, inp=_inputs(conf_w=None)) == -1
+    assert _fwd(L, shape=_shape(draft_vocab=100)) == -2
+    assert _fwd(L, shape=_shape(grad_dtype=5)) == -3
+    assert _fwd(L, inp=_inputs(target_hidden=None, lm_head=None)) == -4          # no teacher
+    assert _fwd(L, inp=_inputs(target_hidden=None), hp=capi.HParamsC(1, 0, 0, 4)) == -4  # conf head
+    assert _fwd(L, wsbytes=100) == -5
+    assert _fwd(L, ws=None) == -5
+    assert _fwd(L, inp=_inputs(lm_head=FAKE + 4)) == -6
+    assert _fwd(L, out=capi.FwdOutC(FAKE, None, FAKE, None, None, FAKE)) == -1
+    hp = capi.HParamsC(0.1, 0.9, 1.0, 4.0)
+    o = capi.BwdOutC(None, FAKE, FAKE, FAKE, FAKE, None)
+    s = _shape()
+    assert L.dspark_loss_bwd(C.byref(s), C.byref(hp), C.byref(_inputs()), FAKE, 1 << 40, 1.0,
+                             C.byref(o), None) == -1
+    assert L.dspark_accept_report(1, 1, 7, None, FAKE, None, FAKE, None) == -1
+    assert L.dspark_accept_report(1, 0, 7, FAKE, FAKE, None, FAKE, None) == -2
+    assert L.dspark_accept_report(1, 1, 7, FAKE + 2, FAKE, None, FAKE, None) == -6
+
+
+def test_status_strings(L):
+    for code in capi.STATUS:
+        assert len(L.dspark_status_string(code)) > 0
+    assert L.dspark_status_string(123) == b"unknown status"
+
+
+def test_binding_fails_loudly_on_cpu_tensors():
+    z = torch.zeros(7, 64)
+    b = DSparkBatch(B=1, N=1, K=7, draft_logits=z, target_ids=torch.zeros(7, dtype=torch.int32),
+                    eval_mask=torch.ones(7, dtype=torch.uint8))
+    with pytest.raises(DSparkError):
+        dspark_loss_fwd(b)
+
+
+def test_product_never_imports_the_oracle():
+    for root, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert not re.search(r"\boracle\b", text), f
+
+
+def test_missing_library_is_a_loud_error(monkeypatch, tmp_path):
+    monkeypatch.setattr(capi, "_lib", None)
+    monkeypatch.setattr(capi, "LIB_PATH", str(tmp_path / "libdspark.so"))
+    with pytest.raises(DSparkError):
+        capi.lib()

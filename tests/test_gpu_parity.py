@@ -1,0 +1,283 @@
+"""GPU parity of the HIP path (through the C ABI) against the FP64 oracle.
+
+Tolerances (relative; normwise for arrays): 1e-4 for fp32 inputs, 2e-3 for
+bf16 inputs; denominators and token counts must be exact.  The oracle consumes
+the same rounded inputs.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_draft_dspark_amd import HParams, DSparkBatch, dspark_loss_fwd
+from tests.common import oracle_inputs
+from tests.gpu_common import (TOL, assert_norm, assert_scalar, compare_forward, ohp, run_gpu,
+                              say, to_np)
+from workloads import Workload, get_workload, make_inputs
+from workloads.synth import subset_blocks
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+GS = 0.0125  # upstream gradient of the loss numerator
+
+
+def _full_parity(d, hp, tol, grad_tol=None, teacher="hidden", conf=True, grad_dtype=None):
+    grad_tol = grad_tol or tol
+    b, f, g = run_gpu(d, hp, GS, teacher=teacher, conf=conf, grad_dtype=grad_dtype)
+    inp = oracle_inputs(d, teacher=teacher, conf=conf)
+    fw = oracle.forward(inp, ohp(hp))
+    compare_forward(f, fw, tol)
+    gr = oracle.backward(inp, ohp(hp), grad_scale=GS)
+    assert_norm("dz", to_np(g["d_draft_logits"]), gr.dz, grad_tol)
+    if inp.has_markov:
+        assert_norm("dW1", to_np(g["d_markov_w1"]), gr.dW1, grad_tol)
+        assert_norm("dW2", to_np(g["d_markov_w2"]), gr.dW2, grad_tol)
+    if inp.has_conf:
+        assert_norm("dW_c", to_np(g["d_conf_w"]), gr.dW_c, grad_tol)
+        assert_scalar("db_c", g["d_conf_b"].item(), gr.db_c[0], grad_tol)
+        assert_norm("dh_d", to_np(g["d_conf_hidden"]), gr.dh_d, grad_tol)
+    return f, g, fw, gr
+
+
+def test_tiny_fp32_full_parity():
+    wl = get_workload(0)
+    say(f"[parity] {wl.name}")
+    d = make_inputs(wl, DEV)
+    _full_parity(d, HParams(), TOL["f32"])
+
+
+def test_small_bf16_full_parity():
+    wl = get_workload(1)
+    say(f"[parity] {wl.name}")
+    d = make_inputs(wl, DEV)
+    _full_parity(d, HParams(), TOL["bf16"])
+
+
+def test_small_bf16_fp32_grads():
+    wl = get_workload(1)
+    say(f"[parity] {wl.name} fp32 grads")
+    d = make_inputs(wl, DEV)
+    _full_parity(d, HParams(ce_alpha=0.3, l1_alpha=0.7, confidence_alpha=0.5),
+                 TOL["bf16"], grad_tol=TOL["bf16"], grad_dtype=torch.float32)
+
+
+def _ragged(dtype="f32", V=1000, r=24, H=40, B=1, N=5, seed=11, Vt=None):
+    return Workload(f"ragged-{dtype}-v{V}", B=B, N=N, K=7, Vd=V, Vt=Vt or V + 17, H=H, Hd=H + 8,
+                    r=r, dtype=dtype, seed=seed, recipe="tiny")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_tiles_and_tails(dtype):
+    """V not a multiple of the 256-column tile, R not a multiple of the row tile, odd H, r."""
+    wl = _ragged(dtype)
+    say(f"[parity] {wl.name}")
+    d = make_inputs(wl, DEV)
+    d["eval_mask"][7 + 4:14] = 0      # one truncated block
+    d["block_keep"][3] = 0            # one dropped block
+    _full_parity(d, HParams(ce_alpha=0.25, l1_alpha=0.75, confidence_alpha=0.6), TOL[dtype])
+
+
+def test_aligned_teacher_and_no_decay():
+    wl = _ragged("f32", V=520, r=8, H=16, N=3, seed=3)
+    say(f"[parity] {wl.name} aligned teacher")
+    d = make_inputs(wl, DEV)
+    d["aligned"] = (d["H_t"] @ d["LM"].T).contiguous()
+    _full_parity(d, HParams(loss_decay_gamma=None), TOL["f32"], teacher="aligned")
+
+
+def test_no_teacher_ce_only():
+    wl = _ragged("bf16", V=264, r=8, H=16, N=2, seed=5)
+    say(f"[parity] {wl.name} CE only")
+    d = make_inputs(wl, DEV)
+    hp = HParams(ce_alpha=1.0, l1_alpha=0.0, confidence_alpha=0.0)
+    b, f, g = run_gpu(d, hp, GS, teacher="none", conf=False)
+    assert int(f.flags.item()) & 8
+    inp = oracle_inputs(d, teacher="none", conf=False)
+    fw = oracle.forward(inp, ohp(hp))
+    assert_scalar("loss", f.loss.item(), fw.loss, TOL["bf16"])
+    gr = oracle.backward(inp, ohp(hp), grad_scale=GS)
+    assert_norm("dz", to_np(g["d_draft_logits"]), gr.dz, TOL["bf16"])
+    assert_norm("dW2", to_np(g["d_markov_w2"]), gr.dW2, TOL["bf16"])
+
+
+def test_no_markov_head():
+    wl = _ragged("f32", V=256, r=8, H=16, N=2, seed=9)
+    say(f"[parity] {wl.name} no Markov head")
+    d = make_inputs(wl, DEV)
+    for k in ("prev_ids", "W1", "W2"):
+        d.pop(k)
+    d["with_markov_conf"] = False
+    d["W_c"] = d["W_c"][:, :wl.Hd].contiguous()
+    _full_parity(d, HParams(), TOL["f32"])
+
+
+def test_all_masked():
+    wl = _ragged("bf16", V=512, N=2, seed=4)
+    d = make_inputs(wl, DEV)
+    d["eval_mask"].zero_()
+    b, f, g = run_gpu(d, HParams(), GS)
+    assert f.loss.item() == 0.0 and int(f.num_tokens.item()) == 0
+    assert not torch.any(g["d_draft_logits"] != 0)
+    assert not torch.any(g["d_markov_w1"] != 0) and not torch.any(g["d_markov_w2"] != 0)
+    p = f.pairs.cpu()
+    assert p[4, 0].item() == 2.0 and p[4, 1].item() == 2.0   # tau = 1 per kept block
+
+
+def test_garbage_in_masked_rows_changes_nothing():
+    wl = _ragged("bf16", V=768, N=4, seed=8)
+    d = make_inputs(wl, DEV)
+    d["eval_mask"][3:7] = 0
+    d["block_keep"][2] = 0
+    b1, f1, g1 = run_gpu(d, HParams(), GS)
+    bad = dict(d)
+    m = torch.tensor(oracle.effective_mask(d["eval_mask"].cpu().numpy(),
+                                           d["block_keep"].cpu().numpy(), 1, wl.N, 7),
+                     device=DEV) == 0
+    bad["z"] = d["z"].clone(); bad["z"][m] = float("nan")
+    bad["prev_ids"] = d["prev_ids"].clone(); bad["prev_ids"][m] = -1
+    bad["target_ids"] = d["target_ids"].clone(); bad["target_ids"][m] = -5
+    bad["h_d"] = d["h_d"].clone(); bad["h_d"][m] = float("inf")
+    bad["H_t"] = d["H_t"].clone(); bad["H_t"][m] = float("nan")
+    b2, f2, g2 = run_gpu(bad, HParams(), GS)
+    assert f1.loss.item() == f2.loss.item()
+    assert torch.equal(f1.pairs, f2.pairs) and torch.equal(f1.row_terms, f2.row_terms)
+    assert int(f2.flags.item()) == 0
+    assert torch.equal(g1["d_draft_logits"], g2["d_draft_logits"])
+    assert torch.equal(g1["d_markov_w2"], g2["d_markov_w2"])
+    assert torch.equal(g1["d_conf_w"], g2["d_conf_w"])
+
+
+def test_out_of_range_ids_flagged():
+    wl = _ragged("f32", V=256, N=2, seed=12)
+    d = make_inputs(wl, DEV)
+    d["target_ids"][0] = wl.Vd + 3
+    d["prev_ids"][1] = -2
+    b, f, g = run_gpu(d, HParams(), GS)
+    assert int(f.flags.item()) & 3 == 3
+
+
+def test_forward_is_deterministic():
+    wl = get_workload(1)
+    d = make_inputs(wl, DEV)
+    b = DSparkBatch.from_workload(d)
+    f1 = dspark_loss_fwd(b, HParams())
+    f2 = dspark_loss_fwd(b, HParams())
+    torch.cuda.synchronize()
+    assert torch.equal(f1.loss, f2.loss) and torch.equal(f1.pairs, f2.pairs)
+    assert torch.equal(f1.row_terms, f2.row_terms)
+
+
+# ---------------------------------------------------------------- large workloads
+
+def _edge_checks(d, f, wl):
+    """Exact-zero L1 on identical and uniform-vs-uniform rows of the edge workload."""
+    R, K, N = wl.R, wl.K, wl.N
+    blk = np.arange(R) // K
+    n = blk % N
+    b = blk // N
+    cls = n % 4
+    half = ((b + n // 4) % 2) == 0
+    rt = f.row_terms.cpu().numpy()
+    acc = f.accept_rate.cpu().numpy()
+    m = oracle.effective_mask(d["eval_mask"].cpu().numpy(), d["block_keep"].cpu().numpy(),
+                              wl.B, N, K)
+    exact = (m != 0) & ((cls == 1) | ((cls == 2) & half))
+    assert exact.sum() > 0
+    assert np.all(rt[exact, 1] == 0.0), "L1 must be exactly 0 on identical rows"
+    assert np.all(acc[exact] == 1.0)
+    inval = m == 0
+    assert np.all(rt[inval] == 0.0) and np.all(acc[inval] == 1.0)
+
+
+def test_edge_distributions_full_parity():
+    wl = get_workload(4)
+    say(f"[parity] {wl.name}")
+    d = make_inputs(wl, DEV)
+    f, g, fw, gr = _full_parity(d, HParams(), TOL["bf16"])
+    _edge_checks(d, f, wl)
+    assert int(f.flags.item()) == 0
+
+
+def _sampled_blocks(wl, count, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(wl.B * wl.N, size=count, replace=False))
+
+
+@pytest.mark.parametrize("idx,count", [(2, 24), (3, 24)])
+def test_full_size_sampled_rows(idx, count):
+    """Full-size launch; sampled whole blocks checked against the oracle row by row."""
+    wl = get_workload(idx)
+    say(f"[parity] {wl.name} full size, {count} sampled blocks")
+    d = make_inputs(wl, DEV)
+    hp = HParams()
+    b, f, g = run_gpu(d, hp, GS)
+    blocks = _sampled_blocks(wl, count, 100 + idx)
+    sub = subset_blocks(d, blocks)
+    inp = oracle_inputs(sub)
+    rows = (blocks[:, None] * wl.K + np.arange(wl.K)[None, :]).ravel()
+    ref = oracle.forward_rows(inp, ohp(hp), np.arange(len(rows)))
+    rt = to_np(f.row_terms)[rows]
+    tol = TOL["bf16"]
+    for j, k in enumerate(("ce", "l1", "bce", "conf_logit")):
+        assert_norm(k, rt[:, j], ref[k], tol)
+    assert_norm("accept", to_np(f.accept_rate)[rows], ref["accept"], tol)
+    dz_ref = oracle.grad_rows(inp, ohp(hp), np.arange(len(rows)), grad_scale=GS)
+    assert_norm("dz rows", to_np(g["d_draft_logits"][torch.as_tensor(rows, device=DEV)]), dz_ref,
+                tol)
+    # totals are the sums of the per-row terms (property at any size)
+    w = oracle.decay_weights(wl.K, hp.loss_decay_gamma)[np.arange(wl.R) % wl.K]
+    m = oracle.effective_mask(d["eval_mask"].cpu().numpy(), d["block_keep"].cpu().numpy(),
+                              wl.B, wl.N, wl.K)
+    rtall = to_np(f.row_terms)
+    num = np.sum(np.where(m != 0, w, 0)[:, None] * rtall[:, :3], axis=0)
+    p = f.pairs.cpu().numpy()
+    for i in range(3):
+        assert_scalar(f"pair {i}", p[i, 0], num[i], 1e-5)
+    assert int(f.num_tokens.item()) == int(m.sum())
+    acc = to_np(f.accept_rate).reshape(wl.B * wl.N, wl.K)
+    mm = m.reshape(-1, wl.K)
+    tau = 1 + np.cumprod(np.where(mm != 0, acc, 0), axis=1).sum(1)
+    assert_scalar("tau", p[4, 0], tau.sum(), 1e-6)
+    assert p[4, 1] == wl.B * wl.N
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_full_size_gradients_additive_and_sub_batch_parity(idx):
+    """Weight gradients: a sub-batch matches the oracle; the full-size launch equals
+    the sum of launches over a partition of its blocks (data-parallel additivity)."""
+    wl = get_workload(idx)
+    say(f"[parity] {wl.name} gradient additivity")
+    d = make_inputs(wl, DEV)
+    hp = HParams()
+    _, f, g = run_gpu(d, hp, GS)
+    nb = wl.B * wl.N
+    parts = np.array_split(np.arange(nb), 4)
+    acc = {k: torch.zeros_like(v, dtype=torch.float64) for k, v in g.items()
+           if k != "d_draft_logits"}
+    loss = 0.0
+    for i, blocks in enumerate(parts):
+        sub = subset_blocks(d, blocks)
+        _, fs, gs = run_gpu(sub, hp, GS)
+        loss += fs.loss.item()
+        for k in acc:
+            acc[k] += gs[k].double()
+        if i == 0:
+            few = subset_blocks(d, blocks[:8])
+            _, fo, go = run_gpu(few, hp, GS)
+            inp = oracle_inputs(few)
+            fw = oracle.forward(inp, ohp(hp))
+            compare_forward(fo, fw, TOL["bf16"])
+            gr = oracle.backward(inp, ohp(hp), grad_scale=GS)
+            assert_norm("sub dW1", to_np(go["d_markov_w1"]), gr.dW1, TOL["bf16"])
+            assert_norm("sub dW2", to_np(go["d_markov_w2"]), gr.dW2, TOL["bf16"])
+            assert_norm("sub dW_c", to_np(go["d_conf_w"]), gr.dW_c, TOL["bf16"])
+            assert_norm("sub dz", to_np(go["d_draft_logits"]), gr.dz, TOL["bf16"])
+    assert_scalar("loss additivity", f.loss.item(), loss, 1e-9)
+    for k in acc:
+        assert_norm(k + " additivity", to_np(g[k]), to_np(acc[k]), 1e-4)
