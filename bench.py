@@ -1,0 +1,190 @@
+#!/usr/bin/env python
+"""Throughput of the fused DSpark loss (forward + backward) on one MI355X.
+
+One step = dspark_loss_fwd + dspark_loss_bwd over one batch of the
+large-batch workload (batch 8 x 256 blocks x block_size 7 = 14336 rows,
+vocab 151936, hidden 4096, markov rank 256, bf16 inputs, confidence head on
+[hidden ; markov embedding]), with every input already resident in HBM.
+Prints one JSON line.  Synthetic, seeded data (workloads package).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def _gpu_leg(args):
+    import torch
+
+    from speculative_decoding_draft_dspark_amd import (DSparkBatch, HParams, _capi,
+                                                       dspark_loss_bwd, dspark_loss_fwd,
+                                                       dspark_workspace_size)
+    from workloads import get_workload, make_inputs
+
+    _capi.lib()  # fail loudly without the HIP library
+    wl = get_workload(args.workload)
+    dev = "cuda:0"
+    t0 = time.time()
+    d = make_inputs(wl, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {wl.name} ready in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    b = DSparkBatch.from_workload(d)
+    hp = HParams()
+    ws = torch.empty(dspark_workspace_size(b), dtype=torch.uint8, device=dev)
+    gs = 1.0 / wl.R
+    fwd = dspark_loss_fwd(b, hp, workspace=ws)
+    grads = dspark_loss_bwd(b, hp, fwd, gs)
+
+    def step():
+        f = dspark_loss_fwd(b, hp, workspace=ws)
+        dspark_loss_bwd(b, hp, f, gs, out=grads)
+        return f
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _capi.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        f = step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stages = _capi.profile_read()
+    _capi.profile_enable(False)
+    loss = f.loss.item()
+    flags = int(f.flags.item())
+    print(f"[bench] {args.steps} steps in {elapsed:.3f}s, loss numerator {loss:.4f}, "
+          f"flags {flags}", file=sys.stderr, flush=True)
+    return wl, elapsed, stages
+
+
+def _avg_ms(stages, name):
+    ms, n = stages.get(name, (0.0, 0))
+    return ms / n if n else None
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+        return rec.get("bytes_per_launch") if rec.get("current", False) else None
+    except (OSError, ValueError):
+        return None
+
+
+def _cpu_leg(wl, blocks: int):
+    """The FP64 oracle on a bounded sample of the same workload (whole blocks)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workloads import make_inputs, to_numpy_f64
+    from workloads.synth import subset_blocks
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = torch.get_num_threads()
+    d = make_inputs(wl, "cuda:0")
+    sub = subset_blocks(d, np.arange(blocks))
+    n = to_numpy_f64(sub)
+    del d, sub
+    torch.cuda.empty_cache()
+    swl = wl
+    inp = oracle.Inputs(B=1, N=blocks, K=swl.K, z=n["z"], target_ids=n["target_ids"],
+                        eval_mask=n["eval_mask"], block_keep=n["block_keep"],
+                        prev_ids=n["prev_ids"], W1=n["W1"], W2=n["W2"], H_t=n["H_t"],
+                        LM=n["LM"], h_d=n["h_d"], W_c=n["W_c"], b_c=n["b_c"])
+    hp = oracle.HParams()
+    t0 = time.perf_counter()
+    oracle.forward(inp, hp)
+    oracle.backward(inp, hp, grad_scale=1.0 / wl.R)
+    dt = time.perf_counter() - t0
+    rows = blocks * wl.K
+    return {"value": rows / dt, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{blocks} whole blocks ({rows} rows) of {wl.name}, fwd+bwd in "
+                      f"{dt:.1f}s, numpy float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="large-batch-r14336-v151936")
+    ap.add_argument("--cpu-blocks", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    wl, elapsed, stages = _gpu_leg(args)
+    R, V, H, r = wl.R, wl.Vd, wl.H, wl.r
+    ms_step = 1000.0 * elapsed / args.steps
+    rows_per_s = R * args.steps / elapsed
+
+    gemm_ms = _avg_ms(stages, "teacher_gemm")
+    gemm_flops = 2.0 * R * V * H
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "teacher_gemm (lm_head projection, bf16 MFMA)",
+                "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": _traffic("teacher_gemm"),
+                "flops_per_launch": gemm_flops, "avg_ms": round(gemm_ms, 4)}
+
+    # row sweeps: algorithmic bytes per launch / average duration
+    sweeps = {}
+    for name, bytes_per_elem in (("l1_sweep", 8), ("grad_sweep", 12)):
+        ms = _avg_ms(stages, name)
+        if ms:
+            gbs = bytes_per_elem * R * V / (ms * 1e-3) / 1e9
+            sweeps[name] = {"avg_ms": round(ms, 4), "GB/s": round(gbs, 1),
+                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                            "bytes_per_row": bytes_per_elem * V}
+    stage_ms = {k: round(v[0] / v[1], 4) for k, v in stages.items() if v[1]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_leg(wl, args.cpu_blocks)
+
+    line = {
+        "metric": "DSpark loss fwd+bwd rows/s at V=151936",
+        "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded workloads package)",
+        "config": {"workload": wl.name, "rows": R, "batch": wl.B, "num_blocks": wl.N,
+                   "block_size": wl.K, "draft_vocab": V, "target_vocab": wl.Vt, "hidden": H,
+                   "markov_rank": r, "confidence_head": "with_markov", "gamma": wl.gamma,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "sweeps": sweeps,
+        "stage_ms": stage_ms,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

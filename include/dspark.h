@@ -167,6 +167,17 @@ int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,
 const char *dspark_status_string(int status);
 const char *dspark_last_hip_error(void);
 
+/* ---- per-stage GPU timers (a tracing aid; off by default) -------------------
+ * When enabled, every fwd / bwd call records a pair of HIP events around each
+ * of its stages on the call's stream (adds two event records per stage).
+ * dspark_profile_read() waits for all recorded events, adds their elapsed
+ * times to per-stage totals, and copies min(n, stage count) totals (ms) and
+ * launch counts out; it returns the number of stages.  Enabling or disabling
+ * clears the totals.  Process-wide, guarded by a mutex. */
+int dspark_profile_enable(int on);
+int dspark_profile_read(double *ms, int64_t *counts, int n);
+const char *dspark_stage_name(int stage);
+
 #ifdef __cplusplus
 }
 #endif

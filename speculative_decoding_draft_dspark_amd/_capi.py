@@ -81,6 +81,12 @@ def lib():
     L.dspark_status_string.restype = C.c_char_p
     L.dspark_last_hip_error.argtypes = []
     L.dspark_last_hip_error.restype = C.c_char_p
+    L.dspark_profile_enable.argtypes = [C.c_int]
+    L.dspark_profile_enable.restype = C.c_int
+    L.dspark_profile_read.argtypes = [C.c_void_p, C.c_void_p, C.c_int]
+    L.dspark_profile_read.restype = C.c_int
+    L.dspark_stage_name.argtypes = [C.c_int]
+    L.dspark_stage_name.restype = C.c_char_p
     _lib = L
     return L
 
@@ -98,3 +104,18 @@ def declared_functions() -> list:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def profile_enable(on: bool = True) -> None:
+    """Turn the library's per-stage HIP-event timers on or off (clears totals)."""
+    lib().dspark_profile_enable(1 if on else 0)
+
+
+def profile_read() -> dict:
+    """{stage name: (total ms, launches)} accumulated since profile_enable()."""
+    L = lib()
+    n = L.dspark_profile_read(None, None, 0)
+    ms = (C.c_double * n)()
+    cnt = (C.c_int64 * n)()
+    L.dspark_profile_read(C.cast(ms, C.c_void_p), C.cast(cnt, C.c_void_p), n)
+    return {L.dspark_stage_name(i).decode(): (ms[i], cnt[i]) for i in range(n)}

@@ -2,8 +2,12 @@
 // the launch sequences of the forward, backward and acceptance report.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "../../include/dspark.h"
 #include "internal.h"
@@ -19,12 +23,15 @@ inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Dims {
   int64_t B, N, K, R, Vd, Vt, H, Hd, r, nstat, splits, conf_chunks, F;
+  int64_t R32;  // R rounded up to a multiple of 32 (k-blocked row operands)
   int dtype, gdtype, esize;
   bool markov, conf, conf_markov;
 };
 
 struct Layout {
-  size_t Zp, T, sz, st, E, mask, rowf, ghi, glo, g32, dEpart, dE, confpart, total;
+  size_t Zp, T, sz, st, E, mask, rowf, ghi, glo, g32, dEpart, dE, confpart;
+  size_t w2t, eblk, blkhi, blklo, dw2part;  // bf16 backward operands
+  size_t total;
 };
 
 constexpr int kRowArrays = 10;  // float row arrays of RowState (w .. dcoef)
@@ -62,6 +69,7 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   d->splits = d->markov ? sp : 0;
   d->conf_chunks = d->R < 256 ? static_cast<int>(d->R) : 256;
   d->F = d->Hd + (d->conf_markov ? d->r : 0);
+  d->R32 = (d->R + 31) / 32 * 32;
   return DSPARK_OK;
 }
 
@@ -76,10 +84,18 @@ Layout make_layout(const Dims& d) {
   L.E = o; o = up(o + static_cast<size_t>(d.R) * d.r * d.esize);
   L.mask = o; o = up(o + d.R);
   L.rowf = o; o = up(o + static_cast<size_t>(d.R) * 4 * kRowArrays);
-  L.ghi = L.glo = L.g32 = 0;
+  L.ghi = L.glo = L.g32 = L.w2t = L.eblk = L.blkhi = L.blklo = L.dw2part = 0;
   if (d.dtype == DSPARK_BF16) {
     if (d.gdtype != DSPARK_BF16) { L.ghi = o; o = up(o + RV * 2); }
     L.glo = o; o = up(o + RV * 2);
+    if (d.markov) {
+      const size_t R32V = static_cast<size_t>(d.R32) * d.Vd;
+      L.w2t = o; o = up(o + static_cast<size_t>(d.Vd) * d.r * 2);
+      L.eblk = o; o = up(o + static_cast<size_t>(d.R32) * d.r * 2);
+      L.blkhi = o; o = up(o + R32V * 2);
+      L.blklo = o; o = up(o + R32V * 2);
+      L.dw2part = o; o = up(o + static_cast<size_t>(2) * d.Vd * d.r * 4);
+    }
   } else if (d.gdtype != DSPARK_F32) {
     L.g32 = o; o = up(o + RV * 4);
   }
@@ -115,6 +131,61 @@ int hip_status(hipError_t e) {
   } while (0)
 
 enum Teacher { kNone = 0, kHidden = 1, kAligned = 2 };
+
+// ---- per-stage timers (tracing aid)
+enum Stage {
+  kPrep, kGather, kDraftGemm, kTeacherGemm, kL1Sweep, kFinalize, kReduce, kGradSweep, kDeGemm,
+  kDeReduce, kDw1, kDw2Gemm, kConfBwd, kStages
+};
+const char* const kStageNames[kStages] = {
+    "prep_rows", "gather_embed", "draft_logits_gemm", "teacher_gemm", "l1_sweep",
+    "finalize_rows", "reduce_fwd", "grad_sweep", "dE_gemm", "dE_reduce", "dW1_scatter",
+    "dW2_gemm", "conf_bwd"};
+
+struct Profiler {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[kStages];
+  std::vector<hipEvent_t> pool;
+  double ms[kStages] = {};
+  int64_t count[kStages] = {};
+};
+Profiler g_prof;
+
+hipEvent_t take_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t staged(int id, hipStream_t s, F&& launch) {
+  if (!g_prof.on.load(std::memory_order_relaxed)) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    a = take_event();
+    b = take_event();
+  }
+  if (a && hipEventRecord(a, s) != hipSuccess) a = nullptr;
+  const hipError_t e = launch();
+  if (b && hipEventRecord(b, s) != hipSuccess) b = nullptr;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (a && b) {
+    g_prof.pending[id].emplace_back(a, b);
+  } else {
+    if (a) g_prof.pool.push_back(a);
+    if (b) g_prof.pool.push_back(b);
+  }
+  return e;
+}
+
+#define DSPARK_STAGE(id, expr) DSPARK_TRY(staged((id), s, [&] { return (expr); }))
 
 int check_inputs(const Dims& d, const dspark_hparams* hp, const dspark_inputs* in, Teacher* t) {
   if (!hp || !in) return DSPARK_ERR_NULL;
@@ -186,25 +257,25 @@ int dspark_loss_fwd(const dspark_shape* shape, const dspark_hparams* hp, const d
   float2* stt = reinterpret_cast<float2*>(ws + L.st);
   void* E = ws + L.E;
 
-  DSPARK_TRY(launch_prep_rows(d.R, static_cast<int>(d.K), in->eval_mask, in->block_keep_mask,
+  DSPARK_STAGE(kPrep, launch_prep_rows(d.R, static_cast<int>(d.K), in->eval_mask, in->block_keep_mask,
                               in->target_ids, in->prev_ids, d.Vd, d.Vt, d.markov,
                               hp->loss_decay_gamma, teacher == kNone ? DSPARK_FLAG_NO_TEACHER : 0u,
                               rs.mask, rs.w, out->flags, s));
   if (d.markov)
-    DSPARK_TRY(launch_gather_embed(d.dtype, d.R, d.r, d.Vt, in->prev_ids, rs.mask, in->markov_w1,
+    DSPARK_STAGE(kGather, launch_gather_embed(d.dtype, d.R, d.r, d.Vt, in->prev_ids, rs.mask, in->markov_w1,
                                    E, s));
 
   // corrected draft logits z' = z + E W2^T (fp32) with per-tile softmax statistics
   {
     Operand A{}, B{};
     A.seg[0] = A.seg[1] = E; A.kseg = d.r; A.kpad = gemm_kpad(d.r, d.esize); A.ld = d.r;
-    A.mcontig = 0; A.nseg = 1;
+    A.layout = LAYOUT_KC; A.nseg = 1;
     B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.r; B.kpad = A.kpad; B.ld = d.r;
-    B.mcontig = 0; B.nseg = 1;
+    B.layout = LAYOUT_KC; B.nseg = 1;
     EpiParams ep{};
     ep.C = Zp; ep.ldc = d.Vd; ep.X = in->draft_logits; ep.ldx = d.Vd; ep.stats = sz;
     ep.nstat = d.nstat;
-    DSPARK_TRY(launch_gemm(d.dtype, EPI_STATS, d.R, d.Vd, A, B, 1, ep, s));
+    DSPARK_STAGE(kDraftGemm, launch_gemm(d.dtype, EPI_STATS, 0, d.R, d.Vd, A, B, 1, ep, s));
   }
   // teacher logits T (fp32) with the same statistics
   if (teacher != kNone) {
@@ -219,15 +290,15 @@ int dspark_loss_fwd(const dspark_shape* shape, const dspark_hparams* hp, const d
       A.nseg = B.nseg = 1;  // K = 0: T = aligned logits
       ep.X = in->aligned_target_logits; ep.ldx = d.Vd;
     }
-    DSPARK_TRY(launch_gemm(d.dtype, EPI_STATS, d.R, d.Vd, A, B, 1, ep, s));
+    DSPARK_STAGE(kTeacherGemm, launch_gemm(d.dtype, EPI_STATS, 1, d.R, d.Vd, A, B, 1, ep, s));
   }
-  DSPARK_TRY(launch_l1_sweep(d.R, d.Vd, Zp, T, sz, stt, d.nstat, rs.mask, in->target_ids,
+  DSPARK_STAGE(kL1Sweep, launch_l1_sweep(d.R, d.Vd, Zp, T, sz, stt, d.nstat, rs.mask, in->target_ids,
                              teacher != kNone, rs, s));
-  DSPARK_TRY(launch_finalize_rows(d.dtype, d.R, d.Hd, d.r, d.conf_markov, d.conf,
+  DSPARK_STAGE(kFinalize, launch_finalize_rows(d.dtype, d.R, d.Hd, d.r, d.conf_markov, d.conf,
                                   in->conf_hidden, E, in->conf_w, in->conf_b, rs,
                                   out->accept_rate, out->row_terms, out->flags, hp->ce_alpha,
                                   hp->l1_alpha, hp->confidence_alpha, s));
-  DSPARK_TRY(launch_reduce_fwd(d.R, d.B * d.N, static_cast<int>(d.K), rs, in->eval_mask,
+  DSPARK_STAGE(kReduce, launch_reduce_fwd(d.R, d.B * d.N, static_cast<int>(d.K), rs, in->eval_mask,
                                in->block_keep_mask, hp->ce_alpha, hp->l1_alpha,
                                d.conf ? hp->confidence_alpha : 0.f, out->loss, out->num_tokens,
                                out->pairs, s));
@@ -260,59 +331,151 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
   const float g = grad_scale;
   const float c_a = d.conf ? hp->confidence_alpha : 0.f;
 
-  // G = dloss/dz' (also dloss/dz); operand copies for the MFMA products
-  bf16_t* ghi = nullptr;
-  bf16_t* glo = nullptr;
-  float* g32 = nullptr;
-  const void* gA = nullptr;  // first K segment of the G operand
+  float* dEpart = reinterpret_cast<float*>(ws + L.dEpart);
+  float* dE = reinterpret_cast<float*>(ws + L.dE);
   if (d.dtype == DSPARK_BF16) {
-    ghi = d.gdtype == DSPARK_BF16 ? nullptr : reinterpret_cast<bf16_t*>(ws + L.ghi);
-    glo = reinterpret_cast<bf16_t*>(ws + L.glo);
-    gA = ghi ? static_cast<const void*>(ghi) : out->d_draft_logits;
-  } else {
-    g32 = d.gdtype == DSPARK_F32 ? nullptr : reinterpret_cast<float*>(ws + L.g32);
-    gA = g32 ? static_cast<const void*>(g32) : out->d_draft_logits;
-  }
-  DSPARK_TRY(launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs, teacher != kNone,
-                               g, hp->ce_alpha, hp->l1_alpha, out->d_draft_logits, ghi, glo, g32,
-                               s));
-  const int nseg = d.dtype == DSPARK_BF16 ? 2 : 1;
-  if (d.markov) {
-    float* dEpart = reinterpret_cast<float*>(ws + L.dEpart);
-    float* dE = reinterpret_cast<float*>(ws + L.dE);
-    {  // dE partials = G . W2 over vocabulary splits
-      Operand A{}, B{};
-      A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.Vd; A.kpad = gemm_kpad(d.Vd, d.esize);
-      A.ld = d.Vd; A.mcontig = 0; A.nseg = nseg;
-      B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.Vd; B.kpad = A.kpad; B.ld = d.r;
-      B.mcontig = 1; B.nseg = nseg;
-      EpiParams ep{};
-      ep.C = dEpart; ep.ldc = d.r;
-      DSPARK_TRY(launch_gemm(d.dtype, EPI_PARTIAL, d.R, d.r, A, B, static_cast<int>(d.splits), ep,
-                             s));
+    // G = dloss/dz' (= dloss/dz) as dz plus bf16 hi/lo parts: row-major for
+    // dE = G . W2 (contraction over the vocabulary) and k-blocked by 8 rows for
+    // dW2 = G^T . E (contraction over rows).
+    bf16_t* ghi = d.gdtype == DSPARK_BF16 ? nullptr : reinterpret_cast<bf16_t*>(ws + L.ghi);
+    bf16_t* glo = reinterpret_cast<bf16_t*>(ws + L.glo);
+    const void* gA = ghi ? static_cast<const void*>(ghi) : out->d_draft_logits;
+    bf16_t* bhi = reinterpret_cast<bf16_t*>(ws + L.blkhi);
+    bf16_t* blo = reinterpret_cast<bf16_t*>(ws + L.blklo);
+    const int64_t rgroups = d.R32 / 8;
+    if (d.markov) {
+      DSPARK_STAGE(kGradSweep, launch_grad_sweep8(d.gdtype, d.R, rgroups, d.Vd, Zp, T,
+                                                  in->target_ids, rs, teacher != kNone, g,
+                                                  hp->ce_alpha, hp->l1_alpha, out->d_draft_logits,
+                                                  ghi, glo, bhi, blo, s));
+    } else {
+      DSPARK_STAGE(kGradSweep, launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs,
+                                                 teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
+                                                 out->d_draft_logits, nullptr, nullptr, nullptr,
+                                                 s));
     }
-    DSPARK_TRY(launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits), dEpart, rs,
-                                d.conf_markov, in->conf_w, d.Hd, g, c_a, dE, s));
-    DSPARK_TRY(launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
-    DSPARK_TRY(launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE, out->d_markov_w1, s));
-    {  // dW2 = G^T . E (reduction over rows)
-      Operand A{}, B{};
-      A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.R; A.kpad = gemm_kpad(d.R, d.esize);
-      A.ld = d.Vd; A.mcontig = 1; A.nseg = nseg;
-      B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = A.kpad; B.ld = d.r; B.mcontig = 1;
-      B.nseg = nseg;
-      EpiParams ep{};
-      ep.C = out->d_markov_w2; ep.ldc = d.r;
-      DSPARK_TRY(launch_gemm(d.dtype, EPI_STORE, d.Vd, d.r, A, B, 1, ep, s));
+    if (d.markov) {
+      void* w2t = ws + L.w2t;
+      void* eblk = ws + L.eblk;
+      DSPARK_STAGE(kDeGemm, launch_transpose_bf16(d.Vd, d.r, in->markov_w2, w2t, s));
+      {  // dE partials = G . W2 over vocabulary splits (both operands K-contiguous)
+        Operand A{}, B{};
+        A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.Vd; A.kpad = gemm_kpad(d.Vd, 2);
+        A.ld = d.Vd; A.layout = LAYOUT_KC; A.nseg = 2;
+        B.seg[0] = B.seg[1] = w2t; B.kseg = d.Vd; B.kpad = A.kpad; B.ld = d.Vd;
+        B.layout = LAYOUT_KC; B.nseg = 2;
+        EpiParams ep{};
+        ep.C = dEpart; ep.ldc = d.r;
+        DSPARK_STAGE(kDeGemm, launch_gemm(d.dtype, EPI_PARTIAL, 2, d.R, d.r, A, B,
+                                          static_cast<int>(d.splits), ep, s));
+      }
+      DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
+                                               dEpart, rs, d.conf_markov, in->conf_w, d.Hd, g,
+                                               c_a, dE, s));
+      DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
+      DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
+                                            out->d_markov_w1, s));
+      DSPARK_STAGE(kDw2Gemm, launch_embed_blocked(d.R, rgroups, d.r, E, eblk, s));
+      {  // dW2 = G^T . E: hi and lo segments as two splits, then summed
+        float* part = reinterpret_cast<float*>(ws + L.dw2part);
+        Operand A{}, B{};
+        A.seg[0] = bhi; A.seg[1] = blo; A.kseg = d.R32; A.kpad = gemm_kpad(d.R32, 2);
+        A.ld = d.Vd; A.layout = LAYOUT_KB; A.nseg = 2;
+        B.seg[0] = B.seg[1] = eblk; B.kseg = d.R32; B.kpad = A.kpad; B.ld = d.r;
+        B.layout = LAYOUT_KB; B.nseg = 2;
+        EpiParams ep{};
+        ep.C = part; ep.ldc = d.r;
+        DSPARK_STAGE(kDw2Gemm, launch_gemm(d.dtype, EPI_PARTIAL, 3, d.Vd, d.r, A, B, 2, ep, s));
+        DSPARK_STAGE(kDw2Gemm, launch_add2(d.Vd * d.r, part, part + d.Vd * d.r,
+                                           out->d_markov_w2, s));
+      }
+    }
+  } else {
+    // fp32 operands: G in fp32, products on the fp32 MFMA with strided operands
+    float* g32 = d.gdtype == DSPARK_F32 ? nullptr : reinterpret_cast<float*>(ws + L.g32);
+    const void* gA = g32 ? static_cast<const void*>(g32) : out->d_draft_logits;
+    DSPARK_STAGE(kGradSweep, launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs,
+                                               teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
+                                               out->d_draft_logits, nullptr, nullptr, g32, s));
+    if (d.markov) {
+      {  // dE partials = G . W2 over vocabulary splits
+        Operand A{}, B{};
+        A.seg[0] = A.seg[1] = gA; A.kseg = d.Vd; A.kpad = gemm_kpad(d.Vd, 4);
+        A.ld = d.Vd; A.layout = LAYOUT_KC; A.nseg = 1;
+        B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.Vd; B.kpad = A.kpad; B.ld = d.r;
+        B.layout = LAYOUT_MC; B.nseg = 1;
+        EpiParams ep{};
+        ep.C = dEpart; ep.ldc = d.r;
+        DSPARK_STAGE(kDeGemm, launch_gemm(d.dtype, EPI_PARTIAL, 2, d.R, d.r, A, B,
+                                          static_cast<int>(d.splits), ep, s));
+      }
+      DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
+                                               dEpart, rs, d.conf_markov, in->conf_w, d.Hd, g,
+                                               c_a, dE, s));
+      DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
+      DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
+                                            out->d_markov_w1, s));
+      {  // dW2 = G^T . E (reduction over rows)
+        Operand A{}, B{};
+        A.seg[0] = A.seg[1] = gA; A.kseg = d.R; A.kpad = gemm_kpad(d.R, 4);
+        A.ld = d.Vd; A.layout = LAYOUT_MC; A.nseg = 1;
+        B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = A.kpad; B.ld = d.r;
+        B.layout = LAYOUT_MC; B.nseg = 1;
+        EpiParams ep{};
+        ep.C = out->d_markov_w2; ep.ldc = d.r;
+        DSPARK_STAGE(kDw2Gemm, launch_gemm(d.dtype, EPI_STORE, 3, d.Vd, d.r, A, B, 1, ep, s));
+      }
     }
   }
   if (d.conf) {
     float* part = reinterpret_cast<float*>(ws + L.confpart);
-    DSPARK_TRY(launch_conf_bwd(d.dtype, d.R, d.Hd, d.r, d.conf_markov, in->conf_hidden, E,
+    DSPARK_STAGE(kConfBwd, launch_conf_bwd(d.dtype, d.R, d.Hd, d.r, d.conf_markov, in->conf_hidden, E,
                                in->conf_w, rs, g, c_a, part, d.conf_chunks, out->d_conf_w,
                                out->d_conf_b, out->d_conf_hidden, s));
   }
   return DSPARK_OK;
+}
+
+int dspark_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (int i = 0; i < kStages; ++i) {
+    for (auto& pr : g_prof.pending[i]) {
+      (void)hipEventSynchronize(pr.second);
+      g_prof.pool.push_back(pr.first);
+      g_prof.pool.push_back(pr.second);
+    }
+    g_prof.pending[i].clear();
+    g_prof.ms[i] = 0.0;
+    g_prof.count[i] = 0;
+  }
+  g_prof.on.store(on != 0);
+  return DSPARK_OK;
+}
+
+int dspark_profile_read(double* ms, int64_t* counts, int n) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (int i = 0; i < kStages; ++i) {
+    for (auto& pr : g_prof.pending[i]) {
+      float t = 0.f;
+      if (hipEventSynchronize(pr.second) == hipSuccess &&
+          hipEventElapsedTime(&t, pr.first, pr.second) == hipSuccess) {
+        g_prof.ms[i] += t;
+        g_prof.count[i] += 1;
+      }
+      g_prof.pool.push_back(pr.first);
+      g_prof.pool.push_back(pr.second);
+    }
+    g_prof.pending[i].clear();
+  }
+  for (int i = 0; i < n && i < kStages; ++i) {
+    if (ms) ms[i] = g_prof.ms[i];
+    if (counts) counts[i] = g_prof.count[i];
+  }
+  return kStages;
+}
+
+const char* dspark_stage_name(int stage) {
+  return (stage >= 0 && stage < kStages) ? kStageNames[stage] : "";
 }
 
 int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,

@@ -32,11 +32,19 @@ template <> struct Elem<float> {
   static constexpr int kPerChunk = 4;  // elements per 16-byte chunk
   __device__ static float load(const float* p, int64_t i) { return p[i]; }
   __device__ static float to_f32(float x) { return x; }
+  // 4 consecutive elements (16-byte aligned) widened to fp32
+  __device__ static float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 };
 template <> struct Elem<bf16_t> {
   static constexpr int kPerChunk = 8;
   __device__ static float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   __device__ static float to_f32(bf16_t x) { return bf16_to_f32(x); }
+  // 4 consecutive elements (8-byte aligned) widened to fp32
+  __device__ static float4 load4(const bf16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
 };
 
 // The one exponential every softmax statistic and probability goes through,

@@ -7,20 +7,28 @@
 //     "DSpark Auxiliary Heads", Inputs and Outputs),
 //   - the backward products dE = G . W2 and dW2 = G^T . E.
 //
-// Design: BM x BN x BK tiles staged through LDS (double buffered, XOR-swizzled
-// 16-byte chunks so MFMA operand reads are bank-conflict free), each wave
-// computing a (BM/WM) x (BN/WN) sub-tile with 16x16 MFMAs
-// (v_mfma_f32_16x16x32_bf16 for bf16, v_mfma_f32_16x16x4_f32 for fp32).  The
-// tile order is XCD-aware (each of the 8 XCDs works a contiguous range of a
-// grouped-M ordering so operand tiles are shared through its own L2).
-// Operands may be K-contiguous or M-contiguous (the latter is transposed on its
-// way into LDS) and may consist of two K segments (used for hi/lo splits).
+// Two main loops share one tile order and one epilogue:
+//   * gemm_dma_kernel (bf16, both operands K-contiguous, K a multiple of 32):
+//     operand tiles go global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//     staging), through a 4-stage ring of BK = 32 slices prefetched 3 slices
+//     ahead, one barrier per slice.  This is the lm_head / logits path.
+//   * gemm_kernel (fp32 or bf16, any operand layout): register-staged,
+//     double-buffered LDS; operands may be K-contiguous, M-contiguous
+//     (transposed on the way into LDS) or k-blocked ([K/c][M][c] with c
+//     elements per 16-byte chunk).
+// Both: 256 x 256 output tiles, 8 waves of 128 x 64 each built from
+// v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32); LDS rows
+// of 16-byte chunks XOR-swizzled so MFMA operand reads are conflict-free; an
+// XCD-aware grouped tile order (each of the 8 XCDs works a contiguous range so
+// operand slices are shared through its own L2).  Operands may consist of two
+// K segments (used for hi/lo splits of a bf16 gradient).
 #include "common.h"
 #include "internal.h"
 
 namespace dspark {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
@@ -41,64 +49,208 @@ template <> struct Mfma<float> {
 };
 
 // Buffer resource: raw (stride 0) buffer of kNumRecords bytes; word 3 holds the
-// gfx9 data-format bits that make untyped dword loads valid.
+// gfx9 data-format bits that make untyped dword loads valid.  Offsets at or
+// past num_records read as zero.
 constexpr int kNumRecords = 0x7fffffff;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// LDS row of a tile = 8 chunks of 16 bytes; chunk c of row m sits at slot c ^ swz(m).
-__device__ __forceinline__ int swz(int m) { return (m ^ (m >> 3)) & 7; }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, kNumRecords, kRsrcWord3);
+}
 
-// Per-lane 32-bit offsets (in elements, relative to the tile base) and row
-// validity for one operand tile of ROWS rows x 8 chunks, fixed for the whole
-// K loop.  kcontig: lane chunk (row, c) -> row*ld + c*KPC; mcontig: lane chunk
-// (kr, mc) -> kr*ld + mc*KPC (KPC consecutive rows at one k).
-template <typename T, int ROWS, int NT, bool MC>
+// ------------------------------------------------------------------ tile order
+
+struct TileCoord {
+  int64_t m0, n0, tn;
+};
+
+// XCD-contiguous ranges of a grouped-M order: hardware hands consecutive
+// workgroups to the 8 XCDs in turn, so block b is remapped to give each XCD a
+// contiguous slice of the order; within it, group_m row tiles share each
+// column tile.
+__device__ __forceinline__ TileCoord tile_coord(int64_t M, int64_t N, int BM, int BN,
+                                                int group_m) {
+  const int64_t nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN;
+  const int64_t tiles = nM * nN;
+  int64_t b = blockIdx.x;
+  const int64_t per_xcd = tiles / 8;
+  if (b < per_xcd * 8) b = (b % 8) * per_xcd + b / 8;
+  const int64_t gsz = static_cast<int64_t>(group_m) * nN;
+  const int64_t fm = (b / gsz) * group_m;
+  const int64_t gm = (nM - fm) < group_m ? (nM - fm) : group_m;
+  const int64_t tm = fm + (b % gsz) % gm;
+  const int64_t tn = (b % gsz) / gm;
+  return {tm * BM, tn * BN, tn};
+}
+
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() also fences
+// global memory, which makes every wave drain its in-flight global loads and
+// stores (vmcnt(0)) at each barrier; here only LDS hazards need ordering, so
+// the wave waits for its own LDS operations (lgkmcnt(0)) and meets the others.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
+// ------------------------------------------------------------------ epilogue
+
+// The accumulator tile goes through LDS in chunks of 64 rows; 8 consecutive
+// lanes then own one 256-column row, lane sub handling columns 4 sub + 32 i
+// (i = 0..7), so a chunk's 64 rows are finished in parallel with 16-byte
+// stores, 8-byte addend loads and 3-step shuffle reductions per row.  In the
+// MFMA layout lane (g, cl) of wave (wm, wn) holds, for sub-tile (i, j) and
+// element e, the output at row wm*WTM + 16 i + 4 g + e, column wn*WTN + 16 j + cl.
+template <typename T, int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ void row_epilogue(f32x4_v (&acc)[BM / WM / 16][BN / WN / 16],
+                                             float* stage, int64_t M, int64_t N, int64_t m0,
+                                             int64_t n0, int64_t tn, const EpiParams& ep) {
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int NT = WM * WN * 64;
+  static_assert(BN == 256, "row epilogue assumes 256 columns");
+  constexpr int kChunkRows = 64;
+  constexpr int kLanesPerRow = NT / kChunkRows;      // 8
+  constexpr int kVecs = BN / 4 / kLanesPerRow;       // float4 column groups per lane (8)
+  static_assert(kLanesPerRow == 8, "8 lanes per row");
+  constexpr int kStride = BN + 4;  // floats; 4 * kStride = 16 (mod 32) banks: conflict-free writes
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int g = lane >> 4, cl = lane & 15;
+  const int rr = threadIdx.x >> 3, sub = threadIdx.x & 7;
+  float* C = ep.C;
+  if (EPI == EPI_PARTIAL) C += static_cast<int64_t>(blockIdx.y) * M * ep.ldc;
+  const T* X = static_cast<const T*>(ep.X);
+  lds_barrier();  // main-loop LDS reads are done (no LDS-DMA is in flight here)
+#pragma unroll 1
+  for (int q = 0; q < BM / kChunkRows; ++q) {
+    const int64_t row = m0 + q * kChunkRows + rr;
+    const bool rowok = row < M;
+    // addends of this lane's columns, fetched before the chunk is staged
+    float4 xs[kVecs];
+    if (EPI == EPI_STATS) {
+#pragma unroll
+      for (int i = 0; i < kVecs; ++i) {
+        const int64_t col = n0 + sub * 4 + 32 * i;
+        xs[i] = (X && rowok && col < N) ? Elem<T>::load4(X + row * ep.ldx + col)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rl = wm * WTM + i * 16 + g * 4 + e - q * kChunkRows;
+        if (rl < 0 || rl >= kChunkRows) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) stage[rl * kStride + wn * WTN + j * 16 + cl] = acc[i][j][e];
+      }
+    lds_barrier();
+    float4 v[kVecs];
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i)
+      v[i] = *reinterpret_cast<const float4*>(&stage[rr * kStride + sub * 4 + 32 * i]);
+    if (EPI == EPI_STATS) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kVecs; ++i) {
+        const int64_t col = n0 + sub * 4 + 32 * i;
+        v[i].x += xs[i].x; v[i].y += xs[i].y; v[i].z += xs[i].z; v[i].w += xs[i].w;
+        if (col < N) {  // N % 4 == 0: the 4 columns are all in or all out
+          if (rowok) *reinterpret_cast<float4*>(C + row * ep.ldc + col) = v[i];
+          mx = fmaxf(mx, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < kLanesPerRow; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+      // fixed-point sum of exp(x - max): exact integer adds, so the result does
+      // not depend on the order in which the columns are visited
+      uint64_t sum = 0;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < kVecs; ++i) {
+          const int64_t col = n0 + sub * 4 + 32 * i;
+          if (col < N) {
+            sum += static_cast<uint64_t>(rintf(dexp(v[i].x - mx) * kFixScale)) +
+                   static_cast<uint64_t>(rintf(dexp(v[i].y - mx) * kFixScale)) +
+                   static_cast<uint64_t>(rintf(dexp(v[i].z - mx) * kFixScale)) +
+                   static_cast<uint64_t>(rintf(dexp(v[i].w - mx) * kFixScale));
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < kLanesPerRow; o <<= 1) {
+        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(sum), o, kWave);
+        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(sum >> 32), o, kWave);
+        sum += (static_cast<uint64_t>(hi) << 32) | lo;
+      }
+      if (sub == 0 && rowok) {
+        const float l = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
+        ep.stats[row * ep.nstat + tn] = make_float2(mx, l);
+      }
+    } else if (rowok) {
+#pragma unroll
+      for (int i = 0; i < kVecs; ++i) {
+        const int64_t col = n0 + sub * 4 + 32 * i;
+        if (col < N) *reinterpret_cast<float4*>(C + row * ep.ldc + col) = v[i];
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// ------------------------------------------------------------------ generic kernel
+
+// LDS row of a generic tile = 8 chunks of 16 bytes; chunk c of row m sits at slot c ^ swz8(m).
+__device__ __forceinline__ int swz8(int m) { return (m ^ (m >> 3)) & 7; }
+
+// Which (row, k) of a ROWS x 8-chunk tile lane-chunk idx covers, by layout.
+// K-contiguous: chunk-fastest so a row is one 128-byte run; k-blocked:
+// row-fastest so consecutive rows of a block are one run; M-contiguous: KPC
+// consecutive rows at one k (8 such chunks side by side per k-row).
+template <int LAYOUT, int ROWS, int BK, int KPC>
+__device__ __forceinline__ void chunk_of(int idx, int* row, int* kin) {
+  if (LAYOUT == LAYOUT_KC) { *row = idx >> 3; *kin = (idx & 7) * KPC; }
+  else if (LAYOUT == LAYOUT_KB) { *row = idx % ROWS; *kin = (idx / ROWS) * KPC; }
+  else { *row = ((idx & 7) + ((idx >> 3) / BK) * 8) * KPC; *kin = (idx >> 3) % BK; }
+}
+
+template <typename T, int ROWS, int NT, int LAYOUT>
 struct TileLoader {
   static constexpr int KPC = Elem<T>::kPerChunk;
   static constexpr int PER = ROWS * 8 / NT;
   static constexpr int BK = 8 * KPC;
-  static constexpr int MCH = ROWS / KPC;
-  uint32_t off[PER];
-  uint32_t rowok;   // bit p: row of chunk p is inside the operand
-  int kofs[PER];    // k of chunk p within the K-tile
+  uint32_t off[PER];  // element offset of lane chunk p from the tile base
+  uint32_t rowok;     // bit p: the row of chunk p is inside the operand
+  int kofs[PER];      // k of chunk p within the K-tile
 
   __device__ __forceinline__ void init(const Operand& op, int64_t r0, int64_t rlim) {
     rowok = 0;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = threadIdx.x + p * NT;
       int row, k;
-      if (!MC) {
-        row = idx >> 3;
-        k = (idx & 7) * KPC;
-        off[p] = static_cast<uint32_t>(row * op.ld + k);
-      } else {
-        const int mc = (idx & 7) + ((idx >> 3) / BK) * 8;
-        k = (idx >> 3) % BK;
-        row = mc * KPC;
-        off[p] = static_cast<uint32_t>(k * op.ld + row);
-      }
+      chunk_of<LAYOUT, ROWS, BK, KPC>(threadIdx.x + p * NT, &row, &k);
+      if (LAYOUT == LAYOUT_KC) off[p] = static_cast<uint32_t>(row * op.ld + k);
+      else if (LAYOUT == LAYOUT_KB) off[p] = static_cast<uint32_t>(k * op.ld + row * KPC);
+      else off[p] = static_cast<uint32_t>(k * op.ld + row);
       kofs[p] = k;
       if (r0 + row < rlim) rowok |= 1u << p;
     }
   }
 
-  // Load K-tile kt (global k range [kt*BK, kt*BK+BK) of the padded K axis)
-  // with buffer loads: a uniform (SGPR) resource based at the tile origin and
-  // a 32-bit byte offset per lane.  Chunks outside the operand get an offset
-  // past num_records, for which the hardware returns zeros.
+  // Load K-tile kt (padded-K positions [kt*BK, kt*BK+BK)) with buffer loads
+  // based at the tile origin; chunks outside the operand read as zero.
   __device__ __forceinline__ void load(const Operand& op, int64_t r0, int kt, int64_t kend,
                                        u32x4* reg) const {
-    const int64_t kg = static_cast<int64_t>(kt) * BK;   // padded-K position (uniform)
+    const int64_t kg = static_cast<int64_t>(kt) * BK;
     const int s = static_cast<int>(kg / op.kpad);
-    const int64_t kk0 = kg - s * op.kpad;                  // k within segment s
-    const int64_t kvalid = op.kseg - kk0;                 // chunks with k < kvalid are real
-    const T* base = static_cast<const T*>(op.seg[s]) +
-                    (MC ? kk0 * op.ld + r0 : r0 * op.ld + kk0);
-    const int64_t klim = kend - kg;                        // split-K end
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, kNumRecords, kRsrcWord3);
+    const int64_t kk0 = kg - s * op.kpad;
+    const int64_t kvalid = op.kseg - kk0;
+    const int64_t rofs = LAYOUT == LAYOUT_KC ? r0 * op.ld : (LAYOUT == LAYOUT_KB ? r0 * KPC : r0);
+    const int64_t kofs0 = LAYOUT == LAYOUT_KC ? kk0 : kk0 * op.ld;
+    const T* base = static_cast<const T*>(op.seg[s]) + rofs + kofs0;
+    const int64_t klim = kend - kg;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base);
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const bool ok = ((rowok >> p) & 1u) && kofs[p] < kvalid && kofs[p] < klim;
@@ -109,37 +261,34 @@ struct TileLoader {
 };
 
 // Registers -> LDS (K-contiguous, swizzled) for the tile loaded by TileLoader.
-template <typename T, int ROWS, int NT, bool MC>
+template <typename T, int ROWS, int NT, int LAYOUT>
 __device__ __forceinline__ void store_tile(u32x4* lds, const u32x4* reg) {
   constexpr int KPC = Elem<T>::kPerChunk;
   constexpr int PER = ROWS * 8 / NT;
   constexpr int BK = 8 * KPC;
-  if (!MC) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int idx = threadIdx.x + p * NT;
-      const int row = idx >> 3, c = idx & 7;
-      lds[row * 8 + (c ^ swz(row))] = reg[p];
-    }
-  } else {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int idx = threadIdx.x + p * NT;
-      const int mc = (idx & 7) + ((idx >> 3) / BK) * 8;
-      const int kr = (idx >> 3) % BK;
-      const int kc = kr / KPC, ke = kr % KPC;
+  for (int p = 0; p < PER; ++p) {
+    int row, k;
+    chunk_of<LAYOUT, ROWS, BK, KPC>(threadIdx.x + p * NT, &row, &k);
+    if (LAYOUT != LAYOUT_MC) {
+      const int c = k / KPC;
+      lds[row * 8 + (c ^ swz8(row))] = reg[p];
+    } else {
+      const int kc = k / KPC, ke = k % KPC;
       T vals[KPC];
       __builtin_memcpy(vals, &reg[p], 16);
 #pragma unroll
       for (int j = 0; j < KPC; ++j) {
-        const int m = mc * KPC + j;
-        reinterpret_cast<T*>(&lds[m * 8 + (kc ^ swz(m))])[ke] = vals[j];
+        const int m = row + j;
+        reinterpret_cast<T*>(&lds[m * 8 + (kc ^ swz8(m))])[ke] = vals[j];
       }
     }
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int EPI, bool AMC, bool BMC>
+// TAG only names the kernel symbol per role (draft logits / teacher / backward),
+// so profilers report each role separately.
+template <typename T, int BM, int BN, int WM, int WN, int EPI, int AL, int BL, int TAG>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t N, int64_t K,
                                                               int64_t kper, Operand A, Operand B,
                                                               EpiParams ep, int group_m) {
@@ -154,20 +303,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t
   static_assert(EPI != EPI_STATS || BN == kStatTile, "stats epilogue needs BN == stat tile");
 
   __shared__ u32x4 lds[2 * (A_CH + B_CH)];
-
-  // ---- tile assignment: XCD-contiguous ranges of a grouped-M order
-  const int64_t nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN;
-  const int64_t tiles = nM * nN;
-  int64_t b = blockIdx.x;
-  const int64_t per_xcd = tiles / 8;
-  if (b < per_xcd * 8) b = (b % 8) * per_xcd + b / 8;
-  const int64_t gsz = static_cast<int64_t>(group_m) * nN;
-  const int64_t fm = (b / gsz) * group_m;
-  const int64_t gm = (nM - fm) < group_m ? (nM - fm) : group_m;
-  const int64_t tm = fm + (b % gsz) % gm;
-  const int64_t tn = (b % gsz) / gm;
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-
+  const TileCoord tc = tile_coord(M, N, BM, BN, group_m);
+  const int64_t m0 = tc.m0, n0 = tc.n0;
   const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * kper;
   const int64_t kend = (kbeg + kper) < K ? (kbeg + kper) : K;
   const int nk = kend > kbeg ? static_cast<int>((kend - kbeg + BK - 1) / BK) : 0;
@@ -183,16 +320,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
   if (nk > 0) {
-    TileLoader<T, BM, NT, AMC> la;
-    TileLoader<T, BN, NT, BMC> lb;
+    TileLoader<T, BM, NT, AL> la;
+    TileLoader<T, BN, NT, BL> lb;
     la.init(A, m0, M);
     lb.init(B, n0, N);
     const int kt0 = static_cast<int>(kbeg / BK);
     u32x4 ra[A_PER], rb[B_PER];
     la.load(A, m0, kt0, kend, ra);
     lb.load(B, n0, kt0, kend, rb);
-    store_tile<T, BM, NT, AMC>(lds, ra);
-    store_tile<T, BN, NT, BMC>(lds + A_CH, rb);
+    store_tile<T, BM, NT, AL>(lds, ra);
+    store_tile<T, BN, NT, BL>(lds + A_CH, rb);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       u32x4* As = lds + (kt & 1) * (A_CH + B_CH);
@@ -209,12 +346,12 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int m = wm * WTM + i * 16 + cl;
-          af[i] = As[m * 8 + (c ^ swz(m))];
+          af[i] = As[m * 8 + (c ^ swz8(m))];
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int n = wn * WTN + j * 16 + cl;
-          bfr[j] = Bs[n * 8 + (c ^ swz(n))];
+          bfr[j] = Bs[n * 8 + (c ^ swz8(n))];
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -223,153 +360,237 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t
       }
       if (more) {
         u32x4* An = lds + ((kt + 1) & 1) * (A_CH + B_CH);
-        store_tile<T, BM, NT, AMC>(An, ra);
-        store_tile<T, BN, NT, BMC>(An + A_CH, rb);
+        store_tile<T, BM, NT, AL>(An, ra);
+        store_tile<T, BN, NT, BL>(An + A_CH, rb);
       }
       __syncthreads();
     }
   }
-
-  // ---- epilogue.  Lane (g, cl) of wave (wm, wn) holds, for sub-tile (i, j) and
-  // element e, the output at row wm*WTM + 16 i + 4 g + e, column wn*WTN + 16 j + cl.
-  if (EPI == EPI_STORE || EPI == EPI_PARTIAL) {
-    float* C = ep.C;
-    if (EPI == EPI_PARTIAL) C += static_cast<int64_t>(blockIdx.y) * M * ep.ldc;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + wm * WTM + i * 16 + g * 4 + e;
-        if (row >= M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t col = n0 + wn * WTN + j * 16 + cl;
-          if (col < N) C[row * ep.ldc + col] = acc[i][j][e];
-        }
-      }
-    return;
-  }
-
-  // EPI_STATS: C = acc (+ X), plus per-(row, stat tile) max and fixed-point exp-sum.
-  const T* X = static_cast<const T*>(ep.X);
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t row = m0 + wm * WTM + i * 16 + g * 4 + e;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = n0 + wn * WTN + j * 16 + cl;
-        float x = acc[i][j][e];
-        if (row < M && col < N) {
-          if (X) x += Elem<T>::to_f32(X[row * ep.ldx + col]);
-          ep.C[row * ep.ldc + col] = x;
-        }
-        acc[i][j][e] = x;
-      }
-    }
-  float* smax = reinterpret_cast<float*>(lds);           // [WN][BM]
-  uint64_t* ssum = reinterpret_cast<uint64_t*>(smax + WN * BM);        // [WN][BM]
-  // row maxima over this wave's columns, then across the WN waves of the row
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = n0 + wn * WTN + j * 16 + cl;
-        if (col < N) mx = fmaxf(mx, acc[i][j][e]);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-      if (cl == 0) smax[wn * BM + wm * WTM + i * 16 + g * 4 + e] = mx;
-    }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rl = wm * WTM + i * 16 + g * 4 + e;
-      float mx = smax[rl];
-#pragma unroll
-      for (int w = 1; w < WN; ++w) mx = fmaxf(mx, smax[w * BM + rl]);
-      uint64_t sum = 0;
-      if (mx != -INFINITY) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t col = n0 + wn * WTN + j * 16 + cl;
-          if (col < N) sum += static_cast<uint64_t>(rintf(dexp(acc[i][j][e] - mx) * kFixScale));
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(sum), o, kWave);
-        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(sum >> 32), o, kWave);
-        sum += (static_cast<uint64_t>(hi) << 32) | lo;
-      }
-      if (cl == 0) ssum[wn * BM + rl] = sum;
-    }
-  __syncthreads();
-  if (wn == 0 && cl == 0) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rl = wm * WTM + i * 16 + g * 4 + e;
-        const int64_t row = m0 + rl;
-        if (row >= M) continue;
-        float mx = smax[rl];
-        uint64_t sum = ssum[rl];
-#pragma unroll
-        for (int w = 1; w < WN; ++w) {
-          mx = fmaxf(mx, smax[w * BM + rl]);
-          sum += ssum[w * BM + rl];
-        }
-        const float l = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
-        ep.stats[row * ep.nstat + tn] = make_float2(mx, l);
-      }
-  }
+  row_epilogue<T, BM, BN, WM, WN, EPI>(acc, reinterpret_cast<float*>(lds), M, N, m0, n0, tc.tn,
+                                       ep);
 }
+
+// ------------------------------------------------------------------ LDS-DMA kernel
+
+// bf16; each operand K-contiguous (LAYOUT_KC) or k-blocked by 8 (LAYOUT_KB);
+// every K segment a multiple of 32.  LDS slice row = 32 bf16 = 4 chunks; chunk
+// c of row m sits at slot c ^ swz4(m).
+__device__ __forceinline__ int swz4(int m) { return (m >> 1) & 3; }
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier of the DMA loop: lds_barrier(), after each wave waited for
+// its own DMA slices explicitly (a fence would drain every in-flight slice).
+__device__ __forceinline__ void dma_barrier() { lds_barrier(); }
+
+// DMA slice t of a split into stage t % STAGES: the wave's p-th A load fills
+// LDS chunks [(wave*A_LD + p) * 64, +64) of the stage (B after A_CH chunks).
+// Element offset of chunk (row, c) of a 32-wide K slice, and of the slice base.
+template <int LAYOUT>
+__device__ __forceinline__ int64_t dma_chunk(int row, int c, int64_t ld) {
+  return LAYOUT == LAYOUT_KB ? static_cast<int64_t>(c) * 8 * ld + row * 8 : row * ld + c * 8;
+}
+template <int LAYOUT>
+__device__ __forceinline__ int64_t dma_base(int64_t r0, int64_t kk, int64_t ld) {
+  return LAYOUT == LAYOUT_KB ? r0 * 8 + kk * ld : r0 * ld + kk;
+}
+
+template <int AL, int BL, int A_LD, int B_LD, int A_CH, int STAGE_CH, int STAGES>
+__device__ __forceinline__ void dma_issue(const Operand& A, const Operand& B, int64_t kbeg, int t,
+                                          int64_t m0, int64_t n0, int wave, const uint32_t* offA,
+                                          const uint32_t* offB, u32x4* lds) {
+  const int64_t kg = kbeg + static_cast<int64_t>(t) * 32;
+  const bool s1 = kg >= A.kseg;  // at most two K segments
+  const int64_t kk = s1 ? kg - A.kseg : kg;
+  const bf16_t* abase = static_cast<const bf16_t*>(s1 ? A.seg[1] : A.seg[0]);
+  const bf16_t* bbase = static_cast<const bf16_t*>(s1 ? B.seg[1] : B.seg[0]);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase + dma_base<AL>(m0, kk, A.ld));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase + dma_base<BL>(n0, kk, B.ld));
+  u32x4* st = lds + (t % STAGES) * STAGE_CH;
+#pragma unroll
+  for (int p = 0; p < A_LD; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave * A_LD + p) * 64), 16,
+                                             offA[p], 0, 0, 0);
+#pragma unroll
+  for (int p = 0; p < B_LD; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + A_CH + (wave * B_LD + p) * 64),
+                                             16, offB[p], 0, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int AL, int BL, int TAG>
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int64_t N, int64_t K,
+                                                                  int64_t kper, Operand A,
+                                                                  Operand B, EpiParams ep,
+                                                                  int group_m) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int NW = NT / 64;
+  constexpr int BK = 32;
+  constexpr int STAGES = 4;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int A_CH = BM * 4, B_CH = BN * 4;                 // 16-byte chunks per slice
+  constexpr int A_LD = A_CH / 64 / NW, B_LD = B_CH / 64 / NW;  // DMA loads per wave per slice
+  constexpr int STAGE_CH = A_CH + B_CH;
+  static_assert(A_CH % (64 * NW) == 0 && B_CH % (64 * NW) == 0, "tile / wave mismatch");
+  static_assert(STAGES * STAGE_CH * 16 <= 160 * 1024, "LDS budget");
+  static_assert(EPI != EPI_STATS || BN == kStatTile, "stats epilogue needs BN == stat tile");
+
+  __shared__ u32x4 lds[STAGES * STAGE_CH];
+  const TileCoord tc = tile_coord(M, N, BM, BN, group_m);
+  const int64_t m0 = tc.m0, n0 = tc.n0;
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * kper;
+  const int64_t kend = (kbeg + kper) < K ? (kbeg + kper) : K;
+  const int nk = kend > kbeg ? static_cast<int>((kend - kbeg) / BK) : 0;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int g = lane >> 4, cl = lane & 15;
+
+  // Lane chunk of each DMA load: the wave's p-th load fills LDS chunks
+  // [(wave*X_LD + p) * 64, +64) of the slice, lane l the one at +l, i.e. row
+  // idx / 4, slot idx % 4, which holds global chunk slot ^ swz4(row).
+  uint32_t offA[A_LD], offB[B_LD];
+#pragma unroll
+  for (int p = 0; p < A_LD; ++p) {
+    const int idx = (wave * A_LD + p) * 64 + lane;
+    const int row = idx >> 2, c = (idx & 3) ^ swz4(idx >> 2);
+    offA[p] = (m0 + row < M) ? static_cast<uint32_t>(dma_chunk<AL>(row, c, A.ld) * 2) : kOutOfRange;
+  }
+#pragma unroll
+  for (int p = 0; p < B_LD; ++p) {
+    const int idx = (wave * B_LD + p) * 64 + lane;
+    const int row = idx >> 2, c = (idx & 3) ^ swz4(idx >> 2);
+    offB[p] = (n0 + row < N) ? static_cast<uint32_t>(dma_chunk<BL>(row, c, B.ld) * 2) : kOutOfRange;
+  }
+
+  f32x4_v acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int LPS = A_LD + B_LD;  // loads per wave per slice
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < nk)
+      dma_issue<AL, BL, A_LD, B_LD, A_CH, STAGE_CH, STAGES>(A, B, kbeg, t, m0, n0, wave, offA, offB,
+                                                            lds);
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt has landed once at most (slices issued after it) * LPS loads remain
+    const int after = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
+    if (after >= 2) wait_vmcnt<2 * LPS>();
+    else if (after == 1) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    dma_barrier();  // every wave's slice-kt loads are in LDS; slice kt-1 is consumed
+    if (kt + STAGES - 1 < nk)
+      dma_issue<AL, BL, A_LD, B_LD, A_CH, STAGE_CH, STAGES>(A, B, kbeg, kt + STAGES - 1, m0, n0,
+                                                            wave, offA, offB, lds);
+    const u32x4* As = lds + (kt % STAGES) * STAGE_CH;
+    const u32x4* Bs = As + A_CH;
+    u32x4 af[TM], bfr[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * WTM + i * 16 + cl;
+      af[i] = As[m * 4 + (g ^ swz4(m))];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = wn * WTN + j * 16 + cl;
+      bfr[j] = Bs[n * 4 + (g ^ swz4(n))];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) Mfma<bf16_t>::run(acc[i][j], af[i], bfr[j]);
+  }
+  row_epilogue<bf16_t, BM, BN, WM, WN, EPI>(acc, reinterpret_cast<float*>(lds), M, N, m0, n0,
+                                            tc.tn, ep);
+}
+
+// ------------------------------------------------------------------ launch
 
 namespace {
 constexpr int kGroupM = 8;
 
-template <typename T, int BM, int BN, int WM, int WN, int EPI, bool AMC, bool BMC>
-hipError_t launch_cfg(int64_t M, int64_t N, const Operand& A, const Operand& B, int splits,
-                      const EpiParams& ep, hipStream_t s) {
+int64_t split_kper(int64_t K, int splits, int bk) {
+  if (splits <= 1) return K;
+  return ((K + splits - 1) / splits + bk - 1) / bk * bk;
+}
+
+template <typename T, int EPI, int AL, int BL, int TAG>
+hipError_t launch_generic(int64_t M, int64_t N, const Operand& A, const Operand& B, int splits,
+                          const EpiParams& ep, hipStream_t s) {
   constexpr int BK = 8 * Elem<T>::kPerChunk;
   const int64_t K = A.kpad * A.nseg;
-  const int64_t nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN;
-  int64_t kper = K;
-  if (splits > 1) kper = ((K + splits - 1) / splits + BK - 1) / BK * BK;
+  const int64_t nM = (M + 255) / 256, nN = (N + 255) / 256;
   dim3 grid(static_cast<uint32_t>(nM * nN), static_cast<uint32_t>(splits), 1);
-  if (A.mcontig != AMC || B.mcontig != BMC) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI, AMC, BMC>), grid, dim3(WM * WN * 64), 0, s, M, N,
-                     K, kper, A, B, ep, kGroupM);
+  hipLaunchKernelGGL((gemm_kernel<T, 256, 256, 2, 4, EPI, AL, BL, TAG>), grid, dim3(512), 0, s, M,
+                     N, K, split_kper(K, splits, BK), A, B, ep, kGroupM);
   return hipGetLastError();
 }
 
+template <int EPI, int AL, int BL, int TAG>
+hipError_t launch_dma(int64_t M, int64_t N, const Operand& A, const Operand& B, int splits,
+                      const EpiParams& ep, hipStream_t s) {
+  const int64_t K = A.kseg * A.nseg;
+  const int64_t nM = (M + 255) / 256, nN = (N + 255) / 256;
+  dim3 grid(static_cast<uint32_t>(nM * nN), static_cast<uint32_t>(splits), 1);
+  hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 2, 4, EPI, AL, BL, TAG>), grid, dim3(512), 0, s, M,
+                     N, K, split_kper(K, splits, 32), A, B, ep, kGroupM);
+  return hipGetLastError();
+}
+
+// The DMA path needs bf16, K-contiguous (or both k-blocked) operands and
+// 32-aligned K segments.
+bool dma_ok(const Operand& A, const Operand& B) {
+  const bool kc = A.layout == LAYOUT_KC && B.layout == LAYOUT_KC;
+  const bool kb = A.layout == LAYOUT_KB && B.layout == LAYOUT_KB;
+  return (kc || kb) && A.kseg % 32 == 0 && A.kseg > 0 && A.kseg == B.kseg && A.nseg == B.nseg;
+}
+
 template <typename T>
-hipError_t launch_t(int epi, int64_t M, int64_t N, const Operand& A, const Operand& B, int splits,
-                    const EpiParams& ep, hipStream_t s) {
-  switch (epi) {
-    // logits / teacher projections: both operands K-contiguous
-    case EPI_STATS: return launch_cfg<T, 256, 256, 2, 4, EPI_STATS, false, false>(M, N, A, B, 1, ep, s);
-    // dW2 = G^T . E: both operands row-strided along K
-    case EPI_STORE: return launch_cfg<T, 256, 256, 2, 4, EPI_STORE, true, true>(M, N, A, B, 1, ep, s);
-    // dE = G . W2 (split over the vocabulary): A K-contiguous, B row-strided
-    case EPI_PARTIAL: return launch_cfg<T, 256, 256, 2, 4, EPI_PARTIAL, false, true>(M, N, A, B, splits, ep, s);
+hipError_t launch_t(int epi, int tag, int64_t M, int64_t N, const Operand& A, const Operand& B,
+                    int splits, const EpiParams& ep, hipStream_t s) {
+  const bool kc = A.layout == LAYOUT_KC && B.layout == LAYOUT_KC;
+  if (epi == EPI_STATS) {
+    if (!kc) return hipErrorInvalidValue;
+    return tag == 1 ? launch_generic<T, EPI_STATS, LAYOUT_KC, LAYOUT_KC, 1>(M, N, A, B, 1, ep, s)
+                    : launch_generic<T, EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, A, B, 1, ep, s);
   }
+  if (epi == EPI_PARTIAL && A.layout == LAYOUT_KC && B.layout == LAYOUT_MC)
+    return launch_generic<T, EPI_PARTIAL, LAYOUT_KC, LAYOUT_MC, 2>(M, N, A, B, splits, ep, s);
+  if (epi == EPI_PARTIAL && kc)
+    return launch_generic<T, EPI_PARTIAL, LAYOUT_KC, LAYOUT_KC, 2>(M, N, A, B, splits, ep, s);
+  if (epi == EPI_PARTIAL && A.layout == LAYOUT_KB && B.layout == LAYOUT_KB)
+    return launch_generic<T, EPI_PARTIAL, LAYOUT_KB, LAYOUT_KB, 3>(M, N, A, B, splits, ep, s);
+  if (epi == EPI_STORE && A.layout == LAYOUT_MC && B.layout == LAYOUT_MC)
+    return launch_generic<T, EPI_STORE, LAYOUT_MC, LAYOUT_MC, 3>(M, N, A, B, 1, ep, s);
   return hipErrorInvalidValue;
 }
 }  // namespace
 
-hipError_t launch_gemm(int dtype, int epi, int64_t M, int64_t N, const Operand& A,
+hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const Operand& A,
                        const Operand& B, int splits, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  return dtype == 1 ? launch_t<bf16_t>(epi, M, N, A, B, splits, ep, s)
-                    : launch_t<float>(epi, M, N, A, B, splits, ep, s);
+  if (dtype == 1 && dma_ok(A, B)) {
+    if (A.layout == LAYOUT_KB) {
+      if (epi == EPI_PARTIAL)
+        return launch_dma<EPI_PARTIAL, LAYOUT_KB, LAYOUT_KB, 3>(M, N, A, B, splits, ep, s);
+    } else {
+      if (epi == EPI_STATS)
+        return tag == 1 ? launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 1>(M, N, A, B, 1, ep, s)
+                        : launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, A, B, 1, ep, s);
+      if (epi == EPI_PARTIAL)
+        return launch_dma<EPI_PARTIAL, LAYOUT_KC, LAYOUT_KC, 2>(M, N, A, B, splits, ep, s);
+    }
+  }
+  return dtype == 1 ? launch_t<bf16_t>(epi, tag, M, N, A, B, splits, ep, s)
+                    : launch_t<float>(epi, tag, M, N, A, B, splits, ep, s);
 }
 
 }  // namespace dspark

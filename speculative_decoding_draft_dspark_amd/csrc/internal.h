@@ -10,15 +10,20 @@ namespace dspark {
 // The K axis is padded: segment s covers k in [s*kpad, s*kpad + kseg), and
 // k in [s*kpad + kseg, (s+1)*kpad) reads as zero.  kpad must be a multiple of
 // the GEMM's BK (64 for bf16, 32 for fp32) and equal for A and B.
-//   kcontig: element (i, k) of segment s at seg[s][i * ld + k]  (row i K-contiguous)
-//   mcontig: element (i, k) of segment s at seg[s][k * ld + i]  (row i strided)
+//   LAYOUT_KC: element (i, k) of segment s at seg[s][i * ld + k]   (row i K-contiguous)
+//   LAYOUT_MC: element (i, k) of segment s at seg[s][k * ld + i]   (row i strided)
+//   LAYOUT_KB: element (i, k) of segment s at
+//              seg[s][(k / c) * c * ld + i * c + k % c]  (k-blocked: c = elements per
+//              16-byte chunk, i.e. c consecutive k of one row are contiguous)
 // Byte offsets i*ld + k (resp. k*ld + i) within one 256-row tile must stay below 2^31.
+enum OperandLayout { LAYOUT_KC = 0, LAYOUT_MC = 1, LAYOUT_KB = 2 };
+
 struct Operand {
   const void* seg[2];
   int64_t kseg;
   int64_t kpad;
   int64_t ld;
-  int mcontig;
+  int layout;
   int nseg;
 };
 
@@ -39,8 +44,9 @@ struct EpiParams {
   int64_t nstat;
 };
 
-// dtype: 0 = fp32, 1 = bf16.  splits > 1 only with EPI_PARTIAL.
-hipError_t launch_gemm(int dtype, int epi, int64_t M, int64_t N, const Operand& A,
+// dtype: 0 = fp32, 1 = bf16.  splits > 1 only with EPI_PARTIAL.  tag (EPI_STATS):
+// 0 = corrected draft logits, 1 = teacher logits (separate kernel symbols).
+hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const Operand& A,
                        const Operand& B, int splits, const EpiParams& ep, hipStream_t s);
 
 }  // namespace dspark

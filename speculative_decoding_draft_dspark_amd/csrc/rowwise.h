@@ -47,6 +47,16 @@ hipError_t launch_grad_sweep(int grad_dtype, int64_t R, int64_t V, const float* 
                              const float* Tt, const int32_t* tid, RowState rs, int has_teacher,
                              float g, float ce_a, float l1_a, void* dz, bf16_t* ghi, bf16_t* glo,
                              float* g32, hipStream_t s);
+hipError_t launch_grad_sweep8(int grad_dtype, int64_t R, int64_t rgroups, int64_t V,
+                              const float* Zp, const float* Tt, const int32_t* tid, RowState rs,
+                              int has_teacher, float g, float ce_a, float l1_a, void* dz,
+                              bf16_t* ghi_rm, bf16_t* glo_rm, bf16_t* blk_hi, bf16_t* blk_lo,
+                              hipStream_t s);
+hipError_t launch_transpose_bf16(int64_t rows, int64_t cols, const void* in, void* out,
+                                 hipStream_t s);
+hipError_t launch_embed_blocked(int64_t R, int64_t rgroups, int64_t rank, const void* E, void* out,
+                                hipStream_t s);
+hipError_t launch_add2(int64_t n, const float* a, const float* b, float* out, hipStream_t s);
 hipError_t launch_de_reduce(int dtype, int64_t R, int64_t rank, int splits, const float* part,
                             RowState rs, int conf_markov, const void* Wc, int64_t Hd, float g,
                             float c_a, float* dE, hipStream_t s);

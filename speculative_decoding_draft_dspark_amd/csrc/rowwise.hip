@@ -446,6 +446,194 @@ hipError_t launch_grad_sweep(int grad_dtype, int64_t R, int64_t V, const float* 
   return hipGetLastError();
 }
 
+// 8-row gradient sweep (bf16 operands).  One workgroup per group of 8 rows;
+// thread t handles 4 consecutive vocabulary entries at a time for all 8 rows, so
+// besides dz and the row-major low part of G it can write G in the k-blocked
+// layout [rows/8][V][8] (8 consecutive rows of one entry in 16 bytes) that the
+// row-contracting product dW2 = G^T E reads as K-contiguous chunks.
+// hi = bf16(G) is dz itself when dz is bf16, else written to ghi_rm.
+template <typename GT>
+__global__ __launch_bounds__(kSweepThreads) void grad_sweep8_kernel(
+    int64_t R, int64_t V, const float* Zp, const float* Tt, const int32_t* tid, RowState rs,
+    int has_teacher, float g, float ce_a, float l1_a, GT* dz, bf16_t* ghi_rm, bf16_t* glo_rm,
+    bf16_t* blk_hi, bf16_t* blk_lo) {
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 8;
+  bool mk[8];
+  float lz[8], lt[8], cc[8], cl[8], Sr[8];
+  int32_t yy[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t r = r0 + j;
+    mk[j] = r < R && rs.mask[r] != 0;
+    const float gw = mk[j] ? g * rs.w[r] : 0.f;
+    lz[j] = mk[j] ? rs.lse_z[r] : 0.f;
+    lt[j] = mk[j] ? rs.lse_t[r] : 0.f;
+    Sr[j] = mk[j] ? rs.S[r] : 0.f;
+    cc[j] = gw * ce_a;
+    cl[j] = gw * l1_a;
+    int32_t y = mk[j] ? tid[r] : -1;
+    yy[j] = mk[j] ? (y < 0 ? 0 : (y >= V ? static_cast<int32_t>(V - 1) : y)) : -1;
+  }
+  const int64_t n4 = V / 4;
+  for (int64_t c = threadIdx.x; c < n4; c += kSweepThreads) {
+    const int64_t v0 = 4 * c;
+    float G[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) G[j][e] = 0.f;
+      if (!mk[j]) continue;
+      const int64_t r = r0 + j;
+      const float4 zz = reinterpret_cast<const float4*>(Zp + r * V)[c];
+      const float p[4] = {dexp(zz.x - lz[j]), dexp(zz.y - lz[j]), dexp(zz.z - lz[j]),
+                          dexp(zz.w - lz[j])};
+      if (has_teacher) {
+        const float4 tt = reinterpret_cast<const float4*>(Tt + r * V)[c];
+        const float q[4] = {dexp(tt.x - lt[j]), dexp(tt.y - lt[j]), dexp(tt.z - lt[j]),
+                            dexp(tt.w - lt[j])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) G[j][e] = p[e] * (cc[j] + cl[j] * (sgnf(p[e] - q[e]) - Sr[j]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) G[j][e] = p[e] * cc[j];
+      }
+      if (yy[j] >= v0 && yy[j] < v0 + 4) G[j][yy[j] - v0] -= cc[j];
+    }
+    uint32_t hi[8][2], lo[8][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16(G[j][e]);
+        l[e] = f32_to_bf16(G[j][e] - bf16_to_f32(h[e]));
+      }
+      hi[j][0] = h[0] | (static_cast<uint32_t>(h[1]) << 16);
+      hi[j][1] = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+      lo[j][0] = l[0] | (static_cast<uint32_t>(l[1]) << 16);
+      lo[j][1] = l[2] | (static_cast<uint32_t>(l[3]) << 16);
+      const int64_t r = r0 + j;
+      if (r < R) {
+        if (sizeof(GT) == 2) {
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(dz) + r * V + v0) =
+              make_uint2(hi[j][0], hi[j][1]);
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(dz) + r * V + v0) =
+              make_float4(G[j][0], G[j][1], G[j][2], G[j][3]);
+          *reinterpret_cast<uint2*>(ghi_rm + r * V + v0) = make_uint2(hi[j][0], hi[j][1]);
+        }
+        *reinterpret_cast<uint2*>(glo_rm + r * V + v0) = make_uint2(lo[j][0], lo[j][1]);
+      }
+    }
+    // blocked: entry v0 + e of this row group = rows 0..7 packed in 16 bytes
+    uint4* bh = reinterpret_cast<uint4*>(blk_hi + (static_cast<int64_t>(blockIdx.x) * V + v0) * 8);
+    uint4* bl = reinterpret_cast<uint4*>(blk_lo + (static_cast<int64_t>(blockIdx.x) * V + v0) * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      uint4 H, L;
+      H.x = ((hi[0][w] >> sh) & 0xffffu) | (((hi[1][w] >> sh) & 0xffffu) << 16);
+      H.y = ((hi[2][w] >> sh) & 0xffffu) | (((hi[3][w] >> sh) & 0xffffu) << 16);
+      H.z = ((hi[4][w] >> sh) & 0xffffu) | (((hi[5][w] >> sh) & 0xffffu) << 16);
+      H.w = ((hi[6][w] >> sh) & 0xffffu) | (((hi[7][w] >> sh) & 0xffffu) << 16);
+      L.x = ((lo[0][w] >> sh) & 0xffffu) | (((lo[1][w] >> sh) & 0xffffu) << 16);
+      L.y = ((lo[2][w] >> sh) & 0xffffu) | (((lo[3][w] >> sh) & 0xffffu) << 16);
+      L.z = ((lo[4][w] >> sh) & 0xffffu) | (((lo[5][w] >> sh) & 0xffffu) << 16);
+      L.w = ((lo[6][w] >> sh) & 0xffffu) | (((lo[7][w] >> sh) & 0xffffu) << 16);
+      bh[e] = H;
+      bl[e] = L;
+    }
+  }
+}
+
+hipError_t launch_grad_sweep8(int grad_dtype, int64_t R, int64_t rgroups, int64_t V,
+                              const float* Zp, const float* Tt, const int32_t* tid, RowState rs,
+                              int has_teacher, float g, float ce_a, float l1_a, void* dz,
+                              bf16_t* ghi_rm, bf16_t* glo_rm, bf16_t* blk_hi, bf16_t* blk_lo,
+                              hipStream_t s) {
+  if (rgroups <= 0) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>(rgroups));
+  if (grad_dtype == 1)
+    hipLaunchKernelGGL(grad_sweep8_kernel<bf16_t>, grid, dim3(kSweepThreads), 0, s, R, V, Zp, Tt,
+                       tid, rs, has_teacher, g, ce_a, l1_a, static_cast<bf16_t*>(dz), ghi_rm,
+                       glo_rm, blk_hi, blk_lo);
+  else
+    hipLaunchKernelGGL(grad_sweep8_kernel<float>, grid, dim3(kSweepThreads), 0, s, R, V, Zp, Tt,
+                       tid, rs, has_teacher, g, ce_a, l1_a, static_cast<float*>(dz), ghi_rm,
+                       glo_rm, blk_hi, blk_lo);
+  return hipGetLastError();
+}
+
+// out[c, r] = in[r, c] for a [rows, cols] bf16 matrix, through 64 x 64 LDS tiles.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(int64_t rows, int64_t cols,
+                                                             const bf16_t* in, bf16_t* out) {
+  __shared__ bf16_t t[64][66];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    t[i][tx] = (r < rows && c < cols) ? in[r * cols + c] : bf16_t(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) out[c * rows + r] = t[tx][i];
+  }
+}
+
+hipError_t launch_transpose_bf16(int64_t rows, int64_t cols, const void* in, void* out,
+                                 hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>((cols + 63) / 64), static_cast<uint32_t>((rows + 63) / 64));
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, rows, cols,
+                     static_cast<const bf16_t*>(in), static_cast<bf16_t*>(out));
+  return hipGetLastError();
+}
+
+// Eblk[rg, j, 0..7] = E[8 rg + 0..7, j] (zero past R), rg < rgroups.
+__global__ void embed_blocked_kernel(int64_t R, int64_t rgroups, int64_t rank, const bf16_t* E,
+                                     bf16_t* out) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= rgroups * rank) return;
+  const int64_t rg = i / rank, j = i - rg * rank;
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t ra = rg * 8 + 2 * k, rb = ra + 1;
+    const uint32_t a = ra < R ? E[ra * rank + j] : 0u;
+    const uint32_t b = rb < R ? E[rb * rank + j] : 0u;
+    w[k] = a | (b << 16);
+  }
+  reinterpret_cast<uint4*>(out)[i] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+hipError_t launch_embed_blocked(int64_t R, int64_t rgroups, int64_t rank, const void* E, void* out,
+                                hipStream_t s) {
+  const int64_t n = rgroups * rank;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_blocked_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256),
+                     0, s, R, rgroups, rank, static_cast<const bf16_t*>(E),
+                     static_cast<bf16_t*>(out));
+  return hipGetLastError();
+}
+
+// out = a + b (fp32, n a multiple of 4).
+__global__ void add2_kernel(int64_t n4, const float4* a, const float4* b, float4* out) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= n4) return;
+  const float4 x = a[i], y = b[i];
+  out[i] = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+}
+
+hipError_t launch_add2(int64_t n, const float* a, const float* b, float* out, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(add2_kernel, dim3(static_cast<uint32_t>((n4 + 255) / 256)), dim3(256), 0, s,
+                     n4, reinterpret_cast<const float4*>(a), reinterpret_cast<const float4*>(b),
+                     reinterpret_cast<float4*>(out));
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- backward helpers
 
 // dE[r, j] = sum_s part[s, r, j] + dc_r W_c[Hd + j]  (dc_r = g w_r c_a (sigmoid(c_r) - accept_r)),

@@ -259,7 +259,7 @@ def test_full_size_gradients_additive_and_sub_batch_parity(idx):
     nb = wl.B * wl.N
     parts = np.array_split(np.arange(nb), 4)
     acc = {k: torch.zeros_like(v, dtype=torch.float64) for k, v in g.items()
-           if k != "d_draft_logits"}
+           if k not in ("d_draft_logits", "d_conf_hidden")}
     loss = 0.0
     for i, blocks in enumerate(parts):
         sub = subset_blocks(d, blocks)
