@@ -144,13 +144,14 @@ def main():
     ms_step = 1000.0 * elapsed / args.steps
     rows_per_s = R * args.steps / elapsed
 
-    gemm_ms = _avg_ms(stages, "teacher_gemm")
-    gemm_flops = 2.0 * R * V * H
+    gemm_ms = _avg_ms(stages, "logits_gemm")
+    gemm_flops = 2.0 * R * V * (H + r)   # teacher projection (K = H) + Markov bias (K = r)
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "teacher_gemm (lm_head projection, bf16 MFMA)",
+    roofline = {"bound": "mfma",
+                "kernel": "logits_gemm (lm_head projection + Markov-corrected draft logits, bf16 MFMA)",
                 "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": _traffic("teacher_gemm"),
+                "traffic": _traffic("logits_gemm"),
                 "flops_per_launch": gemm_flops, "avg_ms": round(gemm_ms, 4)}
 
     # row sweeps: algorithmic bytes per launch / average duration

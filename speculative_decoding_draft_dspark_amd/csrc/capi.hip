@@ -134,11 +134,11 @@ enum Teacher { kNone = 0, kHidden = 1, kAligned = 2 };
 
 // ---- per-stage timers (tracing aid)
 enum Stage {
-  kPrep, kGather, kDraftGemm, kTeacherGemm, kL1Sweep, kFinalize, kReduce, kGradSweep, kDeGemm,
+  kPrep, kGather, kLogitsGemm, kL1Sweep, kFinalize, kReduce, kGradSweep, kDeGemm,
   kDeReduce, kDw1, kDw2Gemm, kConfBwd, kStages
 };
 const char* const kStageNames[kStages] = {
-    "prep_rows", "gather_embed", "draft_logits_gemm", "teacher_gemm", "l1_sweep",
+    "prep_rows", "gather_embed", "logits_gemm", "l1_sweep",
     "finalize_rows", "reduce_fwd", "grad_sweep", "dE_gemm", "dE_reduce", "dW1_scatter",
     "dW2_gemm", "conf_bwd"};
 
@@ -265,32 +265,33 @@ int dspark_loss_fwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     DSPARK_STAGE(kGather, launch_gather_embed(d.dtype, d.R, d.r, d.Vt, in->prev_ids, rs.mask, in->markov_w1,
                                    E, s));
 
-  // corrected draft logits z' = z + E W2^T (fp32) with per-tile softmax statistics
+  // Corrected draft logits z' = z + E W2^T and teacher logits T (both fp32),
+  // each with per-tile softmax statistics, over the same [R, Vd] tile grid.
   {
-    Operand A{}, B{};
-    A.seg[0] = A.seg[1] = E; A.kseg = d.r; A.kpad = gemm_kpad(d.r, d.esize); A.ld = d.r;
-    A.layout = LAYOUT_KC; A.nseg = 1;
-    B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.r; B.kpad = A.kpad; B.ld = d.r;
-    B.layout = LAYOUT_KC; B.nseg = 1;
-    EpiParams ep{};
-    ep.C = Zp; ep.ldc = d.Vd; ep.X = in->draft_logits; ep.ldx = d.Vd; ep.stats = sz;
-    ep.nstat = d.nstat;
-    DSPARK_STAGE(kDraftGemm, launch_gemm(d.dtype, EPI_STATS, 0, d.R, d.Vd, A, B, 1, ep, s));
-  }
-  // teacher logits T (fp32) with the same statistics
-  if (teacher != kNone) {
-    Operand A{}, B{};
-    EpiParams ep{};
-    ep.C = T; ep.ldc = d.Vd; ep.stats = stt; ep.nstat = d.nstat;
-    if (teacher == kHidden) {
-      A.seg[0] = A.seg[1] = in->target_hidden; A.kseg = d.H; A.kpad = gemm_kpad(d.H, d.esize);
-      A.ld = d.H; A.nseg = 1;
-      B.seg[0] = B.seg[1] = in->lm_head; B.kseg = d.H; B.kpad = A.kpad; B.ld = d.H; B.nseg = 1;
-    } else {
-      A.nseg = B.nseg = 1;  // K = 0: T = aligned logits
-      ep.X = in->aligned_target_logits; ep.ldx = d.Vd;
+    Operand A[2] = {}, B[2] = {};
+    EpiParams ep[2] = {};
+    A[0].seg[0] = A[0].seg[1] = E; A[0].kseg = d.r; A[0].kpad = gemm_kpad(d.r, d.esize);
+    A[0].ld = d.r; A[0].layout = LAYOUT_KC; A[0].nseg = 1;
+    B[0].seg[0] = B[0].seg[1] = in->markov_w2; B[0].kseg = d.r; B[0].kpad = A[0].kpad;
+    B[0].ld = d.r; B[0].layout = LAYOUT_KC; B[0].nseg = 1;
+    ep[0].C = Zp; ep[0].ldc = d.Vd; ep[0].X = in->draft_logits; ep[0].ldx = d.Vd;
+    ep[0].stats = sz; ep[0].nstat = d.nstat;
+    int njobs = 1;
+    if (teacher != kNone) {
+      njobs = 2;
+      ep[1].C = T; ep[1].ldc = d.Vd; ep[1].stats = stt; ep[1].nstat = d.nstat;
+      A[1].nseg = B[1].nseg = 1;
+      A[1].layout = B[1].layout = LAYOUT_KC;
+      if (teacher == kHidden) {
+        A[1].seg[0] = A[1].seg[1] = in->target_hidden; A[1].kseg = d.H;
+        A[1].kpad = gemm_kpad(d.H, d.esize); A[1].ld = d.H;
+        B[1].seg[0] = B[1].seg[1] = in->lm_head; B[1].kseg = d.H; B[1].kpad = A[1].kpad;
+        B[1].ld = d.H;
+      } else {  // K = 0: T = aligned logits
+        ep[1].X = in->aligned_target_logits; ep[1].ldx = d.Vd;
+      }
     }
-    DSPARK_STAGE(kTeacherGemm, launch_gemm(d.dtype, EPI_STATS, 1, d.R, d.Vd, A, B, 1, ep, s));
+    DSPARK_STAGE(kLogitsGemm, launch_logits(d.dtype, d.R, d.Vd, A, B, ep, njobs, s));
   }
   DSPARK_STAGE(kL1Sweep, launch_l1_sweep(d.R, d.Vd, Zp, T, sz, stt, d.nstat, rs.mask, in->target_ids,
                              teacher != kNone, rs, s));

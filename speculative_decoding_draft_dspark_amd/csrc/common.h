@@ -34,6 +34,9 @@ template <> struct Elem<float> {
   __device__ static float to_f32(float x) { return x; }
   // 4 consecutive elements (16-byte aligned) widened to fp32
   __device__ static float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  typedef float4 Raw4;  // 4 elements as loaded
+  __device__ static Raw4 load4raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static float4 widen4(const Raw4& r) { return r; }
 };
 template <> struct Elem<bf16_t> {
   static constexpr int kPerChunk = 8;
@@ -42,6 +45,12 @@ template <> struct Elem<bf16_t> {
   // 4 consecutive elements (8-byte aligned) widened to fp32
   __device__ static float4 load4(const bf16_t* p) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+  typedef uint2 Raw4;  // 4 elements as loaded
+  __device__ static Raw4 load4raw(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ static float4 widen4(const Raw4& u) {
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
   }

@@ -17,7 +17,8 @@
 //     (transposed on the way into LDS) or k-blocked ([K/c][M][c] with c
 //     elements per 16-byte chunk).
 // Both: 256 x 256 output tiles, 8 waves of 128 x 64 each built from
-// v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32); LDS rows
+// v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32; in this
+// loss the 32x32x16 form measured slower in the full GEMM); LDS rows
 // of 16-byte chunks XOR-swizzled so MFMA operand reads are conflict-free; an
 // XCD-aware grouped tile order (each of the 8 XCDs works a contiguous range so
 // operand slices are shared through its own L2).  Operands may consist of two
@@ -93,69 +94,124 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// ------------------------------------------------------------------ accumulators
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_v;
+
+// A wave's accumulator tile built from 16x16 MFMA blocks.  Lane (g, cl) holds,
+// for block (i, j) and element e, row 16 i + 4 g + e, column 16 j + cl.
+template <int TM, int TN>
+struct Acc16 {
+  f32x4_v v[TM][TN];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) v[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  }
+  // Rows [r0, r0 + ROWS) of the workgroup tile into stage (row stride STRIDE);
+  // (wr, wc) is this wave's tile origin.
+  template <int ROWS, int STRIDE>
+  __device__ __forceinline__ void scatter(float* stage, int wr, int wc, int r0) const {
+    const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rl = wr + i * 16 + g * 4 + e - r0;
+        if (rl < 0 || rl >= ROWS) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) stage[rl * STRIDE + wc + j * 16 + cl] = v[i][j][e];
+      }
+  }
+};
+
+// A wave's accumulator tile built from 32x32 MFMA blocks.  Lane (h, c) = (l / 32,
+// l % 32) holds, for block (i, j) and element e, row 32 i + 8 (e / 4) + 4 h + e % 4,
+// column 32 j + c.
+template <int TM, int TN>
+struct Acc32 {
+  f32x16_v v[TM][TN];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[i][j][e] = 0.f;
+  }
+  template <int ROWS, int STRIDE>
+  __device__ __forceinline__ void scatter(float* stage, int wr, int wc, int r0) const {
+    const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rl = wr + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3) - r0;
+        if (rl < 0 || rl >= ROWS) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) stage[rl * STRIDE + wc + j * 32 + c] = v[i][j][e];
+      }
+  }
+};
+
 // ------------------------------------------------------------------ epilogue
 
 // The accumulator tile goes through LDS in chunks of 64 rows; 8 consecutive
 // lanes then own one 256-column row, lane sub handling columns 4 sub + 32 i
 // (i = 0..7), so a chunk's 64 rows are finished in parallel with 16-byte
-// stores, 8-byte addend loads and 3-step shuffle reductions per row.  In the
-// MFMA layout lane (g, cl) of wave (wm, wn) holds, for sub-tile (i, j) and
-// element e, the output at row wm*WTM + 16 i + 4 g + e, column wn*WTN + 16 j + cl.
-template <typename T, int BM, int BN, int WM, int WN, int EPI>
-__device__ __forceinline__ void row_epilogue(f32x4_v (&acc)[BM / WM / 16][BN / WN / 16],
-                                             float* stage, int64_t M, int64_t N, int64_t m0,
-                                             int64_t n0, int64_t tn, const EpiParams& ep) {
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int NT = WM * WN * 64;
+// stores, 8-byte addend loads and 3-step shuffle reductions per row.  (wr, wc)
+// is the calling wave's tile origin within the workgroup tile.
+template <typename T, int BM, int BN, int NT, int EPI, typename AccT>
+__device__ __forceinline__ void row_epilogue(const AccT& acc, int wr, int wc, float* stage,
+                                             int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                             int64_t tn, const EpiParams& ep) {
   static_assert(BN == 256, "row epilogue assumes 256 columns");
   constexpr int kChunkRows = 64;
   constexpr int kLanesPerRow = NT / kChunkRows;      // 8
   constexpr int kVecs = BN / 4 / kLanesPerRow;       // float4 column groups per lane (8)
   static_assert(kLanesPerRow == 8, "8 lanes per row");
   constexpr int kStride = BN + 4;  // floats; 4 * kStride = 16 (mod 32) banks: conflict-free writes
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int g = lane >> 4, cl = lane & 15;
   const int rr = threadIdx.x >> 3, sub = threadIdx.x & 7;
   float* C = ep.C;
   if (EPI == EPI_PARTIAL) C += static_cast<int64_t>(blockIdx.y) * M * ep.ldc;
   const T* X = static_cast<const T*>(ep.X);
+  // Addends are loaded one chunk ahead and before the previous chunk's stores:
+  // vmcnt retires in issue order, so a load issued after a store cannot be
+  // waited for without also waiting for that store.
+  typedef typename Elem<T>::Raw4 Raw4;
+  Raw4 xr[kVecs];
+  auto load_x = [&](int q) {
+    const int64_t row = m0 + q * kChunkRows + rr;
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) {
+      const int64_t col = n0 + sub * 4 + 32 * i;
+      xr[i] = (X && row < M && col < N) ? Elem<T>::load4raw(X + row * ep.ldx + col) : Raw4{};
+    }
+  };
+  if (EPI == EPI_STATS) load_x(0);
   lds_barrier();  // main-loop LDS reads are done (no LDS-DMA is in flight here)
 #pragma unroll 1
   for (int q = 0; q < BM / kChunkRows; ++q) {
     const int64_t row = m0 + q * kChunkRows + rr;
     const bool rowok = row < M;
-    // addends of this lane's columns, fetched before the chunk is staged
-    float4 xs[kVecs];
-    if (EPI == EPI_STATS) {
-#pragma unroll
-      for (int i = 0; i < kVecs; ++i) {
-        const int64_t col = n0 + sub * 4 + 32 * i;
-        xs[i] = (X && rowok && col < N) ? Elem<T>::load4(X + row * ep.ldx + col)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rl = wm * WTM + i * 16 + g * 4 + e - q * kChunkRows;
-        if (rl < 0 || rl >= kChunkRows) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) stage[rl * kStride + wn * WTN + j * 16 + cl] = acc[i][j][e];
-      }
+    acc.template scatter<kChunkRows, kStride>(stage, wr, wc, q * kChunkRows);
     lds_barrier();
     float4 v[kVecs];
 #pragma unroll
     for (int i = 0; i < kVecs; ++i)
       v[i] = *reinterpret_cast<const float4*>(&stage[rr * kStride + sub * 4 + 32 * i]);
     if (EPI == EPI_STATS) {
+#pragma unroll
+      for (int i = 0; i < kVecs; ++i) {
+        const float4 x = Elem<T>::widen4(xr[i]);
+        v[i].x += x.x; v[i].y += x.y; v[i].z += x.z; v[i].w += x.w;
+      }
+      if (q + 1 < BM / kChunkRows) load_x(q + 1);
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < kVecs; ++i) {
         const int64_t col = n0 + sub * 4 + 32 * i;
-        v[i].x += xs[i].x; v[i].y += xs[i].y; v[i].z += xs[i].z; v[i].w += xs[i].w;
         if (col < N) {  // N % 4 == 0: the 4 columns are all in or all out
           if (rowok) *reinterpret_cast<float4*>(C + row * ep.ldc + col) = v[i];
           mx = fmaxf(mx, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
@@ -313,11 +369,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t
   const int wm = wave / WN, wn = wave % WN;
   const int g = lane >> 4, cl = lane & 15;
 
-  f32x4_v acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  Acc16<TM, TN> acc;
+  acc.zero();
 
   if (nk > 0) {
     TileLoader<T, BM, NT, AL> la;
@@ -356,7 +409,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) Mfma<T>::run(acc[i][j], af[i], bfr[j]);
+          for (int j = 0; j < TN; ++j) Mfma<T>::run(acc.v[i][j], af[i], bfr[j]);
       }
       if (more) {
         u32x4* An = lds + ((kt + 1) & 1) * (A_CH + B_CH);
@@ -366,8 +419,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t
       __syncthreads();
     }
   }
-  row_epilogue<T, BM, BN, WM, WN, EPI>(acc, reinterpret_cast<float*>(lds), M, N, m0, n0, tc.tn,
-                                       ep);
+  row_epilogue<T, BM, BN, NT, EPI>(acc, wm * WTM, wn * WTN, reinterpret_cast<float*>(lds), M, N,
+                                   m0, n0, tc.tn, ep);
 }
 
 // ------------------------------------------------------------------ LDS-DMA kernel
@@ -422,34 +475,25 @@ __device__ __forceinline__ void dma_issue(const Operand& A, const Operand& B, in
                                              16, offB[p], 0, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int AL, int BL, int TAG>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int64_t N, int64_t K,
-                                                                  int64_t kper, Operand A,
-                                                                  Operand B, EpiParams ep,
-                                                                  int group_m) {
+// One output tile's K loop on the DMA path: slices [kbeg, kbeg + 32 nk) of
+// A (rows m0..) and B (rows n0..) accumulate into acc.
+template <int BM, int BN, int WM, int WN, int AL, int BL>
+__device__ __forceinline__ void dma_mainloop(Acc16<BM / WM / 16, BN / WN / 16>& acc,
+                                             const Operand& A, const Operand& B, int64_t kbeg,
+                                             int nk, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                             u32x4* lds) {
   constexpr int NT = WM * WN * 64;
   constexpr int NW = NT / 64;
-  constexpr int BK = 32;
   constexpr int STAGES = 4;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int TM = WTM / 16, TN = WTN / 16;                 // 16x16 MFMA blocks per wave
   constexpr int A_CH = BM * 4, B_CH = BN * 4;                 // 16-byte chunks per slice
   constexpr int A_LD = A_CH / 64 / NW, B_LD = B_CH / 64 / NW;  // DMA loads per wave per slice
   constexpr int STAGE_CH = A_CH + B_CH;
   static_assert(A_CH % (64 * NW) == 0 && B_CH % (64 * NW) == 0, "tile / wave mismatch");
   static_assert(STAGES * STAGE_CH * 16 <= 160 * 1024, "LDS budget");
-  static_assert(EPI != EPI_STATS || BN == kStatTile, "stats epilogue needs BN == stat tile");
-
-  __shared__ u32x4 lds[STAGES * STAGE_CH];
-  const TileCoord tc = tile_coord(M, N, BM, BN, group_m);
-  const int64_t m0 = tc.m0, n0 = tc.n0;
-  const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * kper;
-  const int64_t kend = (kbeg + kper) < K ? (kbeg + kper) : K;
-  const int nk = kend > kbeg ? static_cast<int>((kend - kbeg) / BK) : 0;
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int g = lane >> 4, cl = lane & 15;
 
   // Lane chunk of each DMA load: the wave's p-th load fills LDS chunks
   // [(wave*X_LD + p) * 64, +64) of the slice, lane l the one at +l, i.e. row
@@ -468,18 +512,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int
     offB[p] = (n0 + row < N) ? static_cast<uint32_t>(dma_chunk<BL>(row, c, B.ld) * 2) : kOutOfRange;
   }
 
-  f32x4_v acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-
   constexpr int LPS = A_LD + B_LD;  // loads per wave per slice
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
     if (t < nk)
       dma_issue<AL, BL, A_LD, B_LD, A_CH, STAGE_CH, STAGES>(A, B, kbeg, t, m0, n0, wave, offA, offB,
                                                             lds);
+  const int g = lane >> 4, cl = lane & 15;
   for (int kt = 0; kt < nk; ++kt) {
     // slice kt has landed once at most (slices issued after it) * LPS loads remain
     const int after = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
@@ -492,6 +531,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int
                                                             wave, offA, offB, lds);
     const u32x4* As = lds + (kt % STAGES) * STAGE_CH;
     const u32x4* Bs = As + A_CH;
+    // v_mfma_f32_16x16x32_bf16: lane (g, cl) supplies row cl of a 16-row block at
+    // k = 8 g .. 8 g + 7, i.e. chunk g of the 32-wide slice.
     u32x4 af[TM], bfr[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -506,10 +547,42 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) Mfma<bf16_t>::run(acc[i][j], af[i], bfr[j]);
+      for (int j = 0; j < TN; ++j) Mfma<bf16_t>::run(acc.v[i][j], af[i], bfr[j]);
   }
-  row_epilogue<bf16_t, BM, BN, WM, WN, EPI>(acc, reinterpret_cast<float*>(lds), M, N, m0, n0,
-                                            tc.tn, ep);
+}
+
+// One job of the DMA kernel on this workgroup's output tile.
+template <int BM, int BN, int WM, int WN, int EPI, int AL, int BL>
+__device__ __forceinline__ void dma_job(const GemmJob& J, int64_t M, int64_t N, int64_t kper,
+                                        const TileCoord& tc, u32x4* lds) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * kper;
+  const int64_t kend = (kbeg + kper) < J.K ? (kbeg + kper) : J.K;
+  const int nk = kend > kbeg ? static_cast<int>((kend - kbeg) / 32) : 0;
+  Acc16<BM / WM / 16, BN / WN / 16> acc;
+  acc.zero();
+  dma_mainloop<BM, BN, WM, WN, AL, BL>(acc, J.A, J.B, kbeg, nk, M, N, tc.m0, tc.n0, lds);
+  row_epilogue<bf16_t, BM, BN, NT, EPI>(acc, wm * WTM, wn * WTN, reinterpret_cast<float*>(lds), M,
+                                        N, tc.m0, tc.n0, tc.tn, J.ep);
+}
+
+// Up to two GEMM jobs over the same output tile grid, run back to back per
+// tile (the corrected draft logits and the teacher logits share M and N, so a
+// workgroup's memory-heavy draft epilogue overlaps other workgroups' MFMA
+// phases).  A job with K = 0 is its epilogue alone (C = X).
+template <int BM, int BN, int WM, int WN, int EPI, int AL, int BL, int TAG>
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int64_t N,
+                                                                  int64_t kper, GemmJob j0,
+                                                                  GemmJob j1, int njobs,
+                                                                  int group_m) {
+  static_assert(EPI != EPI_STATS || BN == kStatTile, "stats epilogue needs BN == stat tile");
+  __shared__ u32x4 lds[4 * (BM * 4 + BN * 4)];
+  const TileCoord tc = tile_coord(M, N, BM, BN, group_m);
+  dma_job<BM, BN, WM, WN, EPI, AL, BL>(j0, M, N, kper, tc, lds);
+  if (njobs > 1) dma_job<BM, BN, WM, WN, EPI, AL, BL>(j1, M, N, kper, tc, lds);
 }
 
 // ------------------------------------------------------------------ launch
@@ -535,14 +608,20 @@ hipError_t launch_generic(int64_t M, int64_t N, const Operand& A, const Operand&
 }
 
 template <int EPI, int AL, int BL, int TAG>
-hipError_t launch_dma(int64_t M, int64_t N, const Operand& A, const Operand& B, int splits,
-                      const EpiParams& ep, hipStream_t s) {
-  const int64_t K = A.kseg * A.nseg;
+hipError_t launch_dma(int64_t M, int64_t N, const GemmJob& j0, const GemmJob& j1, int njobs,
+                      int splits, hipStream_t s) {
   const int64_t nM = (M + 255) / 256, nN = (N + 255) / 256;
   dim3 grid(static_cast<uint32_t>(nM * nN), static_cast<uint32_t>(splits), 1);
+  const int64_t kper = splits > 1 ? split_kper(j0.K, splits, 32) : (j0.K > j1.K ? j0.K : j1.K);
   hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 2, 4, EPI, AL, BL, TAG>), grid, dim3(512), 0, s, M,
-                     N, K, split_kper(K, splits, 32), A, B, ep, kGroupM);
+                     N, kper, j0, j1, njobs, kGroupM);
   return hipGetLastError();
+}
+
+GemmJob job_of(const Operand& A, const Operand& B, const EpiParams& ep) {
+  GemmJob j;
+  j.A = A; j.B = B; j.ep = ep; j.K = A.kseg * A.nseg;
+  return j;
 }
 
 // The DMA path needs bf16, K-contiguous (or both k-blocked) operands and
@@ -578,19 +657,42 @@ hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const 
                        const Operand& B, int splits, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dtype == 1 && dma_ok(A, B)) {
+    const GemmJob j = job_of(A, B, ep);
     if (A.layout == LAYOUT_KB) {
       if (epi == EPI_PARTIAL)
-        return launch_dma<EPI_PARTIAL, LAYOUT_KB, LAYOUT_KB, 3>(M, N, A, B, splits, ep, s);
+        return launch_dma<EPI_PARTIAL, LAYOUT_KB, LAYOUT_KB, 3>(M, N, j, j, 1, splits, s);
     } else {
       if (epi == EPI_STATS)
-        return tag == 1 ? launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 1>(M, N, A, B, 1, ep, s)
-                        : launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, A, B, 1, ep, s);
+        return tag == 1 ? launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 1>(M, N, j, j, 1, 1, s)
+                        : launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, j, j, 1, 1, s);
       if (epi == EPI_PARTIAL)
-        return launch_dma<EPI_PARTIAL, LAYOUT_KC, LAYOUT_KC, 2>(M, N, A, B, splits, ep, s);
+        return launch_dma<EPI_PARTIAL, LAYOUT_KC, LAYOUT_KC, 2>(M, N, j, j, 1, splits, s);
     }
   }
   return dtype == 1 ? launch_t<bf16_t>(epi, tag, M, N, A, B, splits, ep, s)
                     : launch_t<float>(epi, tag, M, N, A, B, splits, ep, s);
+}
+
+// Both logits projections of the forward pass in one launch when both can use
+// the DMA path (bf16, K-contiguous, K a multiple of 32 or K = 0); otherwise one
+// launch each.
+hipError_t launch_logits(int dtype, int64_t M, int64_t N, const Operand* A, const Operand* B,
+                         const EpiParams* ep, int njobs, hipStream_t s) {
+  if (M <= 0 || N <= 0 || njobs <= 0) return hipSuccess;
+  bool fused = dtype == 1 && njobs <= 2;
+  GemmJob j[2];
+  for (int i = 0; i < njobs; ++i) {
+    j[i] = job_of(A[i], B[i], ep[i]);
+    if (j[i].K > 0 && !dma_ok(A[i], B[i])) fused = false;
+  }
+  if (fused)
+    return launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 4>(M, N, j[0], j[njobs - 1], njobs, 1, s);
+  for (int i = 0; i < njobs; ++i) {
+    const hipError_t e = launch_gemm(dtype, EPI_STATS, i == njobs - 1 ? 1 : 0, M, N, A[i], B[i], 1,
+                                     ep[i], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace dspark

@@ -44,8 +44,20 @@ struct EpiParams {
   int64_t nstat;
 };
 
+// One GEMM of a multi-job launch: C = A . B^T with K = A.kseg * A.nseg (0 allowed).
+struct GemmJob {
+  Operand A, B;
+  EpiParams ep;
+  int64_t K;
+};
+
 // dtype: 0 = fp32, 1 = bf16.  splits > 1 only with EPI_PARTIAL.  tag (EPI_STATS):
 // 0 = corrected draft logits, 1 = teacher logits (separate kernel symbols).
+// EPI_STATS jobs sharing M and N (the corrected draft logits, then the teacher
+// logits), fused into one launch where the DMA path applies.
+hipError_t launch_logits(int dtype, int64_t M, int64_t N, const Operand* A, const Operand* B,
+                         const EpiParams* ep, int njobs, hipStream_t s);
+
 hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const Operand& A,
                        const Operand& B, int splits, const EpiParams& ep, hipStream_t s);
 
