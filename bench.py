@@ -71,22 +71,29 @@ def _gpu_leg(args):
     return wl, elapsed, stages
 
 
-def _avg_ms(stages, name):
+def _avg_ms(stages, name, steps):
+    """Milliseconds per step of one stage (a stage may be several launches)."""
     ms, n = stages.get(name, (0.0, 0))
-    return ms / n if n else None
+    return ms / steps if n else None
 
 
 def _traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
+    """HBM-side bytes per launch from the committed rocprofv3 counter summary.
+
+    None when no summary exists or the GEMM source changed since the counters
+    were taken (its SHA-256 is recorded with them).
+    """
+    import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
-    if not os.path.exists(path):
-        return None
+    src = os.path.join(ROOT, "speculative_decoding_draft_dspark_amd", "csrc", "gemm.hip")
     try:
         with open(path) as fh:
             rec = json.load(fh)
-        return rec.get("bytes_per_launch") if rec.get("current", False) else None
+        with open(src, "rb") as fh:
+            cur = hashlib.sha256(fh.read()).hexdigest()
     except (OSError, ValueError):
         return None
+    return rec.get("bytes_per_launch") if rec.get("gemm_source_sha256") == cur else None
 
 
 def _cpu_leg(wl, blocks: int):
@@ -124,14 +131,28 @@ def _cpu_leg(wl, blocks: int):
                       f"{dt:.1f}s, numpy float64"}
 
 
+def _copy_probe(nbytes: int, reps: int = 3):
+    """A plain device-to-device copy of a known size (counter calibration)."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large-batch-r14336-v151936")
-    ap.add_argument("--cpu-blocks", type=int, default=12)
+    ap.add_argument("--cpu-blocks", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (rocprofv3 byte-counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -139,12 +160,15 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe:
+        _copy_probe(args.copy_probe)
+        return
     wl, elapsed, stages = _gpu_leg(args)
     R, V, H, r = wl.R, wl.Vd, wl.H, wl.r
     ms_step = 1000.0 * elapsed / args.steps
     rows_per_s = R * args.steps / elapsed
 
-    gemm_ms = _avg_ms(stages, "logits_gemm")
+    gemm_ms = _avg_ms(stages, "logits_gemm", args.steps)
     gemm_flops = 2.0 * R * V * (H + r)   # teacher projection (K = H) + Markov bias (K = r)
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma",
@@ -156,14 +180,14 @@ def main():
 
     # row sweeps: algorithmic bytes per launch / average duration
     sweeps = {}
-    for name, bytes_per_elem in (("l1_sweep", 8), ("grad_sweep", 12)):
-        ms = _avg_ms(stages, name)
+    for name, bytes_per_elem in (("l1_sweep", 8), ("grad_sweep", 16)):
+        ms = _avg_ms(stages, name, args.steps)
         if ms:
             gbs = bytes_per_elem * R * V / (ms * 1e-3) / 1e9
             sweeps[name] = {"avg_ms": round(ms, 4), "GB/s": round(gbs, 1),
                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                             "bytes_per_row": bytes_per_elem * V}
-    stage_ms = {k: round(v[0] / v[1], 4) for k, v in stages.items() if v[1]}
+    stage_ms = {k: round(v[0] / args.steps, 4) for k, v in stages.items() if v[1]}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -134,12 +134,13 @@ enum Teacher { kNone = 0, kHidden = 1, kAligned = 2 };
 
 // ---- per-stage timers (tracing aid)
 enum Stage {
-  kPrep, kGather, kLogitsGemm, kL1Sweep, kFinalize, kReduce, kGradSweep, kDeGemm,
-  kDeReduce, kDw1, kDw2Gemm, kConfBwd, kStages
+  kPrep, kGather, kLogitsGemm, kL1Sweep, kFinalize, kReduce, kGradSweep, kOperandPrep,
+  kDeGemm, kDeReduce, kDw1, kDw2Gemm, kConfBwd, kStages
 };
 const char* const kStageNames[kStages] = {
     "prep_rows", "gather_embed", "logits_gemm", "l1_sweep",
-    "finalize_rows", "reduce_fwd", "grad_sweep", "dE_gemm", "dE_reduce", "dW1_scatter",
+    "finalize_rows", "reduce_fwd", "grad_sweep", "operand_prep", "dE_gemm", "dE_reduce",
+    "dW1_scatter",
     "dW2_gemm", "conf_bwd"};
 
 struct Profiler {
@@ -358,7 +359,7 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     if (d.markov) {
       void* w2t = ws + L.w2t;
       void* eblk = ws + L.eblk;
-      DSPARK_STAGE(kDeGemm, launch_transpose_bf16(d.Vd, d.r, in->markov_w2, w2t, s));
+      DSPARK_STAGE(kOperandPrep, launch_transpose_bf16(d.Vd, d.r, in->markov_w2, w2t, s));
       {  // dE partials = G . W2 over vocabulary splits (both operands K-contiguous)
         Operand A{}, B{};
         A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.Vd; A.kpad = gemm_kpad(d.Vd, 2);
@@ -376,7 +377,7 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
       DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
       DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
                                             out->d_markov_w1, s));
-      DSPARK_STAGE(kDw2Gemm, launch_embed_blocked(d.R, rgroups, d.r, E, eblk, s));
+      DSPARK_STAGE(kOperandPrep, launch_embed_blocked(d.R, rgroups, d.r, E, eblk, s));
       {  // dW2 = G^T . E: hi and lo segments as two splits, then summed
         float* part = reinterpret_cast<float*>(ws + L.dw2part);
         Operand A{}, B{};
