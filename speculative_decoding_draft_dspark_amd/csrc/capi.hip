@@ -26,6 +26,9 @@ struct Dims {
   int64_t R32;  // R rounded up to a multiple of 32 (k-blocked row operands)
   int dtype, gdtype, esize;
   bool markov, conf, conf_markov;
+  // bf16 backward products read G, W2 and E in place (row counts and the
+  // vocabulary multiples of 32); otherwise through transposed / k-blocked copies
+  bool direct_bwd;
 };
 
 struct Layout {
@@ -66,6 +69,16 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   if (sp > kmax) sp = kmax;
   if (sp > 32) sp = 32;
   if (sp < 1) sp = 1;
+  d->direct_bwd = d->dtype == DSPARK_BF16 && d->markov && d->R % 32 == 0 && d->Vd % 32 == 0;
+  if (d->direct_bwd) {
+    // dE over vocabulary splits: about two waves of 256 workgroups, each split
+    // at least 8 slices of 32 of the 2 Vd (hi, lo) contraction
+    int64_t ds = (512 + nM - 1) / nM;
+    const int64_t dmax = 2 * d->Vd / 32 / 8;
+    if (ds > dmax) ds = dmax;
+    if (ds > 64) ds = 64;
+    sp = ds < 1 ? 1 : ds;
+  }
   d->splits = d->markov ? sp : 0;
   d->conf_chunks = d->R < 256 ? static_cast<int>(d->R) : 256;
   d->F = d->Hd + (d->conf_markov ? d->r : 0);
@@ -88,7 +101,9 @@ Layout make_layout(const Dims& d) {
   if (d.dtype == DSPARK_BF16) {
     if (d.gdtype != DSPARK_BF16) { L.ghi = o; o = up(o + RV * 2); }
     L.glo = o; o = up(o + RV * 2);
-    if (d.markov) {
+    if (d.markov && d.direct_bwd) {
+      L.dw2part = o; o = up(o + static_cast<size_t>(2) * d.Vd * d.r * 4);
+    } else if (d.markov) {
       const size_t R32V = static_cast<size_t>(d.R32) * d.Vd;
       L.w2t = o; o = up(o + static_cast<size_t>(d.Vd) * d.r * 2);
       L.eblk = o; o = up(o + static_cast<size_t>(d.R32) * d.r * 2);
@@ -345,7 +360,39 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     bf16_t* bhi = reinterpret_cast<bf16_t*>(ws + L.blkhi);
     bf16_t* blo = reinterpret_cast<bf16_t*>(ws + L.blklo);
     const int64_t rgroups = d.R32 / 8;
-    if (d.markov) {
+    if (d.direct_bwd) {
+      // G as dz (hi) and its bf16 remainder (lo), row-major; both products
+      // read G, W2 and E in place.
+      DSPARK_STAGE(kGradSweep, launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs,
+                                                 teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
+                                                 out->d_draft_logits, ghi, glo, nullptr, s));
+      {  // dE partials = [G hi | G lo] . [W2 | W2] over vocabulary splits
+        Operand A{}, B{};
+        A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.Vd; A.kpad = d.Vd;
+        A.ld = d.Vd; A.layout = LAYOUT_KC; A.nseg = 2;
+        B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.Vd; B.kpad = d.Vd; B.ld = d.r;
+        B.layout = LAYOUT_MK; B.nseg = 2;
+        DSPARK_STAGE(kDeGemm, launch_gemm_w4p(2, d.R, d.r, A, B, static_cast<int>(d.splits),
+                                              dEpart, d.r, s));
+      }
+      DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
+                                               dEpart, rs, d.conf_markov, in->conf_w, d.Hd, g,
+                                               c_a, dE, s));
+      DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
+      DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
+                                            out->d_markov_w1, s));
+      {  // dW2 = [G hi ; G lo]^T . [E ; E]: hi and lo as two splits, then summed
+        float* part = reinterpret_cast<float*>(ws + L.dw2part);
+        Operand A{}, B{};
+        A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.R; A.kpad = d.R;
+        A.ld = d.Vd; A.layout = LAYOUT_MK; A.nseg = 2;
+        B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = d.R; B.ld = d.r;
+        B.layout = LAYOUT_MK; B.nseg = 2;
+        DSPARK_STAGE(kDw2Gemm, launch_gemm_w4p(3, d.Vd, d.r, A, B, 2, part, d.r, s));
+        DSPARK_STAGE(kDw2Gemm, launch_add2(d.Vd * d.r, part, part + d.Vd * d.r,
+                                           out->d_markov_w2, s));
+      }
+    } else if (d.markov) {
       DSPARK_STAGE(kGradSweep, launch_grad_sweep8(d.gdtype, d.R, rgroups, d.Vd, Zp, T,
                                                   in->target_ids, rs, teacher != kNone, g,
                                                   hp->ce_alpha, hp->l1_alpha, out->d_draft_logits,
@@ -356,7 +403,7 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
                                                  out->d_draft_logits, nullptr, nullptr, nullptr,
                                                  s));
     }
-    if (d.markov) {
+    if (d.markov && !d.direct_bwd) {
       void* w2t = ws + L.w2t;
       void* eblk = ws + L.eblk;
       DSPARK_STAGE(kOperandPrep, launch_transpose_bf16(d.Vd, d.r, in->markov_w2, w2t, s));

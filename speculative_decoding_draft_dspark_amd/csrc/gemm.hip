@@ -70,11 +70,10 @@ struct TileCoord {
 // workgroups to the 8 XCDs in turn, so block b is remapped to give each XCD a
 // contiguous slice of the order; within it, group_m row tiles share each
 // column tile.
-__device__ __forceinline__ TileCoord tile_coord(int64_t M, int64_t N, int BM, int BN,
-                                                int group_m) {
+__device__ __forceinline__ TileCoord tile_coord_of(int64_t b, int64_t M, int64_t N, int BM, int BN,
+                                                   int group_m) {
   const int64_t nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN;
   const int64_t tiles = nM * nN;
-  int64_t b = blockIdx.x;
   const int64_t per_xcd = tiles / 8;
   if (b < per_xcd * 8) b = (b % 8) * per_xcd + b / 8;
   const int64_t gsz = static_cast<int64_t>(group_m) * nN;
@@ -83,6 +82,10 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t M, int64_t N, int BM, in
   const int64_t tm = fm + (b % gsz) % gm;
   const int64_t tn = (b % gsz) / gm;
   return {tm * BM, tn * BN, tn};
+}
+__device__ __forceinline__ TileCoord tile_coord(int64_t M, int64_t N, int BM, int BN,
+                                                int group_m) {
+  return tile_coord_of(blockIdx.x, M, N, BM, BN, group_m);
 }
 
 // Workgroup barrier ordering LDS accesses only.  __syncthreads() also fences
@@ -585,6 +588,754 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int
   if (njobs > 1) dma_job<BM, BN, WM, WN, EPI, AL, BL>(j1, M, N, kper, tc, lds);
 }
 
+// ------------------------------------------------------------------ 4-wave logits kernel
+
+// The logits projections (teacher T = H_t . LM^T, K = hidden; draft bias
+// E . W2^T, K = markov rank, plus the logits addend) on 256 x 256 tiles with
+// 4 waves of 128 x 128 built from v_mfma_f32_32x32x16_bf16: twice the MACs
+// per LDS byte read of the 8-wave loop.  The MFMA takes the vocab (B)
+// fragment as its first operand, so for block (j, i) lane (h, r) = (l / 32,
+// l % 32) holds row 32 i + r of the wave tile at columns 32 j + 8 q + 4 h ..
+// + 3 in elements 4 q .. 4 q + 3: 16-byte stores straight from the
+// accumulators, and a row's softmax statistics need one shuffle and one
+// exchange between the two waves that share the row.  Operands stream
+// through an LDS-DMA ring (4 stages of 32-wide K slices); each wave reads the
+// next slice's fragments into a second register set while its MFMAs run,
+// since with one wave per SIMD no other wave hides LDS latency.
+namespace w4 {
+constexpr int kNW = 4, kNT = 256, kStages = 4;
+constexpr int kACh = 256 * 4, kBCh = 256 * 4, kStageCh = kACh + kBCh;  // 16-byte chunks per slice
+constexpr int kALd = kACh / 64 / kNW, kBLd = kBCh / 64 / kNW;         // DMA loads per wave per slice
+constexpr int kLps = kALd + kBLd;
+}  // namespace w4
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_v;
+typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
+
+// Slot of 16-byte chunk c (0..3) of slice row m: rows 4 apart use different
+// slots, so the 16 rows one ds_read_b128 phase touches hit distinct banks.
+__device__ __forceinline__ int w4_slot(int m, int c) { return m * 4 + (c ^ ((m >> 2) & 3)); }
+
+// One operand's 32-wide K slice of 256 rows in LDS (1024 chunks of 16 bytes),
+// by global layout.
+//   KC ([rows][K]): slice row m holds its 32 k in 4 chunks at w4_slot(m, c);
+//      a lane's 8 consecutive k of one row are one ds_read_b128.
+//   MK ([K][rows]): slice row k holds 256 rows in 32 chunks of 8; chunk c of
+//      row k sits at k * 32 + (c ^ 4 (k & 3)).  A lane's 8 consecutive k of
+//      one row come from two ds_read_b64_tr_b16: in each 16-lane group, lane
+//      i loads 4 rows' worth at (k0 + i / 4, m0 + 4 (i % 4)) and lane j gets
+//      the values of row m0 + j at k0 .. k0 + 3.  The XOR spreads the 4 k rows
+//      (and the neighbouring group's 16 rows) of one such load over distinct
+//      banks.
+template <int L> struct W4Op;
+template <> struct W4Op<LAYOUT_KC> {
+  // (row, chunk) filled by LDS position idx of a slice
+  __device__ static void chunk(int idx, int* row, int* c) {
+    *row = idx >> 2;
+    *c = (idx & 3) ^ ((*row >> 2) & 3);
+  }
+  __device__ static int64_t offset(int row, int c, int64_t ld) { return row * ld + 8 * c; }
+  __device__ static int64_t base(int64_t r0, int64_t kk, int64_t ld) { return r0 * ld + kk; }
+  __device__ static bool in_range(int64_t r0, int row, int c, int64_t rows) { return r0 + row < rows; }
+  // fragment of rows rb .. rb + 31 (lane r = l % 32) at k = 16 ks + 8 (l / 32) .. + 7
+  __device__ static u32x4 frag(const u32x4* s, int rb, int ks) {
+    const int lane = threadIdx.x & 63;
+    return s[w4_slot(rb + (lane & 31), 2 * ks + (lane >> 5))];
+  }
+};
+template <> struct W4Op<LAYOUT_MK> {
+  __device__ static int slot(int k, int c) { return k * 32 + (c ^ (4 * (k & 3))); }
+  __device__ static void chunk(int idx, int* k, int* c) {
+    *k = idx >> 5;
+    *c = (idx & 31) ^ (4 * (*k & 3));
+  }
+  __device__ static int64_t offset(int k, int c, int64_t ld) { return k * ld + 8 * c; }
+  __device__ static int64_t base(int64_t r0, int64_t kk, int64_t ld) { return kk * ld + r0; }
+  __device__ static bool in_range(int64_t r0, int, int c, int64_t rows) { return r0 + 8 * c < rows; }
+  __device__ static u32x4 frag(const u32x4* s, int rb, int ks) {
+    const int lane = threadIdx.x & 63, gi = lane >> 4, i = lane & 15;
+    const int m = rb + 16 * (gi & 1) + 4 * (i & 3);       // first of the lane's 4 loaded rows
+    const int k = 16 * ks + 8 * (gi >> 1) + (i >> 2);
+    const int half = (m & 7) >> 2;                           // 8-byte half of the chunk
+    const char* base = reinterpret_cast<const char*>(s);
+    const s16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + slot(k, m >> 3) * 16 + half * 8));
+    const s16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + slot(k + 4, m >> 3) * 16 + half * 8));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return u32x4{a.x, a.y, b.x, b.y};
+  }
+};
+
+// Fragments of one 32-wide K slice: [k step][block] for A (rows) and B (vocab).
+struct W4Frags {
+  u32x4 a[2][4], b[2][4];
+};
+
+template <int AL, int BL>
+__device__ __forceinline__ void w4_read(W4Frags& f, const u32x4* st, int wm, int wn) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f.a[ks][i] = W4Op<AL>::frag(st, wm * 128 + i * 32, ks);
+      f.b[ks][i] = W4Op<BL>::frag(st + w4::kACh, wn * 128 + i * 32, ks);
+    }
+}
+
+__device__ __forceinline__ void w4_mma(f32x16_v (&acc)[4][4], const W4Frags& f) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_v, f.b[ks][j]), __builtin_bit_cast(bf16x8_v, f.a[ks][i]),
+            acc[j][i], 0, 0, 0);
+}
+
+// Lane chunk offsets (bytes from the slice base) of the wave's DMA loads.
+struct W4Offsets {
+  uint32_t a[w4::kALd], b[w4::kBLd];
+};
+
+template <int AL, int BL>
+__device__ __forceinline__ void w4_offsets(W4Offsets& o, const Operand& A, const Operand& B,
+                                           int64_t M, int64_t N, int64_t m0, int64_t n0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < w4::kALd; ++p) {
+    int row, c;
+    W4Op<AL>::chunk((wave * w4::kALd + p) * 64 + lane, &row, &c);
+    o.a[p] = W4Op<AL>::in_range(m0, row, c, M)
+                 ? static_cast<uint32_t>(W4Op<AL>::offset(row, c, A.ld) * 2)
+                 : kOutOfRange;
+  }
+#pragma unroll
+  for (int p = 0; p < w4::kBLd; ++p) {
+    int row, c;
+    W4Op<BL>::chunk((wave * w4::kBLd + p) * 64 + lane, &row, &c);
+    o.b[p] = W4Op<BL>::in_range(n0, row, c, N)
+                 ? static_cast<uint32_t>(W4Op<BL>::offset(row, c, B.ld) * 2)
+                 : kOutOfRange;
+  }
+}
+
+// The ring's four stages are separate LDS arrays: with stage indices known
+// at compile time, the compiler's own LDS-DMA hazard waits before a fragment
+// read cover only the DMA into that stage (the one the loop waits for
+// anyway), not every slice in flight.
+struct W4Ring {
+  u32x4* st[w4::kStages];
+};
+
+// Queue virtual slice t into stage S for a job whose K range starts at kbeg
+// and holds nk real slices after `shift` leading zero slices.  A zero slice
+// loads through a zero-length buffer: its stage fills with zeros and no
+// memory is touched.
+template <int S, int AL, int BL>
+__device__ __forceinline__ void w4_issue(const Operand& A, const Operand& B, int64_t kbeg, int t,
+                                         int nk, int shift, int64_t m0, int64_t n0,
+                                         const W4Offsets& o, const W4Ring& ring) {
+  const int r = t - shift;
+  const bool real = r >= 0 && r < nk;
+  const int64_t kg = kbeg + (real ? static_cast<int64_t>(r) * 32 : 0);
+  const bool s1 = kg >= A.kseg;  // at most two K segments
+  const int64_t kk = s1 ? kg - A.kseg : kg;
+  const bf16_t* abase = static_cast<const bf16_t*>(s1 ? A.seg[1] : A.seg[0]);
+  const bf16_t* bbase = static_cast<const bf16_t*>(s1 ? B.seg[1] : B.seg[0]);
+  const int nrec = real ? kNumRecords : 0;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(abase + W4Op<AL>::base(m0, kk, A.ld)), 0, nrec, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(bbase + W4Op<BL>::base(n0, kk, B.ld)), 0, nrec, kRsrcWord3);
+  u32x4* st = ring.st[S];
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < w4::kALd; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave * w4::kALd + p) * 64), 16,
+                                             o.a[p], 0, 0, 0);
+#pragma unroll
+  for (int p = 0; p < w4::kBLd; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (lds_void*)(st + w4::kACh + (wave * w4::kBLd + p) * 64), 16, o.b[p], 0, 0, 0);
+}
+
+// One step of the K loop for slice kt in stage S, whose fragments are in
+// `cur`: wait until slice kt + 1 has landed (LATER slices were queued after
+// it), queue slice kt + 3 (ISSUE), read slice kt + 1 into `nxt` (READ), run
+// slice kt's MFMAs.  Scheduling fences keep each step's MFMAs between its
+// own fragment reads and the next step's barrier.
+template <int S, int LATER, bool ISSUE, bool READ, int AL, int BL>
+__device__ __forceinline__ void w4_step(f32x16_v (&acc)[4][4], const W4Frags& cur, W4Frags& nxt,
+                                        const Operand& A, const Operand& B, int64_t kbeg, int kt,
+                                        int nk, int shift, int64_t m0, int64_t n0,
+                                        const W4Offsets& o, const W4Ring& ring, int wm, int wn) {
+  // LDS read instructions per slice: one per KC fragment, two per MK fragment
+  constexpr int kReads = 8 * (AL == LAYOUT_MK ? 2 : 1) + 8 * (BL == LAYOUT_MK ? 2 : 1);
+  __builtin_amdgcn_sched_barrier(0);
+  if (READ) {
+    if (LATER == 1) wait_vmcnt<w4::kLps>();
+    else wait_vmcnt<0>();
+    dma_barrier();
+  }
+  if (ISSUE)
+    w4_issue<(S + 3) % w4::kStages, AL, BL>(A, B, kbeg, kt + 3, nk, shift, m0, n0, o, ring);
+  if (READ) w4_read<AL, BL>(nxt, ring.st[(S + 1) % w4::kStages], wm, wn);
+  w4_mma(acc, cur);
+  // Interleave the fragment reads and DMA issues with the MFMAs so the matrix
+  // pipe is not left idle while the wave issues its memory operations.
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                   // MFMA
+    if (READ) __builtin_amdgcn_sched_group_barrier(0x100, kReads / 16, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                   // MFMA
+    if (READ) __builtin_amdgcn_sched_group_barrier(0x100, kReads / 16, 0);  // DS read
+    if (ISSUE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // VMEM read (LDS DMA)
+  }
+}
+
+// First kStages - 1 virtual slices of a job's K loop (nothing when nk == 0,
+// so no DMA is left in flight).
+template <int AL, int BL>
+__device__ __forceinline__ void w4_prologue(const Operand& A, const Operand& B, int64_t kbeg,
+                                            int nk, int64_t m0, int64_t n0, const W4Offsets& o,
+                                            const W4Ring& ring) {
+  if (nk <= 0) return;
+  const int shift = (4 - (nk & 3)) & 3;
+  w4_issue<0, AL, BL>(A, B, kbeg, 0, nk, shift, m0, n0, o, ring);
+  w4_issue<1, AL, BL>(A, B, kbeg, 1, nk, shift, m0, n0, o, ring);
+  w4_issue<2, AL, BL>(A, B, kbeg, 2, nk, shift, m0, n0, o, ring);
+}
+
+// K loop of one job whose first slices w4_prologue already queued.  Runs
+// over nv = nk rounded up to a multiple of 4 virtual slices (zero slices
+// first), unrolled by the 4 ring stages; fragments alternate between two
+// register sets so slice kt + 1 is read while slice kt's MFMAs run.  Every
+// DMA has landed when it returns.
+template <int AL, int BL>
+__device__ __forceinline__ void w4_mainloop(f32x16_v (&acc)[4][4], const Operand& A,
+                                            const Operand& B, int64_t kbeg, int nk, int64_t m0,
+                                            int64_t n0, const W4Offsets& o, const W4Ring& ring) {
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
+  if (nk <= 0) return;
+  const int shift = (4 - (nk & 3)) & 3, nv = nk + shift;
+  wait_vmcnt<2 * w4::kLps>();  // slice 0 has landed (slices 1 and 2 follow it)
+  dma_barrier();
+  W4Frags f0, f1;
+  w4_read<AL, BL>(f0, ring.st[0], wm, wn);
+  int kt = 0;
+  for (; kt + 4 < nv; kt += 4) {
+    w4_step<0, 1, true, true, AL, BL>(acc, f0, f1, A, B, kbeg, kt, nk, shift, m0, n0, o, ring, wm, wn);
+    w4_step<1, 1, true, true, AL, BL>(acc, f1, f0, A, B, kbeg, kt + 1, nk, shift, m0, n0, o, ring, wm, wn);
+    w4_step<2, 1, true, true, AL, BL>(acc, f0, f1, A, B, kbeg, kt + 2, nk, shift, m0, n0, o, ring, wm, wn);
+    w4_step<3, 1, true, true, AL, BL>(acc, f1, f0, A, B, kbeg, kt + 3, nk, shift, m0, n0, o, ring, wm, wn);
+  }
+  // last four slices: only slice nv - 1 remains to be queued
+  w4_step<0, 1, true, true, AL, BL>(acc, f0, f1, A, B, kbeg, kt, nk, shift, m0, n0, o, ring, wm, wn);
+  w4_step<1, 1, false, true, AL, BL>(acc, f1, f0, A, B, kbeg, kt + 1, nk, shift, m0, n0, o, ring, wm, wn);
+  w4_step<2, 0, false, true, AL, BL>(acc, f0, f1, A, B, kbeg, kt + 2, nk, shift, m0, n0, o, ring, wm, wn);
+  w4_step<3, 0, false, false, AL, BL>(acc, f1, f0, A, B, kbeg, kt + 3, nk, shift, m0, n0, o, ring, wm, wn);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Partial-sum epilogue: the 256 x 256 fp32 tile straight from the
+// accumulators (lane (h, r) of block (j, i): row 32 i + r, columns
+// 32 j + 8 q + 4 h .. + 3) into C (rows < M, columns < N; N % 4 == 0).
+__device__ __forceinline__ void w4_store(const f32x16_v (&acc)[4][4], int64_t M, int64_t N,
+                                         int64_t m0, int64_t n0, float* C, int64_t ldc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + wm * 128 + 32 * i + r;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n0 + wn * 128 + 32 * j + 8 * q + 4 * h;
+        if (col < N)
+          *reinterpret_cast<float4*>(C + row * ldc + col) =
+              make_float4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                          acc[j][i][4 * q + 3]);
+      }
+  }
+}
+
+// C[blockIdx.y] = A . B^T over K range [blockIdx.y kper, + kper) on 256 x 256
+// tiles (backward products; operands KC or MK).
+template <int AL, int BL, int TAG>
+__global__ __launch_bounds__(256, 1) void gemm_w4p_kernel(int64_t M, int64_t N, int64_t K,
+                                                          int64_t kper, Operand A, Operand B,
+                                                          float* C, int64_t ldc, int group_m) {
+  __shared__ u32x4 st0[w4::kStageCh], st1[w4::kStageCh], st2[w4::kStageCh], st3[w4::kStageCh];
+  const W4Ring ring{{st0, st1, st2, st3}};
+  const TileCoord tc = tile_coord(M, N, 256, 256, group_m);
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * kper;
+  const int64_t kend = (kbeg + kper) < K ? (kbeg + kper) : K;
+  const int nk = kend > kbeg ? static_cast<int>((kend - kbeg) / 32) : 0;
+  W4Offsets o;
+  w4_offsets<AL, BL>(o, A, B, M, N, tc.m0, tc.n0);
+  w4_prologue<AL, BL>(A, B, kbeg, nk, tc.m0, tc.n0, o, ring);
+  f32x16_v acc[4][4];
+  w4_mainloop<AL, BL>(acc, A, B, kbeg, nk, tc.m0, tc.n0, o, ring);
+  w4_store(acc, M, N, tc.m0, tc.n0, C + static_cast<int64_t>(blockIdx.y) * M * ldc, ldc);
+}
+
+// Stores the tile (plus the bf16 addend X when given) and, per row, the
+// maximum and exp-sum of its 256 columns.  The accumulators go through two
+// free ring stages (32 rows x 256 fp32 each, 16-byte slots XOR-swizzled by
+// row so both the accumulator writes and the row reads are conflict-free),
+// one 32-row block of each wave-row half at a time; then 16 lanes own a row:
+// 256-byte coalesced stores and addend loads, and the row's maximum and
+// exp-sum reduce over 4 shuffle steps in a fixed order, so z' and T, which
+// both take this path, give bitwise-equal statistics for equal rows.
+__device__ __forceinline__ int w4_eslot(int row, int c4) { return row * 64 + (c4 ^ (row & 15)); }
+
+// Maximum / sum over each row of 16 lanes with DPP row rotations (VALU
+// only, no LDS round trips); every lane of the row receives the result, in
+// an order that depends only on the lane.
+template <int ROR>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + ROR, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  return v + row_ror<1>(v);
+}
+
+__device__ __forceinline__ void w4_epilogue(const f32x16_v (&acc)[4][4], int64_t M, int64_t N,
+                                            int64_t m0, int64_t n0, int64_t tn,
+                                            const EpiParams& ep, float4* ea, float4* eb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r = lane & 31;
+  const int sub = lane & 15;                   // 16 lanes per row in the row phase
+  const int chunk = wave >> 1;                 // row phase: wave-row half this wave reads
+  const int rbase = 16 * (wave & 1) + (lane >> 4);  // + 4 p: row within the 32-row block
+  const bf16_t* X = static_cast<const bf16_t*>(ep.X);
+  float4* mine = wm == 0 ? ea : eb;
+  const float4* src = chunk == 0 ? ea : eb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // unrolled: acc[.][i] must stay in registers
+    // addends of this block's rows, issued before the barrier so they are in
+    // flight while the accumulators are staged
+    uint2 xv[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int64_t row = m0 + chunk * 128 + 32 * i + rbase + 4 * p;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t col = n0 + 4 * sub + 64 * t;
+        xv[p][t] = (X && row < M && col < N)
+                       ? *reinterpret_cast<const uint2*>(X + row * ep.ldx + col)
+                       : uint2{0u, 0u};
+      }
+    }
+    lds_barrier();  // the stages are free (main-loop reads or the previous block's reads done)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        mine[w4_eslot(r, wn * 32 + 8 * j + 2 * q + h)] =
+            make_float4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                        acc[j][i][4 * q + 3]);
+    lds_barrier();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int rr = rbase + 4 * p;
+      const int64_t row = m0 + chunk * 128 + 32 * i + rr;
+      float4 v[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[t] = src[w4_eslot(rr, sub + 16 * t)];
+        v[t].x += __uint_as_float(xv[p][t].x << 16);
+        v[t].y += __uint_as_float(xv[p][t].x & 0xffff0000u);
+        v[t].z += __uint_as_float(xv[p][t].y << 16);
+        v[t].w += __uint_as_float(xv[p][t].y & 0xffff0000u);
+        const int64_t col = n0 + 4 * sub + 64 * t;
+        if (col < N) {  // N % 4 == 0: the lane's 4 columns are all in or all out
+          if (row < M) *reinterpret_cast<float4*>(ep.C + row * ep.ldc + col) = v[t];
+          mx = fmaxf(mx, fmaxf(fmaxf(v[t].x, v[t].y), fmaxf(v[t].z, v[t].w)));
+        }
+      }
+      mx = row16_max(mx);
+      float l = 0.f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (n0 + 4 * sub + 64 * t < N)
+            l += (dexp(v[t].x - mx) + dexp(v[t].y - mx)) + (dexp(v[t].z - mx) + dexp(v[t].w - mx));
+      }
+      l = row16_sum(l);
+      if (sub == 0 && row < M) ep.stats[row * ep.nstat + tn] = make_float2(mx, l);
+    }
+  }
+}
+
+// Up to two logits jobs (NJ) over the same 256 x 256 output tile grid: job 0
+// (when NJ == 2) then job 1 per tile.  Persistent: one workgroup per CU
+// walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of the XCD-aware
+// order (gridDim.x a multiple of 8 keeps each workgroup on one XCD's
+// range).  The next job's first two slices are queued into stages 0 and 1
+// before the current job's epilogue, which uses stages 2 and 3, and its
+// third slice right after, so operand loads and the previous tile's stores
+// overlap the epilogue and the next main loop.  A job with K = 0 is its
+// epilogue alone (C = X).  Operands are bf16, K-contiguous, K a multiple of 32.
+template <int NJ>
+__device__ __forceinline__ void w4_queue(const GemmJob& J, const TileCoord& tc, int64_t M,
+                                         int64_t N, W4Offsets& o, const W4Ring& ring) {
+  const int nk = static_cast<int>(J.K / 32);
+  const int shift = (4 - (nk & 3)) & 3;
+  w4_offsets<LAYOUT_KC, LAYOUT_KC>(o, J.A, J.B, M, N, tc.m0, tc.n0);
+  if (nk > 0) {
+    w4_issue<0, LAYOUT_KC, LAYOUT_KC>(J.A, J.B, 0, 0, nk, shift, tc.m0, tc.n0, o, ring);
+    w4_issue<1, LAYOUT_KC, LAYOUT_KC>(J.A, J.B, 0, 1, nk, shift, tc.m0, tc.n0, o, ring);
+  }
+}
+__device__ __forceinline__ void w4_queue_third(const GemmJob& J, const TileCoord& tc,
+                                               const W4Offsets& o, const W4Ring& ring) {
+  const int nk = static_cast<int>(J.K / 32);
+  const int shift = (4 - (nk & 3)) & 3;
+  if (nk > 0) w4_issue<2, LAYOUT_KC, LAYOUT_KC>(J.A, J.B, 0, 2, nk, shift, tc.m0, tc.n0, o, ring);
+}
+
+template <int TAG, int NJ>
+__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(int64_t M, int64_t N, GemmJob j0,
+                                                         GemmJob j1, int group_m) {
+  __shared__ u32x4 st0[w4::kStageCh], st1[w4::kStageCh], st2[w4::kStageCh], st3[w4::kStageCh];
+  const W4Ring ring{{st0, st1, st2, st3}};
+  float4* ea = reinterpret_cast<float4*>(st2);
+  float4* eb = reinterpret_cast<float4*>(st3);
+  const int64_t ntiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const GemmJob& first = NJ == 2 ? j0 : j1;
+  int64_t v = blockIdx.x;
+  TileCoord tc = tile_coord_of(v, M, N, 256, 256, group_m);
+  f32x16_v acc[4][4];
+  W4Offsets o;
+  w4_queue<NJ>(first, tc, M, N, o, ring);
+  w4_queue_third(first, tc, o, ring);
+  for (;;) {
+    if (NJ == 2) {
+      w4_mainloop<LAYOUT_KC, LAYOUT_KC>(acc, j0.A, j0.B, 0, static_cast<int>(j0.K / 32), tc.m0,
+                                        tc.n0, o, ring);
+      lds_barrier();  // every wave has read its last fragments of job 0
+      w4_queue<NJ>(j1, tc, M, N, o, ring);
+      w4_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, j0.ep, ea, eb);
+      lds_barrier();  // stage 2 is read for the last time
+      w4_queue_third(j1, tc, o, ring);
+    }
+    w4_mainloop<LAYOUT_KC, LAYOUT_KC>(acc, j1.A, j1.B, 0, static_cast<int>(j1.K / 32), tc.m0,
+                                      tc.n0, o, ring);
+    const int64_t vn = v + gridDim.x;
+    const bool more = vn < ntiles;
+    const TileCoord tnext = tile_coord_of(more ? vn : v, M, N, 256, 256, group_m);
+    lds_barrier();  // every wave has read its last fragments of job 1
+    if (more) w4_queue<NJ>(first, tnext, M, N, o, ring);
+    w4_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, j1.ep, ea, eb);
+    if (!more) break;
+    lds_barrier();
+    w4_queue_third(first, tnext, o, ring);
+    v = vn;
+    tc = tnext;
+  }
+}
+
+// ------------------------------------------------------------------ 2-per-CU logits kernel
+
+// The logits projections on 128 x 256 tiles, two workgroups per CU: 4 waves
+// of 64 x 128 (v_mfma_f32_32x32x16_bf16, 128 accumulators, 256 registers a
+// wave), a 3-stage LDS-DMA ring of 32-wide K slices (72 KB) and a 2 KB
+// exchange area per workgroup.  While one workgroup runs its epilogue
+// (stores of the fp32 tile, softmax statistics) the other keeps the matrix
+// pipes busy.  Fragment layout as in the 4-wave kernel: the vocab fragment is
+// the first MFMA operand, so lane (h, r) of block (j, i) holds row 32 i + r
+// of the wave tile at columns 32 j + 8 q + 4 h .. + 3 (elements 4 q ..).
+// The ring and the exchange area are one LDS array.
+namespace w8 {
+constexpr int kNT = 256, kStages = 3;
+constexpr int kACh = 128 * 4, kBCh = 256 * 4, kStageCh = kACh + kBCh;  // 16-byte chunks per slice
+constexpr int kALd = kACh / 64 / 4, kBLd = kBCh / 64 / 4;             // DMA loads per wave per slice
+constexpr int kLps = kALd + kBLd;
+constexpr int kRingCh = kStages * kStageCh;
+constexpr int kRedCh = 2 * 128 * 8 / 16;  // [2 wave columns][128 rows] x (max, sum)
+}  // namespace w8
+
+struct W8Frags {
+  u32x4 a[2][2], b[2][4];  // [k step][block]
+};
+
+__device__ __forceinline__ void w8_read(W8Frags& f, const u32x4* st, int wm, int wn) {
+  const u32x4* As = st;
+  const u32x4* Bs = st + w8::kACh;
+  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[ks][i] = As[w4_slot(wm * 64 + i * 32 + r, 2 * ks + h)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[ks][j] = Bs[w4_slot(wn * 128 + j * 32 + r, 2 * ks + h)];
+  }
+}
+
+__device__ __forceinline__ void w8_mma(f32x16_v (&acc)[4][2], const W8Frags& f) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_v, f.b[ks][j]), __builtin_bit_cast(bf16x8_v, f.a[ks][i]),
+            acc[j][i], 0, 0, 0);
+}
+
+struct W8Offsets {
+  uint32_t a[w8::kALd], b[w8::kBLd];
+};
+
+__device__ __forceinline__ void w8_offsets(W8Offsets& o, const Operand& A, const Operand& B,
+                                           int64_t M, int64_t N, int64_t m0, int64_t n0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < w8::kALd; ++p) {
+    const int idx = (wave * w8::kALd + p) * 64 + lane;
+    const int row = idx >> 2, c = (idx & 3) ^ ((row >> 2) & 3);
+    o.a[p] = (m0 + row < M) ? static_cast<uint32_t>((row * A.ld + c * 8) * 2) : kOutOfRange;
+  }
+#pragma unroll
+  for (int p = 0; p < w8::kBLd; ++p) {
+    const int idx = (wave * w8::kBLd + p) * 64 + lane;
+    const int row = idx >> 2, c = (idx & 3) ^ ((row >> 2) & 3);
+    o.b[p] = (n0 + row < N) ? static_cast<uint32_t>((row * B.ld + c * 8) * 2) : kOutOfRange;
+  }
+}
+
+// Queue virtual slice t (zero slices outside [shift, shift + nk), loaded
+// through a zero-length buffer) into stage t % 3.
+__device__ __forceinline__ void w8_issue(const Operand& A, const Operand& B, int t, int nk,
+                                         int shift, int64_t m0, int64_t n0, const W8Offsets& o,
+                                         u32x4* lds) {
+  const int r = t - shift;
+  const bool real = r >= 0 && r < nk;
+  const int64_t kg = real ? static_cast<int64_t>(r) * 32 : 0;
+  const bool s1 = kg >= A.kseg;  // at most two K segments
+  const int64_t kk = s1 ? kg - A.kseg : kg;
+  const bf16_t* abase = static_cast<const bf16_t*>(s1 ? A.seg[1] : A.seg[0]);
+  const bf16_t* bbase = static_cast<const bf16_t*>(s1 ? B.seg[1] : B.seg[0]);
+  const int nrec = real ? kNumRecords : 0;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(abase + m0 * A.ld + kk), 0, nrec, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(bbase + n0 * B.ld + kk), 0, nrec, kRsrcWord3);
+  u32x4* st = lds + (t % w8::kStages) * w8::kStageCh;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < w8::kALd; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave * w8::kALd + p) * 64), 16,
+                                             o.a[p], 0, 0, 0);
+#pragma unroll
+  for (int p = 0; p < w8::kBLd; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (lds_void*)(st + w8::kACh + (wave * w8::kBLd + p) * 64), 16, o.b[p], 0, 0, 0);
+}
+
+__device__ __forceinline__ void w8_prologue(const Operand& A, const Operand& B, int nk, int64_t m0,
+                                            int64_t n0, const W8Offsets& o, u32x4* lds) {
+  const int shift = nk & 1;
+#pragma unroll
+  for (int t = 0; t < w8::kStages; ++t) w8_issue(A, B, t, nk, shift, m0, n0, o, lds);
+}
+
+// One step: slice kt's fragments in `cur`; wait for slice kt + 1 (one slice
+// queued after it), queue slice kt + 3 into slice kt's stage (its fragments
+// were read before this barrier), read slice kt + 1 into `nxt`, run slice
+// kt's MFMAs interleaved with those reads and DMA issues.
+__device__ __forceinline__ void w8_step(f32x16_v (&acc)[4][2], const W8Frags& cur, W8Frags& nxt,
+                                        const Operand& A, const Operand& B, int kt, int nk,
+                                        int shift, int64_t m0, int64_t n0, const W8Offsets& o,
+                                        u32x4* lds, int wm, int wn) {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<w8::kLps>();
+  dma_barrier();
+  w8_issue(A, B, kt + 3, nk, shift, m0, n0, o, lds);
+  w8_read(nxt, lds + ((kt + 1) % w8::kStages) * w8::kStageCh, wm, wn);
+  w8_mma(acc, cur);
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (LDS DMA)
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// K loop of one job (w8_prologue already queued slices 0..2): an even number
+// of virtual slices (a zero slice first when nk is odd) in pairs.
+__device__ __forceinline__ void w8_mainloop(f32x16_v (&acc)[4][2], const Operand& A,
+                                            const Operand& B, int nk, int64_t m0, int64_t n0,
+                                            const W8Offsets& o, u32x4* lds) {
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
+  if (nk <= 0) return;
+  const int shift = nk & 1, nv = nk + shift;
+  wait_vmcnt<2 * w8::kLps>();  // slice 0 has landed (slices 1 and 2 follow it)
+  dma_barrier();
+  W8Frags f0, f1;
+  w8_read(f0, lds, wm, wn);
+  int kt = 0;
+  for (; kt + 2 < nv; kt += 2) {
+    w8_step(acc, f0, f1, A, B, kt, nk, shift, m0, n0, o, lds, wm, wn);
+    w8_step(acc, f1, f0, A, B, kt + 1, nk, shift, m0, n0, o, lds, wm, wn);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<0>();  // the last slice, and the zero slice queued after it, have landed
+  dma_barrier();
+  w8_read(f1, lds + ((kt + 1) % w8::kStages) * w8::kStageCh, wm, wn);
+  w8_mma(acc, f0);
+  w8_mma(acc, f1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stores the 128 x 256 tile (plus the bf16 addend X when given) straight
+// from the accumulators and writes, per row, the maximum and exp-sum over
+// its 256 columns: each wave reduces its 128 columns (maximum first, then a
+// float sum of exp(x - max) in a fixed order), and the two halves of a row
+// merge through the exchange area.  z' and T both take this path, so equal
+// rows give bitwise-equal statistics.
+__device__ __forceinline__ void w8_epilogue(const f32x16_v (&acc)[4][2], int64_t M, int64_t N,
+                                            int64_t m0, int64_t n0, int64_t tn,
+                                            const EpiParams& ep, float2* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r = lane & 31;
+  const int64_t c0 = n0 + wn * 128 + 4 * h;  // + 32 j + 8 q
+  const bf16_t* X = static_cast<const bf16_t*>(ep.X);
+  lds_barrier();  // the previous epilogue's reads of the exchange area are done
+  uint2 xn[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = m0 + wm * 64 + r, col = c0 + 32 * j + 8 * q;
+      xn[j][q] = (X && row < M && col < N) ? *reinterpret_cast<const uint2*>(X + row * ep.ldx + col)
+                                           : uint2{0u, 0u};
+    }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = m0 + wm * 64 + 32 * i + r;
+    float4 v[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[j][q] = make_float4(acc[j][i][4 * q] + __uint_as_float(xn[j][q].x << 16),
+                              acc[j][i][4 * q + 1] + __uint_as_float(xn[j][q].x & 0xffff0000u),
+                              acc[j][i][4 * q + 2] + __uint_as_float(xn[j][q].y << 16),
+                              acc[j][i][4 * q + 3] + __uint_as_float(xn[j][q].y & 0xffff0000u));
+      }
+    // addends of the next row block are loaded before this block is stored:
+    // vmcnt retires in issue order, so a load issued after a store cannot be
+    // waited for without also waiting for that store
+    if (X && i == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = c0 + 32 * j + 8 * q;
+          xn[j][q] = (row + 32 < M && col < N)
+                         ? *reinterpret_cast<const uint2*>(X + (row + 32) * ep.ldx + col)
+                         : uint2{0u, 0u};
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = c0 + 32 * j + 8 * q;
+        if (col < N) {  // N % 4 == 0: the lane's 4 columns are all in or all out
+          if (row < M) *reinterpret_cast<float4*>(ep.C + row * ep.ldc + col) = v[j][q];
+          mx = fmaxf(mx, fmaxf(fmaxf(v[j][q].x, v[j][q].y), fmaxf(v[j][q].z, v[j][q].w)));
+        }
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float l = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c0 + 32 * j + 8 * q < N)
+            l += (dexp(v[j][q].x - mx) + dexp(v[j][q].y - mx)) +
+                 (dexp(v[j][q].z - mx) + dexp(v[j][q].w - mx));
+    }
+    l += __shfl_xor(l, 32, kWave);
+    if (h == 0) red[wn * 128 + wm * 64 + 32 * i + r] = make_float2(mx, l);
+  }
+  lds_barrier();
+  if (threadIdx.x < 128) {
+    const int t = threadIdx.x;
+    const int64_t row = m0 + t;
+    if (row < M) {
+      const float2 a = red[t], b = red[128 + t];
+      const float m = fmaxf(a.x, b.x);
+      const float l = m == -INFINITY ? 0.f : a.y * dexp(a.x - m) + b.y * dexp(b.x - m);
+      ep.stats[row * ep.nstat + tn] = make_float2(m, l);
+    }
+  }
+}
+
+// Up to two logits jobs (NJ) per 128 x 256 output tile: job 0 (when NJ ==
+// 2) then job 1.  The second job's first slices are queued before the first
+// job's epilogue (which does not use the ring).  A job with K = 0 is its
+// epilogue alone (C = X).  Operands are bf16, K-contiguous, K a multiple of 32.
+template <int TAG, int NJ>
+__global__ __launch_bounds__(256, 2) void gemm_w8_kernel(int64_t M, int64_t N, GemmJob j0,
+                                                         GemmJob j1, int group_m) {
+  __shared__ u32x4 lds[w8::kRingCh + w8::kRedCh];
+  float2* red = reinterpret_cast<float2*>(lds + w8::kRingCh);
+  const TileCoord tc = tile_coord(M, N, 128, 256, group_m);
+  f32x16_v acc[4][2];
+  W8Offsets o;
+  if (NJ == 2) {
+    const int nk0 = static_cast<int>(j0.K / 32);
+    w8_offsets(o, j0.A, j0.B, M, N, tc.m0, tc.n0);
+    w8_prologue(j0.A, j0.B, nk0, tc.m0, tc.n0, o, lds);
+    w8_mainloop(acc, j0.A, j0.B, nk0, tc.m0, tc.n0, o, lds);
+    lds_barrier();  // every wave has read its last fragments of job 0
+  }
+  const int nk1 = static_cast<int>(j1.K / 32);
+  w8_offsets(o, j1.A, j1.B, M, N, tc.m0, tc.n0);
+  w8_prologue(j1.A, j1.B, nk1, tc.m0, tc.n0, o, lds);
+  if (NJ == 2) w8_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, j0.ep, red);
+  w8_mainloop(acc, j1.A, j1.B, nk1, tc.m0, tc.n0, o, lds);
+  w8_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, j1.ep, red);
+}
+
 // ------------------------------------------------------------------ launch
 
 namespace {
@@ -615,6 +1366,57 @@ hipError_t launch_dma(int64_t M, int64_t N, const GemmJob& j0, const GemmJob& j1
   const int64_t kper = splits > 1 ? split_kper(j0.K, splits, 32) : (j0.K > j1.K ? j0.K : j1.K);
   hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 2, 4, EPI, AL, BL, TAG>), grid, dim3(512), 0, s, M,
                      N, kper, j0, j1, njobs, kGroupM);
+  return hipGetLastError();
+}
+
+// Workgroups of the persistent 4-wave kernel: one per CU (a multiple of 8,
+// so each stays within one XCD's tile range), at most one per tile.
+int64_t w4_grid(int64_t tiles) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 256;
+    cus = n / 8 * 8;
+  }
+  return tiles < cus ? tiles : cus;
+}
+
+// Job j1 alone (njobs == 1) or j0 then j1 per tile (njobs == 2).
+template <int TAG>
+hipError_t launch_w8(int64_t M, int64_t N, const GemmJob& j0, const GemmJob& j1, int njobs,
+                     hipStream_t s) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+  const dim3 grid(static_cast<uint32_t>(tiles));
+  if (njobs == 2)
+    hipLaunchKernelGGL((gemm_w8_kernel<TAG, 2>), grid, dim3(w8::kNT), 0, s, M, N, j0, j1, 2 * kGroupM);
+  else
+    hipLaunchKernelGGL((gemm_w8_kernel<TAG, 1>), grid, dim3(w8::kNT), 0, s, M, N, j0, j1, 2 * kGroupM);
+  return hipGetLastError();
+}
+
+// Job j1 alone (njobs == 1) or j0 then j1 per tile (njobs == 2).
+template <int TAG>
+hipError_t launch_w4(int64_t M, int64_t N, const GemmJob& j0, const GemmJob& j1, int njobs,
+                     hipStream_t s) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const dim3 grid(static_cast<uint32_t>(w4_grid(tiles)));
+  if (njobs == 2)
+    hipLaunchKernelGGL((gemm_w4_kernel<TAG, 2>), grid, dim3(w4::kNT), 0, s, M, N, j0, j1, kGroupM);
+  else
+    hipLaunchKernelGGL((gemm_w4_kernel<TAG, 1>), grid, dim3(w4::kNT), 0, s, M, N, j0, j1, kGroupM);
+  return hipGetLastError();
+}
+
+template <int AL, int BL, int TAG>
+hipError_t launch_w4p_t(int64_t M, int64_t N, const Operand& A, const Operand& B, int splits,
+                        float* C, int64_t ldc, hipStream_t s) {
+  const int64_t K = A.kseg * A.nseg;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(splits), 1);
+  hipLaunchKernelGGL((gemm_w4p_kernel<AL, BL, TAG>), grid, dim3(w4::kNT), 0, s, M, N, K,
+                     split_kper(K, splits, 32), A, B, C, ldc, kGroupM);
   return hipGetLastError();
 }
 
@@ -653,6 +1455,27 @@ hipError_t launch_t(int epi, int tag, int64_t M, int64_t N, const Operand& A, co
 }
 }  // namespace
 
+bool w4p_ok(const Operand& A, const Operand& B, int64_t M, int64_t N) {
+  auto lay_ok = [](const Operand& X, int64_t rows) {
+    if (X.layout == LAYOUT_KC) return X.ld % 8 == 0;
+    if (X.layout == LAYOUT_MK) return X.ld % 8 == 0 && rows % 8 == 0;
+    return false;
+  };
+  return A.kseg > 0 && A.kseg % 32 == 0 && A.kseg == B.kseg && A.nseg == B.nseg && N % 4 == 0 &&
+         lay_ok(A, M) && lay_ok(B, N);
+}
+
+hipError_t launch_gemm_w4p(int tag, int64_t M, int64_t N, const Operand& A, const Operand& B,
+                           int splits, float* C, int64_t ldc, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!w4p_ok(A, B, M, N) || splits < 1) return hipErrorInvalidValue;
+  if (A.layout == LAYOUT_KC && B.layout == LAYOUT_MK && tag == 2)
+    return launch_w4p_t<LAYOUT_KC, LAYOUT_MK, 2>(M, N, A, B, splits, C, ldc, s);
+  if (A.layout == LAYOUT_MK && B.layout == LAYOUT_MK && tag == 3)
+    return launch_w4p_t<LAYOUT_MK, LAYOUT_MK, 3>(M, N, A, B, splits, C, ldc, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const Operand& A,
                        const Operand& B, int splits, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
@@ -663,8 +1486,7 @@ hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const 
         return launch_dma<EPI_PARTIAL, LAYOUT_KB, LAYOUT_KB, 3>(M, N, j, j, 1, splits, s);
     } else {
       if (epi == EPI_STATS)
-        return tag == 1 ? launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 1>(M, N, j, j, 1, 1, s)
-                        : launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, j, j, 1, 1, s);
+        return tag == 1 ? launch_w4<1>(M, N, j, j, 1, s) : launch_w4<0>(M, N, j, j, 1, s);
       if (epi == EPI_PARTIAL)
         return launch_dma<EPI_PARTIAL, LAYOUT_KC, LAYOUT_KC, 2>(M, N, j, j, 1, splits, s);
     }
@@ -685,8 +1507,7 @@ hipError_t launch_logits(int dtype, int64_t M, int64_t N, const Operand* A, cons
     j[i] = job_of(A[i], B[i], ep[i]);
     if (j[i].K > 0 && !dma_ok(A[i], B[i])) fused = false;
   }
-  if (fused)
-    return launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 4>(M, N, j[0], j[njobs - 1], njobs, 1, s);
+  if (fused) return launch_w4<4>(M, N, j[0], j[njobs - 1], njobs, s);
   for (int i = 0; i < njobs; ++i) {
     const hipError_t e = launch_gemm(dtype, EPI_STATS, i == njobs - 1 ? 1 : 0, M, N, A[i], B[i], 1,
                                      ep[i], s);

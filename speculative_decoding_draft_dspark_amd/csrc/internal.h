@@ -16,7 +16,9 @@ namespace dspark {
 //              seg[s][(k / c) * c * ld + i * c + k % c]  (k-blocked: c = elements per
 //              16-byte chunk, i.e. c consecutive k of one row are contiguous)
 // Byte offsets i*ld + k (resp. k*ld + i) within one 256-row tile must stay below 2^31.
-enum OperandLayout { LAYOUT_KC = 0, LAYOUT_MC = 1, LAYOUT_KB = 2 };
+// KC: [rows][K] (K contiguous); MC: [K][rows] read element-wise; KB: k-blocked
+// [K/c][rows][c]; MK: [K][rows] (rows contiguous) read with transposing LDS loads.
+enum OperandLayout { LAYOUT_KC = 0, LAYOUT_MC = 1, LAYOUT_KB = 2, LAYOUT_MK = 3 };
 
 struct Operand {
   const void* seg[2];
@@ -60,5 +62,13 @@ hipError_t launch_logits(int dtype, int64_t M, int64_t N, const Operand* A, cons
 
 hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const Operand& A,
                        const Operand& B, int splits, const EpiParams& ep, hipStream_t s);
+
+// bf16 products of the backward pass on the 4-wave kernel: C[split] = A . B^T
+// over K split in `splits` ranges (fp32 partials [splits, M, ldc]).  Each
+// operand is KC or MK; every K segment a multiple of 32; MK operands need
+// rows % 8 == 0.  tag names the kernel symbol (2 = dE, 3 = dW2).
+bool w4p_ok(const Operand& A, const Operand& B, int64_t M, int64_t N);
+hipError_t launch_gemm_w4p(int tag, int64_t M, int64_t N, const Operand& A, const Operand& B,
+                           int splits, float* C, int64_t ldc, hipStream_t s);
 
 }  // namespace dspark
