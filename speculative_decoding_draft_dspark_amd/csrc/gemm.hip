@@ -97,6 +97,13 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// exp(x - m) in the fixed point (2^31 scale) of the tile exp-sums: integer
+// adds make a row's sum independent of the order of its columns, so every
+// epilogue that produces statistics gives bitwise-equal results for equal rows.
+__device__ __forceinline__ uint64_t fix_exp(float x, float m) {
+  return static_cast<uint64_t>(rintf(dexp(x - m) * kFixScale));
+}
+
 // ------------------------------------------------------------------ accumulators
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
@@ -230,10 +237,8 @@ __device__ __forceinline__ void row_epilogue(const AccT& acc, int wr, int wc, fl
         for (int i = 0; i < kVecs; ++i) {
           const int64_t col = n0 + sub * 4 + 32 * i;
           if (col < N) {
-            sum += static_cast<uint64_t>(rintf(dexp(v[i].x - mx) * kFixScale)) +
-                   static_cast<uint64_t>(rintf(dexp(v[i].y - mx) * kFixScale)) +
-                   static_cast<uint64_t>(rintf(dexp(v[i].z - mx) * kFixScale)) +
-                   static_cast<uint64_t>(rintf(dexp(v[i].w - mx) * kFixScale));
+            sum += fix_exp(v[i].x, mx) + fix_exp(v[i].y, mx) + fix_exp(v[i].z, mx) +
+                   fix_exp(v[i].w, mx);
           }
         }
       }
@@ -897,8 +902,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4p_kernel(int64_t M, int64_t N, 
 // row so both the accumulator writes and the row reads are conflict-free),
 // one 32-row block of each wave-row half at a time; then 16 lanes own a row:
 // 256-byte coalesced stores and addend loads, and the row's maximum and
-// exp-sum reduce over 4 shuffle steps in a fixed order, so z' and T, which
-// both take this path, give bitwise-equal statistics for equal rows.
+// fixed-point exp-sum reduce over 4 DPP steps.
 __device__ __forceinline__ int w4_eslot(int row, int c4) { return row * 64 + (c4 ^ (row & 15)); }
 
 // Maximum / sum over each row of 16 lanes with DPP row rotations (VALU
@@ -914,12 +918,21 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, row_ror<2>(v));
   return fmaxf(v, row_ror<1>(v));
 }
-__device__ __forceinline__ float row16_sum(float v) {
-  v += row_ror<8>(v);
-  v += row_ror<4>(v);
-  v += row_ror<2>(v);
-  return v + row_ror<1>(v);
+template <int ROR>
+__device__ __forceinline__ uint64_t row_ror64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<uint32_t>(v)), 0x120 + ROR, 0xf, 0xf, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<uint32_t>(v >> 32)), 0x120 + ROR, 0xf, 0xf, false));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
+__device__ __forceinline__ uint64_t row16_sum(uint64_t v) {
+  v += row_ror64<8>(v);
+  v += row_ror64<4>(v);
+  v += row_ror64<2>(v);
+  return v + row_ror64<1>(v);
+}
+
 
 __device__ __forceinline__ void w4_epilogue(const f32x16_v (&acc)[4][4], int64_t M, int64_t N,
                                             int64_t m0, int64_t n0, int64_t tn,
@@ -977,29 +990,31 @@ __device__ __forceinline__ void w4_epilogue(const f32x16_v (&acc)[4][4], int64_t
         }
       }
       mx = row16_max(mx);
-      float l = 0.f;
+      uint64_t sum = 0;
       if (mx != -INFINITY) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           if (n0 + 4 * sub + 64 * t < N)
-            l += (dexp(v[t].x - mx) + dexp(v[t].y - mx)) + (dexp(v[t].z - mx) + dexp(v[t].w - mx));
+            sum += fix_exp(v[t].x, mx) + fix_exp(v[t].y, mx) + fix_exp(v[t].z, mx) +
+                   fix_exp(v[t].w, mx);
       }
-      l = row16_sum(l);
-      if (sub == 0 && row < M) ep.stats[row * ep.nstat + tn] = make_float2(mx, l);
+      sum = row16_sum(sum);
+      if (sub == 0 && row < M) {
+        const float l = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
+        ep.stats[row * ep.nstat + tn] = make_float2(mx, l);
+      }
     }
   }
 }
 
-// Up to two logits jobs (NJ) over the same 256 x 256 output tile grid: job 0
-// (when NJ == 2) then job 1 per tile.  Persistent: one workgroup per CU
-// walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of the XCD-aware
-// order (gridDim.x a multiple of 8 keeps each workgroup on one XCD's
-// range).  The next job's first two slices are queued into stages 0 and 1
-// before the current job's epilogue, which uses stages 2 and 3, and its
-// third slice right after, so operand loads and the previous tile's stores
-// overlap the epilogue and the next main loop.  A job with K = 0 is its
-// epilogue alone (C = X).  Operands are bf16, K-contiguous, K a multiple of 32.
-template <int NJ>
+// One logits job over the 256 x 256 output tile grid.  Persistent: one
+// workgroup per CU walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of the
+// XCD-aware order (gridDim.x a multiple of 8 keeps each workgroup on one
+// XCD's range).  The next tile's first two slices are queued into stages 0
+// and 1 before the current epilogue, which uses stages 2 and 3, and its third
+// slice right after, so operand loads and the previous tile's stores overlap
+// the epilogue and the next main loop.  K = 0 is the epilogue alone (C = X).
+// Operands are bf16, K-contiguous, K a multiple of 32.
 __device__ __forceinline__ void w4_queue(const GemmJob& J, const TileCoord& tc, int64_t M,
                                          int64_t N, W4Offsets& o, const W4Ring& ring) {
   const int nk = static_cast<int>(J.K / 32);
@@ -1017,323 +1032,35 @@ __device__ __forceinline__ void w4_queue_third(const GemmJob& J, const TileCoord
   if (nk > 0) w4_issue<2, LAYOUT_KC, LAYOUT_KC>(J.A, J.B, 0, 2, nk, shift, tc.m0, tc.n0, o, ring);
 }
 
-template <int TAG, int NJ>
-__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(int64_t M, int64_t N, GemmJob j0,
-                                                         GemmJob j1, int group_m) {
+template <int TAG>
+__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(int64_t M, int64_t N, GemmJob J,
+                                                         int group_m) {
   __shared__ u32x4 st0[w4::kStageCh], st1[w4::kStageCh], st2[w4::kStageCh], st3[w4::kStageCh];
   const W4Ring ring{{st0, st1, st2, st3}};
   float4* ea = reinterpret_cast<float4*>(st2);
   float4* eb = reinterpret_cast<float4*>(st3);
   const int64_t ntiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const GemmJob& first = NJ == 2 ? j0 : j1;
+  const int nk = static_cast<int>(J.K / 32);
   int64_t v = blockIdx.x;
   TileCoord tc = tile_coord_of(v, M, N, 256, 256, group_m);
   f32x16_v acc[4][4];
   W4Offsets o;
-  w4_queue<NJ>(first, tc, M, N, o, ring);
-  w4_queue_third(first, tc, o, ring);
+  w4_queue(J, tc, M, N, o, ring);
+  w4_queue_third(J, tc, o, ring);
   for (;;) {
-    if (NJ == 2) {
-      w4_mainloop<LAYOUT_KC, LAYOUT_KC>(acc, j0.A, j0.B, 0, static_cast<int>(j0.K / 32), tc.m0,
-                                        tc.n0, o, ring);
-      lds_barrier();  // every wave has read its last fragments of job 0
-      w4_queue<NJ>(j1, tc, M, N, o, ring);
-      w4_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, j0.ep, ea, eb);
-      lds_barrier();  // stage 2 is read for the last time
-      w4_queue_third(j1, tc, o, ring);
-    }
-    w4_mainloop<LAYOUT_KC, LAYOUT_KC>(acc, j1.A, j1.B, 0, static_cast<int>(j1.K / 32), tc.m0,
-                                      tc.n0, o, ring);
+    w4_mainloop<LAYOUT_KC, LAYOUT_KC>(acc, J.A, J.B, 0, nk, tc.m0, tc.n0, o, ring);
     const int64_t vn = v + gridDim.x;
     const bool more = vn < ntiles;
     const TileCoord tnext = tile_coord_of(more ? vn : v, M, N, 256, 256, group_m);
-    lds_barrier();  // every wave has read its last fragments of job 1
-    if (more) w4_queue<NJ>(first, tnext, M, N, o, ring);
-    w4_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, j1.ep, ea, eb);
+    lds_barrier();  // every wave has read its last fragments of this tile
+    if (more) w4_queue(J, tnext, M, N, o, ring);
+    w4_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, J.ep, ea, eb);
     if (!more) break;
-    lds_barrier();
-    w4_queue_third(first, tnext, o, ring);
+    lds_barrier();  // stage 2 is read for the last time
+    w4_queue_third(J, tnext, o, ring);
     v = vn;
     tc = tnext;
   }
-}
-
-// ------------------------------------------------------------------ 2-per-CU logits kernel
-
-// The logits projections on 128 x 256 tiles, two workgroups per CU: 4 waves
-// of 64 x 128 (v_mfma_f32_32x32x16_bf16, 128 accumulators, 256 registers a
-// wave), a 3-stage LDS-DMA ring of 32-wide K slices (72 KB) and a 2 KB
-// exchange area per workgroup.  While one workgroup runs its epilogue
-// (stores of the fp32 tile, softmax statistics) the other keeps the matrix
-// pipes busy.  Fragment layout as in the 4-wave kernel: the vocab fragment is
-// the first MFMA operand, so lane (h, r) of block (j, i) holds row 32 i + r
-// of the wave tile at columns 32 j + 8 q + 4 h .. + 3 (elements 4 q ..).
-// The ring and the exchange area are one LDS array.
-namespace w8 {
-constexpr int kNT = 256, kStages = 3;
-constexpr int kACh = 128 * 4, kBCh = 256 * 4, kStageCh = kACh + kBCh;  // 16-byte chunks per slice
-constexpr int kALd = kACh / 64 / 4, kBLd = kBCh / 64 / 4;             // DMA loads per wave per slice
-constexpr int kLps = kALd + kBLd;
-constexpr int kRingCh = kStages * kStageCh;
-constexpr int kRedCh = 2 * 128 * 8 / 16;  // [2 wave columns][128 rows] x (max, sum)
-}  // namespace w8
-
-struct W8Frags {
-  u32x4 a[2][2], b[2][4];  // [k step][block]
-};
-
-__device__ __forceinline__ void w8_read(W8Frags& f, const u32x4* st, int wm, int wn) {
-  const u32x4* As = st;
-  const u32x4* Bs = st + w8::kACh;
-  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) f.a[ks][i] = As[w4_slot(wm * 64 + i * 32 + r, 2 * ks + h)];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[ks][j] = Bs[w4_slot(wn * 128 + j * 32 + r, 2 * ks + h)];
-  }
-}
-
-__device__ __forceinline__ void w8_mma(f32x16_v (&acc)[4][2], const W8Frags& f) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_v, f.b[ks][j]), __builtin_bit_cast(bf16x8_v, f.a[ks][i]),
-            acc[j][i], 0, 0, 0);
-}
-
-struct W8Offsets {
-  uint32_t a[w8::kALd], b[w8::kBLd];
-};
-
-__device__ __forceinline__ void w8_offsets(W8Offsets& o, const Operand& A, const Operand& B,
-                                           int64_t M, int64_t N, int64_t m0, int64_t n0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int p = 0; p < w8::kALd; ++p) {
-    const int idx = (wave * w8::kALd + p) * 64 + lane;
-    const int row = idx >> 2, c = (idx & 3) ^ ((row >> 2) & 3);
-    o.a[p] = (m0 + row < M) ? static_cast<uint32_t>((row * A.ld + c * 8) * 2) : kOutOfRange;
-  }
-#pragma unroll
-  for (int p = 0; p < w8::kBLd; ++p) {
-    const int idx = (wave * w8::kBLd + p) * 64 + lane;
-    const int row = idx >> 2, c = (idx & 3) ^ ((row >> 2) & 3);
-    o.b[p] = (n0 + row < N) ? static_cast<uint32_t>((row * B.ld + c * 8) * 2) : kOutOfRange;
-  }
-}
-
-// Queue virtual slice t (zero slices outside [shift, shift + nk), loaded
-// through a zero-length buffer) into stage t % 3.
-__device__ __forceinline__ void w8_issue(const Operand& A, const Operand& B, int t, int nk,
-                                         int shift, int64_t m0, int64_t n0, const W8Offsets& o,
-                                         u32x4* lds) {
-  const int r = t - shift;
-  const bool real = r >= 0 && r < nk;
-  const int64_t kg = real ? static_cast<int64_t>(r) * 32 : 0;
-  const bool s1 = kg >= A.kseg;  // at most two K segments
-  const int64_t kk = s1 ? kg - A.kseg : kg;
-  const bf16_t* abase = static_cast<const bf16_t*>(s1 ? A.seg[1] : A.seg[0]);
-  const bf16_t* bbase = static_cast<const bf16_t*>(s1 ? B.seg[1] : B.seg[0]);
-  const int nrec = real ? kNumRecords : 0;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(abase + m0 * A.ld + kk), 0, nrec, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(bbase + n0 * B.ld + kk), 0, nrec, kRsrcWord3);
-  u32x4* st = lds + (t % w8::kStages) * w8::kStageCh;
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int p = 0; p < w8::kALd; ++p)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave * w8::kALd + p) * 64), 16,
-                                             o.a[p], 0, 0, 0);
-#pragma unroll
-  for (int p = 0; p < w8::kBLd; ++p)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (lds_void*)(st + w8::kACh + (wave * w8::kBLd + p) * 64), 16, o.b[p], 0, 0, 0);
-}
-
-__device__ __forceinline__ void w8_prologue(const Operand& A, const Operand& B, int nk, int64_t m0,
-                                            int64_t n0, const W8Offsets& o, u32x4* lds) {
-  const int shift = nk & 1;
-#pragma unroll
-  for (int t = 0; t < w8::kStages; ++t) w8_issue(A, B, t, nk, shift, m0, n0, o, lds);
-}
-
-// One step: slice kt's fragments in `cur`; wait for slice kt + 1 (one slice
-// queued after it), queue slice kt + 3 into slice kt's stage (its fragments
-// were read before this barrier), read slice kt + 1 into `nxt`, run slice
-// kt's MFMAs interleaved with those reads and DMA issues.
-__device__ __forceinline__ void w8_step(f32x16_v (&acc)[4][2], const W8Frags& cur, W8Frags& nxt,
-                                        const Operand& A, const Operand& B, int kt, int nk,
-                                        int shift, int64_t m0, int64_t n0, const W8Offsets& o,
-                                        u32x4* lds, int wm, int wn) {
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<w8::kLps>();
-  dma_barrier();
-  w8_issue(A, B, kt + 3, nk, shift, m0, n0, o, lds);
-  w8_read(nxt, lds + ((kt + 1) % w8::kStages) * w8::kStageCh, wm, wn);
-  w8_mma(acc, cur);
-#pragma unroll
-  for (int q = 0; q < 6; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (LDS DMA)
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-}
-
-// K loop of one job (w8_prologue already queued slices 0..2): an even number
-// of virtual slices (a zero slice first when nk is odd) in pairs.
-__device__ __forceinline__ void w8_mainloop(f32x16_v (&acc)[4][2], const Operand& A,
-                                            const Operand& B, int nk, int64_t m0, int64_t n0,
-                                            const W8Offsets& o, u32x4* lds) {
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
-  if (nk <= 0) return;
-  const int shift = nk & 1, nv = nk + shift;
-  wait_vmcnt<2 * w8::kLps>();  // slice 0 has landed (slices 1 and 2 follow it)
-  dma_barrier();
-  W8Frags f0, f1;
-  w8_read(f0, lds, wm, wn);
-  int kt = 0;
-  for (; kt + 2 < nv; kt += 2) {
-    w8_step(acc, f0, f1, A, B, kt, nk, shift, m0, n0, o, lds, wm, wn);
-    w8_step(acc, f1, f0, A, B, kt + 1, nk, shift, m0, n0, o, lds, wm, wn);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<0>();  // the last slice, and the zero slice queued after it, have landed
-  dma_barrier();
-  w8_read(f1, lds + ((kt + 1) % w8::kStages) * w8::kStageCh, wm, wn);
-  w8_mma(acc, f0);
-  w8_mma(acc, f1);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Stores the 128 x 256 tile (plus the bf16 addend X when given) straight
-// from the accumulators and writes, per row, the maximum and exp-sum over
-// its 256 columns: each wave reduces its 128 columns (maximum first, then a
-// float sum of exp(x - max) in a fixed order), and the two halves of a row
-// merge through the exchange area.  z' and T both take this path, so equal
-// rows give bitwise-equal statistics.
-__device__ __forceinline__ void w8_epilogue(const f32x16_v (&acc)[4][2], int64_t M, int64_t N,
-                                            int64_t m0, int64_t n0, int64_t tn,
-                                            const EpiParams& ep, float2* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r = lane & 31;
-  const int64_t c0 = n0 + wn * 128 + 4 * h;  // + 32 j + 8 q
-  const bf16_t* X = static_cast<const bf16_t*>(ep.X);
-  lds_barrier();  // the previous epilogue's reads of the exchange area are done
-  uint2 xn[4][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t row = m0 + wm * 64 + r, col = c0 + 32 * j + 8 * q;
-      xn[j][q] = (X && row < M && col < N) ? *reinterpret_cast<const uint2*>(X + row * ep.ldx + col)
-                                           : uint2{0u, 0u};
-    }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t row = m0 + wm * 64 + 32 * i + r;
-    float4 v[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[j][q] = make_float4(acc[j][i][4 * q] + __uint_as_float(xn[j][q].x << 16),
-                              acc[j][i][4 * q + 1] + __uint_as_float(xn[j][q].x & 0xffff0000u),
-                              acc[j][i][4 * q + 2] + __uint_as_float(xn[j][q].y << 16),
-                              acc[j][i][4 * q + 3] + __uint_as_float(xn[j][q].y & 0xffff0000u));
-      }
-    // addends of the next row block are loaded before this block is stored:
-    // vmcnt retires in issue order, so a load issued after a store cannot be
-    // waited for without also waiting for that store
-    if (X && i == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t col = c0 + 32 * j + 8 * q;
-          xn[j][q] = (row + 32 < M && col < N)
-                         ? *reinterpret_cast<const uint2*>(X + (row + 32) * ep.ldx + col)
-                         : uint2{0u, 0u};
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = c0 + 32 * j + 8 * q;
-        if (col < N) {  // N % 4 == 0: the lane's 4 columns are all in or all out
-          if (row < M) *reinterpret_cast<float4*>(ep.C + row * ep.ldc + col) = v[j][q];
-          mx = fmaxf(mx, fmaxf(fmaxf(v[j][q].x, v[j][q].y), fmaxf(v[j][q].z, v[j][q].w)));
-        }
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    float l = 0.f;
-    if (mx != -INFINITY) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (c0 + 32 * j + 8 * q < N)
-            l += (dexp(v[j][q].x - mx) + dexp(v[j][q].y - mx)) +
-                 (dexp(v[j][q].z - mx) + dexp(v[j][q].w - mx));
-    }
-    l += __shfl_xor(l, 32, kWave);
-    if (h == 0) red[wn * 128 + wm * 64 + 32 * i + r] = make_float2(mx, l);
-  }
-  lds_barrier();
-  if (threadIdx.x < 128) {
-    const int t = threadIdx.x;
-    const int64_t row = m0 + t;
-    if (row < M) {
-      const float2 a = red[t], b = red[128 + t];
-      const float m = fmaxf(a.x, b.x);
-      const float l = m == -INFINITY ? 0.f : a.y * dexp(a.x - m) + b.y * dexp(b.x - m);
-      ep.stats[row * ep.nstat + tn] = make_float2(m, l);
-    }
-  }
-}
-
-// Up to two logits jobs (NJ) per 128 x 256 output tile: job 0 (when NJ ==
-// 2) then job 1.  The second job's first slices are queued before the first
-// job's epilogue (which does not use the ring).  A job with K = 0 is its
-// epilogue alone (C = X).  Operands are bf16, K-contiguous, K a multiple of 32.
-template <int TAG, int NJ>
-__global__ __launch_bounds__(256, 2) void gemm_w8_kernel(int64_t M, int64_t N, GemmJob j0,
-                                                         GemmJob j1, int group_m) {
-  __shared__ u32x4 lds[w8::kRingCh + w8::kRedCh];
-  float2* red = reinterpret_cast<float2*>(lds + w8::kRingCh);
-  const TileCoord tc = tile_coord(M, N, 128, 256, group_m);
-  f32x16_v acc[4][2];
-  W8Offsets o;
-  if (NJ == 2) {
-    const int nk0 = static_cast<int>(j0.K / 32);
-    w8_offsets(o, j0.A, j0.B, M, N, tc.m0, tc.n0);
-    w8_prologue(j0.A, j0.B, nk0, tc.m0, tc.n0, o, lds);
-    w8_mainloop(acc, j0.A, j0.B, nk0, tc.m0, tc.n0, o, lds);
-    lds_barrier();  // every wave has read its last fragments of job 0
-  }
-  const int nk1 = static_cast<int>(j1.K / 32);
-  w8_offsets(o, j1.A, j1.B, M, N, tc.m0, tc.n0);
-  w8_prologue(j1.A, j1.B, nk1, tc.m0, tc.n0, o, lds);
-  if (NJ == 2) w8_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, j0.ep, red);
-  w8_mainloop(acc, j1.A, j1.B, nk1, tc.m0, tc.n0, o, lds);
-  w8_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, j1.ep, red);
 }
 
 // ------------------------------------------------------------------ launch
@@ -1383,29 +1110,11 @@ int64_t w4_grid(int64_t tiles) {
   return tiles < cus ? tiles : cus;
 }
 
-// Job j1 alone (njobs == 1) or j0 then j1 per tile (njobs == 2).
 template <int TAG>
-hipError_t launch_w8(int64_t M, int64_t N, const GemmJob& j0, const GemmJob& j1, int njobs,
-                     hipStream_t s) {
-  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
-  const dim3 grid(static_cast<uint32_t>(tiles));
-  if (njobs == 2)
-    hipLaunchKernelGGL((gemm_w8_kernel<TAG, 2>), grid, dim3(w8::kNT), 0, s, M, N, j0, j1, 2 * kGroupM);
-  else
-    hipLaunchKernelGGL((gemm_w8_kernel<TAG, 1>), grid, dim3(w8::kNT), 0, s, M, N, j0, j1, 2 * kGroupM);
-  return hipGetLastError();
-}
-
-// Job j1 alone (njobs == 1) or j0 then j1 per tile (njobs == 2).
-template <int TAG>
-hipError_t launch_w4(int64_t M, int64_t N, const GemmJob& j0, const GemmJob& j1, int njobs,
-                     hipStream_t s) {
+hipError_t launch_w4(int64_t M, int64_t N, const GemmJob& J, hipStream_t s) {
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const dim3 grid(static_cast<uint32_t>(w4_grid(tiles)));
-  if (njobs == 2)
-    hipLaunchKernelGGL((gemm_w4_kernel<TAG, 2>), grid, dim3(w4::kNT), 0, s, M, N, j0, j1, kGroupM);
-  else
-    hipLaunchKernelGGL((gemm_w4_kernel<TAG, 1>), grid, dim3(w4::kNT), 0, s, M, N, j0, j1, kGroupM);
+  hipLaunchKernelGGL((gemm_w4_kernel<TAG>), dim3(static_cast<uint32_t>(w4_grid(tiles))),
+                     dim3(w4::kNT), 0, s, M, N, J, kGroupM);
   return hipGetLastError();
 }
 
@@ -1486,7 +1195,8 @@ hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const 
         return launch_dma<EPI_PARTIAL, LAYOUT_KB, LAYOUT_KB, 3>(M, N, j, j, 1, splits, s);
     } else {
       if (epi == EPI_STATS)
-        return tag == 1 ? launch_w4<1>(M, N, j, j, 1, s) : launch_w4<0>(M, N, j, j, 1, s);
+        return tag == 1 ? launch_w4<1>(M, N, j, s)
+                        : launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, j, j, 1, 1, s);
       if (epi == EPI_PARTIAL)
         return launch_dma<EPI_PARTIAL, LAYOUT_KC, LAYOUT_KC, 2>(M, N, j, j, 1, splits, s);
     }
@@ -1495,22 +1205,30 @@ hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const 
                     : launch_t<float>(epi, tag, M, N, A, B, splits, ep, s);
 }
 
-// Both logits projections of the forward pass in one launch when both can use
-// the DMA path (bf16, K-contiguous, K a multiple of 32 or K = 0); otherwise one
-// launch each.
+// The logits projections of the forward pass: the corrected draft logits
+// (K = markov rank, memory-bound: the 8-wave kernel, whose epilogue overlaps
+// other workgroups' work) and then the teacher logits (K = hidden: the
+// persistent 4-wave kernel).  Both epilogues compute the tile statistics the
+// same way (maximum; fixed-point exp-sum), so equal rows give equal results.
+// Where the bf16 DMA paths do not apply, both jobs take the generic kernel.
 hipError_t launch_logits(int dtype, int64_t M, int64_t N, const Operand* A, const Operand* B,
                          const EpiParams* ep, int njobs, hipStream_t s) {
   if (M <= 0 || N <= 0 || njobs <= 0) return hipSuccess;
-  bool fused = dtype == 1 && njobs <= 2;
+  bool dma = dtype == 1 && njobs <= 2;
   GemmJob j[2];
   for (int i = 0; i < njobs; ++i) {
     j[i] = job_of(A[i], B[i], ep[i]);
-    if (j[i].K > 0 && !dma_ok(A[i], B[i])) fused = false;
+    if (j[i].K > 0 && !dma_ok(A[i], B[i])) dma = false;
   }
-  if (fused) return launch_w4<4>(M, N, j[0], j[njobs - 1], njobs, s);
+  if (dma) {
+    hipError_t e = launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, j[0], j[0], 1, 1, s);
+    if (e == hipSuccess && njobs == 2) e = launch_w4<1>(M, N, j[1], s);
+    return e;
+  }
   for (int i = 0; i < njobs; ++i) {
-    const hipError_t e = launch_gemm(dtype, EPI_STATS, i == njobs - 1 ? 1 : 0, M, N, A[i], B[i], 1,
-                                     ep[i], s);
+    const hipError_t e = (dtype == 1)
+        ? launch_t<bf16_t>(EPI_STATS, i == njobs - 1 ? 1 : 0, M, N, A[i], B[i], 1, ep[i], s)
+        : launch_t<float>(EPI_STATS, i == njobs - 1 ? 1 : 0, M, N, A[i], B[i], 1, ep[i], s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
