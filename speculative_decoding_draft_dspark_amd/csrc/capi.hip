@@ -24,6 +24,7 @@ inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Dims {
   int64_t B, N, K, R, Vd, Vt, H, Hd, r, nstat, splits, conf_chunks, F;
   int64_t R32;  // R rounded up to a multiple of 32 (k-blocked row operands)
+  int64_t dw2_splits;  // K splits of the in-place dW2 product (hi and lo rows)
   int dtype, gdtype, esize;
   bool markov, conf, conf_markov;
   // bf16 backward products read G, W2 and E in place (row counts and the
@@ -37,7 +38,8 @@ struct Layout {
   size_t total;
 };
 
-constexpr int kRowArrays = 10;  // float row arrays of RowState (w .. dcoef)
+constexpr int kRowArrays = 10;
+constexpr int64_t kCUs = 256;  // compute units of an MI355X (sizes the dE split count)  // float row arrays of RowState (w .. dcoef)
 
 int make_dims(const dspark_shape* sh, Dims* d) {
   if (!sh) return DSPARK_ERR_NULL;
@@ -70,14 +72,25 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   if (sp > 32) sp = 32;
   if (sp < 1) sp = 1;
   d->direct_bwd = d->dtype == DSPARK_BF16 && d->markov && d->R % 32 == 0 && d->Vd % 32 == 0;
+  d->dw2_splits = 2;
   if (d->direct_bwd) {
-    // dE over vocabulary splits: about two waves of 256 workgroups, each split
-    // at least 8 slices of 32 of the 2 Vd (hi, lo) contraction
-    int64_t ds = (512 + nM - 1) / nM;
-    const int64_t dmax = 2 * d->Vd / 32 / 8;
-    if (ds > dmax) ds = dmax;
-    if (ds > 64) ds = 64;
-    sp = ds < 1 ? 1 : ds;
+    // Split counts of the in-place products: the smallest whose tiles x
+    // splits workgroups fill whole waves of the 256 CUs within 2 %, each
+    // split at least 8 slices of 32 of its (hi, lo) contraction.
+    auto pick = [](int64_t tiles, int64_t slices) {
+      int64_t best = 1;
+      double best_eff = 0.0;
+      for (int64_t ds = 1; ds <= 64 && ds * 8 <= slices; ++ds) {
+        const int64_t wg = tiles * ds, waves = (wg + kCUs - 1) / kCUs;
+        const double eff = static_cast<double>(wg) / static_cast<double>(waves * kCUs);
+        if (eff > best_eff + 0.02) { best = ds; best_eff = eff; }
+      }
+      return best;
+    };
+    sp = pick(nM, 2 * d->Vd / 32);
+    // dW2: one split per hi / lo half of the rows (more splits measured slower:
+    // the partial-sum traffic outweighs the better wave fill)
+    d->dw2_splits = 2 * d->R / 32 >= 16 ? 2 : 1;
   }
   d->splits = d->markov ? sp : 0;
   d->conf_chunks = d->R < 256 ? static_cast<int>(d->R) : 256;
@@ -102,7 +115,7 @@ Layout make_layout(const Dims& d) {
     if (d.gdtype != DSPARK_BF16) { L.ghi = o; o = up(o + RV * 2); }
     L.glo = o; o = up(o + RV * 2);
     if (d.markov && d.direct_bwd) {
-      L.dw2part = o; o = up(o + static_cast<size_t>(2) * d.Vd * d.r * 4);
+      L.dw2part = o; o = up(o + static_cast<size_t>(d.dw2_splits) * d.Vd * d.r * 4);
     } else if (d.markov) {
       const size_t R32V = static_cast<size_t>(d.R32) * d.Vd;
       L.w2t = o; o = up(o + static_cast<size_t>(d.Vd) * d.r * 2);
@@ -381,16 +394,16 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
       DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
       DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
                                             out->d_markov_w1, s));
-      {  // dW2 = [G hi ; G lo]^T . [E ; E]: hi and lo as two splits, then summed
+      {  // dW2 = [G hi ; G lo]^T . [E ; E] over row splits, then summed
         float* part = reinterpret_cast<float*>(ws + L.dw2part);
         Operand A{}, B{};
         A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.R; A.kpad = d.R;
         A.ld = d.Vd; A.layout = LAYOUT_MK; A.nseg = 2;
         B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = d.R; B.ld = d.r;
         B.layout = LAYOUT_MK; B.nseg = 2;
-        DSPARK_STAGE(kDw2Gemm, launch_gemm_w4p(3, d.Vd, d.r, A, B, 2, part, d.r, s));
-        DSPARK_STAGE(kDw2Gemm, launch_add2(d.Vd * d.r, part, part + d.Vd * d.r,
-                                           out->d_markov_w2, s));
+        const int sp = static_cast<int>(d.dw2_splits);
+        DSPARK_STAGE(kDw2Gemm, launch_gemm_w4p(3, d.Vd, d.r, A, B, sp, part, d.r, s));
+        DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, sp, part, out->d_markov_w2, s));
       }
     } else if (d.markov) {
       DSPARK_STAGE(kGradSweep, launch_grad_sweep8(d.gdtype, d.R, rgroups, d.Vd, Zp, T,

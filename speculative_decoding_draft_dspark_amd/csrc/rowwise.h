@@ -57,6 +57,8 @@ hipError_t launch_transpose_bf16(int64_t rows, int64_t cols, const void* in, voi
 hipError_t launch_embed_blocked(int64_t R, int64_t rgroups, int64_t rank, const void* E, void* out,
                                 hipStream_t s);
 hipError_t launch_add2(int64_t n, const float* a, const float* b, float* out, hipStream_t s);
+// out = sum over k < parts of p[k * n .. k * n + n) (n % 4 == 0), in order of k.
+hipError_t launch_sum_parts(int64_t n, int parts, const float* p, float* out, hipStream_t s);
 hipError_t launch_de_reduce(int dtype, int64_t R, int64_t rank, int splits, const float* part,
                             RowState rs, int conf_markov, const void* Wc, int64_t Hd, float g,
                             float c_a, float* dE, hipStream_t s);

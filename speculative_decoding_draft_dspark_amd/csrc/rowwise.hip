@@ -625,6 +625,26 @@ __global__ void add2_kernel(int64_t n4, const float4* a, const float4* b, float4
   out[i] = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
 }
 
+// out = sum of `parts` slices of n floats (split-K partials), in slice order.
+__global__ void sum_parts_kernel(int64_t n4, int parts, const float4* p, float4* out) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = p[i];
+  for (int k = 1; k < parts; ++k) {
+    const float4 x = p[k * n4 + i];
+    acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+  }
+  out[i] = acc;
+}
+
+hipError_t launch_sum_parts(int64_t n, int parts, const float* p, float* out, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 <= 0 || parts <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(static_cast<uint32_t>((n4 + 255) / 256)), dim3(256), 0,
+                     s, n4, parts, reinterpret_cast<const float4*>(p), reinterpret_cast<float4*>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_add2(int64_t n, const float* a, const float* b, float* out, hipStream_t s) {
   const int64_t n4 = n / 4;
   if (n4 <= 0) return hipSuccess;
