@@ -66,6 +66,18 @@ enum {
   DSPARK_ERR_HIP = -7         /* a HIP launch failed; see dspark_last_hip_error() */
 };
 
+/* Bits of dspark_shape.options; an unknown bit makes the shape invalid
+ * (DSPARK_ERR_SHAPE, workspace size 0). */
+enum {
+  /* Do not store the fp32 Markov-corrected draft logits z + W2 W1[prev]: each
+   * vocabulary sweep (softmax statistics, L1, gradient) recomputes the rank-r
+   * bias from W2 and the gathered W1 rows on bf16 MFMA.  The workspace shrinks
+   * by 4 R Vd bytes, for a few per cent more time.  Applies to bf16 inputs with
+   * markov_rank in {32, 64, 128, 256} and R, Vd multiples of 32; ignored
+   * elsewhere.  (Without a Markov head the sweeps always read z directly.) */
+  DSPARK_OPT_RECOMPUTE_BIAS = 1u
+};
+
 /* Bits of the device word dspark_fwd_out.flags (OR-ed, never cleared by bwd). */
 enum {
   DSPARK_FLAG_TARGET_ID_RANGE = 1u, /* a supervised slot has target id outside [0, draft_vocab) */
@@ -86,7 +98,7 @@ typedef struct {
   int32_t with_markov_conf; /* 1: confidence input is [hidden ; markov embedding] (proj [1, Hd + r]) */
   int32_t dtype;          /* DSPARK_F32 or DSPARK_BF16: type of every float input */
   int32_t grad_dtype;     /* type written to d_draft_logits */
-  int32_t reserved;
+  int32_t options;        /* DSPARK_OPT_* bits (0 = defaults); fwd and bwd must pass the same */
 } dspark_shape;
 
 /* `dspark_loss` keyword arguments (API page, defaults 0.1 / 0.9 / 1.0 / 4.0). */

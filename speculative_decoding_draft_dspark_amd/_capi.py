@@ -17,6 +17,7 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_NO_TARGET",
           -5: "ERR_WORKSPACE", -6: "ERR_ALIGN", -7: "ERR_HIP"}
 FLAG_TARGET_ID_RANGE, FLAG_PREV_ID_RANGE, FLAG_NONFINITE, FLAG_NO_TEACHER = 1, 2, 4, 8
+OPT_RECOMPUTE_BIAS = 1
 
 
 class Shape(C.Structure):
@@ -24,7 +25,7 @@ class Shape(C.Structure):
                 ("draft_vocab", C.c_int64), ("target_vocab", C.c_int64), ("hidden", C.c_int64),
                 ("conf_hidden", C.c_int64), ("markov_rank", C.c_int64),
                 ("with_markov_conf", C.c_int32), ("dtype", C.c_int32), ("grad_dtype", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("options", C.c_int32)]
 
 
 class HParamsC(C.Structure):

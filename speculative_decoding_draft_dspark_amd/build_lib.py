@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["gemm.hip", "rowwise.hip", "capi.hip"]
+SOURCES = ["gemm.hip", "rowwise.hip", "bias_sweep.hip", "capi.hip"]
 LIB = os.path.join(PKG, "libdspark.so")
 ARCH = "gfx950"
 

@@ -1,0 +1,50 @@
+// Vocabulary sweeps over the corrected draft logits z' = z + E . W2^T that
+// recompute the low-rank Markov bias tile by tile (bf16 MFMA) instead of
+// reading a stored z' (NeMo-RL "DSpark Auxiliary Heads": the Markov head adds
+// W2 . W1[prev] to the draft logits).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rowwise.h"
+
+namespace dspark {
+
+// Ranks the bias sweeps handle (0 = no Markov head: z' = z).
+bool bias_sweep_rank_ok(int64_t rank);
+
+// Row tiles of 128 rows x vocabulary splits of `vsplit` columns (a multiple of
+// 256) each sweep launches.
+struct BiasGrid {
+  int64_t row_tiles, splits, vsplit;
+};
+BiasGrid bias_grid(int64_t R, int64_t V);
+
+// Per (row, 256-column tile) maximum and fixed-point exp-sum of z' into sz
+// [R, nstat], computed exactly as the logits GEMM epilogue computes them for T.
+// z [R, V] bf16, E [R, rank] bf16 (zero rows on unsupervised slots), W2 [V, rank] bf16.
+hipError_t launch_bias_stats(int64_t R, int64_t V, int64_t rank, const bf16_t* z, const bf16_t* E,
+                             const bf16_t* W2, float2* sz, int64_t nstat, hipStream_t s);
+
+// On supervised rows, per vocabulary split: sum |p - q| and sum p sign(p - q)
+// (fp64 partials [splits, R] each; 0 without a teacher, T == nullptr), and
+// z'_y of the target column (zy [R]), with p = exp(z' - lse_z), q = exp(T - lse_t).
+hipError_t launch_bias_l1(int64_t R, int64_t V, int64_t rank, const bf16_t* z, const bf16_t* E,
+                          const bf16_t* W2, const float* T, const int32_t* tid, RowState rs,
+                          double* part_l1, double* part_s, float* zy, hipStream_t s);
+
+// Per row: L1, S and CE from the split partials and z'_y (masked rows: 0).
+hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int splits, const double* part_l1,
+                                 const double* part_s, const float* zy, RowState rs,
+                                 hipStream_t s);
+
+// G = g w [ce_a (p - [v = y]) + l1_a p (sign(p - q) - S)] (0 on unsupervised rows):
+// dz in the gradient dtype (grad_dtype 1 = bf16: dz is the bf16 high part),
+// ghi = bf16(G) when dz is fp32, glo = bf16(G - bf16(G)).
+hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, const bf16_t* z,
+                            const bf16_t* E, const bf16_t* W2, const float* T, const int32_t* tid,
+                            RowState rs, int has_teacher, float g, float ce_a, float l1_a, void* dz,
+                            bf16_t* ghi, bf16_t* glo, hipStream_t s);
+
+}  // namespace dspark

@@ -11,6 +11,7 @@
 
 #include "../../include/dspark.h"
 #include "internal.h"
+#include "bias_sweep.h"
 #include "rowwise.h"
 
 namespace dspark {
@@ -30,10 +31,15 @@ struct Dims {
   // bf16 backward products read G, W2 and E in place (row counts and the
   // vocabulary multiples of 32); otherwise through transposed / k-blocked copies
   bool direct_bwd;
+  // bf16 corrected draft logits never stored: every vocabulary sweep rebuilds
+  // z' = z + E W2^T (ranks the bias sweeps support, with the in-place backward)
+  bool bias_path;
+  int64_t bsplits;  // vocabulary splits of the bias sweeps
 };
 
 struct Layout {
   size_t Zp, T, sz, st, E, mask, rowf, ghi, glo, g32, dEpart, dE, confpart;
+  size_t pl1, ps, zy;  // bias path: L1 / S split partials, z'_y
   size_t w2t, eblk, blkhi, blklo, dw2part;  // bf16 backward operands
   size_t total;
 };
@@ -50,6 +56,7 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   if (sh->markov_rank < 0 || sh->markov_rank % 8) return DSPARK_ERR_SHAPE;
   if (sh->hidden < 0 || sh->hidden % 8) return DSPARK_ERR_SHAPE;
   if (sh->conf_hidden < 0) return DSPARK_ERR_SHAPE;
+  if (sh->options & ~static_cast<int32_t>(DSPARK_OPT_RECOMPUTE_BIAS)) return DSPARK_ERR_SHAPE;
   if (sh->markov_rank > 0 && sh->target_vocab <= 0) return DSPARK_ERR_SHAPE;
   if (sh->draft_vocab > (int64_t{1} << 26) || sh->hidden > (int64_t{1} << 20) ||
       sh->markov_rank > 4096)
@@ -93,6 +100,13 @@ int make_dims(const dspark_shape* sh, Dims* d) {
     d->dw2_splits = 2 * d->R / 32 >= 16 ? 2 : 1;
   }
   d->splits = d->markov ? sp : 0;
+  // Sweeps that rebuild z' from z instead of reading a stored fp32 z': always
+  // without a Markov head (z' = z), on request with one (slower: the bias is
+  // recomputed in each of the three sweeps, but the R x Vd fp32 buffer goes).
+  d->bias_path = d->dtype == DSPARK_BF16 && bias_sweep_rank_ok(d->r) &&
+                 (!d->markov ||
+                  (d->direct_bwd && (sh->options & DSPARK_OPT_RECOMPUTE_BIAS) != 0));
+  d->bsplits = d->bias_path ? bias_grid(d->R, d->Vd).splits : 0;
   d->conf_chunks = d->R < 256 ? static_cast<int>(d->R) : 256;
   d->F = d->Hd + (d->conf_markov ? d->r : 0);
   d->R32 = (d->R + 31) / 32 * 32;
@@ -103,7 +117,14 @@ Layout make_layout(const Dims& d) {
   Layout L{};
   size_t o = 0;
   const size_t RV = static_cast<size_t>(d.R) * d.Vd;
-  L.Zp = o; o = up(o + RV * 4);
+  L.Zp = o;
+  if (!d.bias_path) o = up(o + RV * 4);
+  L.pl1 = L.ps = L.zy = o;
+  if (d.bias_path) {
+    L.pl1 = o; o = up(o + static_cast<size_t>(d.bsplits) * d.R * 8);
+    L.ps = o; o = up(o + static_cast<size_t>(d.bsplits) * d.R * 8);
+    L.zy = o; o = up(o + static_cast<size_t>(d.R) * 4);
+  }
   L.T = o; o = up(o + RV * 4);
   L.sz = o; o = up(o + static_cast<size_t>(d.R) * d.nstat * 8);
   L.st = o; o = up(o + static_cast<size_t>(d.R) * d.nstat * 8);
@@ -162,11 +183,11 @@ enum Teacher { kNone = 0, kHidden = 1, kAligned = 2 };
 
 // ---- per-stage timers (tracing aid)
 enum Stage {
-  kPrep, kGather, kLogitsGemm, kL1Sweep, kFinalize, kReduce, kGradSweep, kOperandPrep,
+  kPrep, kGather, kLogitsGemm, kBiasStats, kL1Sweep, kFinalize, kReduce, kGradSweep, kOperandPrep,
   kDeGemm, kDeReduce, kDw1, kDw2Gemm, kConfBwd, kStages
 };
 const char* const kStageNames[kStages] = {
-    "prep_rows", "gather_embed", "logits_gemm", "l1_sweep",
+    "prep_rows", "gather_embed", "logits_gemm", "bias_stats", "l1_sweep",
     "finalize_rows", "reduce_fwd", "grad_sweep", "operand_prep", "dE_gemm", "dE_reduce",
     "dW1_scatter",
     "dW2_gemm", "conf_bwd"};
@@ -294,6 +315,37 @@ int dspark_loss_fwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     DSPARK_STAGE(kGather, launch_gather_embed(d.dtype, d.R, d.r, d.Vt, in->prev_ids, rs.mask, in->markov_w1,
                                    E, s));
 
+  if (d.bias_path) {
+    // Teacher logits T (fp32) with per-tile statistics; the corrected draft
+    // logits are rebuilt inside each sweep and never stored.
+    if (teacher != kNone) {
+      Operand A{}, B{};
+      EpiParams ep{};
+      A.nseg = B.nseg = 1;
+      A.layout = B.layout = LAYOUT_KC;
+      ep.C = T; ep.ldc = d.Vd; ep.stats = stt; ep.nstat = d.nstat;
+      if (teacher == kHidden) {
+        A.seg[0] = A.seg[1] = in->target_hidden; A.kseg = d.H; A.kpad = gemm_kpad(d.H, d.esize);
+        A.ld = d.H;
+        B.seg[0] = B.seg[1] = in->lm_head; B.kseg = d.H; B.kpad = A.kpad; B.ld = d.H;
+      } else {  // K = 0: T = aligned logits
+        ep.X = in->aligned_target_logits; ep.ldx = d.Vd;
+      }
+      DSPARK_STAGE(kLogitsGemm, launch_gemm(d.dtype, EPI_STATS, 1, d.R, d.Vd, A, B, 1, ep, s));
+    }
+    const bf16_t* z = static_cast<const bf16_t*>(in->draft_logits);
+    const bf16_t* Eb = d.markov ? static_cast<const bf16_t*>(E) : nullptr;
+    const bf16_t* W2 = d.markov ? static_cast<const bf16_t*>(in->markov_w2) : nullptr;
+    double* pl1 = reinterpret_cast<double*>(ws + L.pl1);
+    double* ps = reinterpret_cast<double*>(ws + L.ps);
+    float* zy = reinterpret_cast<float*>(ws + L.zy);
+    DSPARK_STAGE(kBiasStats, launch_bias_stats(d.R, d.Vd, d.r, z, Eb, W2, sz, d.nstat, s));
+    DSPARK_STAGE(kL1Sweep, launch_lse_rows(d.R, sz, stt, d.nstat, rs.mask, teacher != kNone, rs, s));
+    DSPARK_STAGE(kL1Sweep, launch_bias_l1(d.R, d.Vd, d.r, z, Eb, W2, teacher != kNone ? T : nullptr,
+                                          in->target_ids, rs, pl1, ps, zy, s));
+    DSPARK_STAGE(kL1Sweep, launch_bias_l1_finish(d.R, d.Vd, static_cast<int>(d.bsplits), pl1, ps,
+                                                 zy, rs, s));
+  } else {
   // Corrected draft logits z' = z + E W2^T and teacher logits T (both fp32),
   // each with per-tile softmax statistics, over the same [R, Vd] tile grid.
   {
@@ -324,6 +376,7 @@ int dspark_loss_fwd(const dspark_shape* shape, const dspark_hparams* hp, const d
   }
   DSPARK_STAGE(kL1Sweep, launch_l1_sweep(d.R, d.Vd, Zp, T, sz, stt, d.nstat, rs.mask, in->target_ids,
                              teacher != kNone, rs, s));
+  }
   DSPARK_STAGE(kFinalize, launch_finalize_rows(d.dtype, d.R, d.Hd, d.r, d.conf_markov, d.conf,
                                   in->conf_hidden, E, in->conf_w, in->conf_b, rs,
                                   out->accept_rate, out->row_terms, out->flags, hp->ce_alpha,
@@ -373,12 +426,24 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     bf16_t* bhi = reinterpret_cast<bf16_t*>(ws + L.blkhi);
     bf16_t* blo = reinterpret_cast<bf16_t*>(ws + L.blklo);
     const int64_t rgroups = d.R32 / 8;
+    if (d.bias_path) {
+      // G (z' rebuilt from z, E and W2) as dz (hi) and its bf16 remainder (lo)
+      DSPARK_STAGE(kGradSweep, launch_bias_grad(
+                                   d.gdtype, d.R, d.Vd, d.r,
+                                   static_cast<const bf16_t*>(in->draft_logits),
+                                   d.markov ? static_cast<const bf16_t*>(E) : nullptr,
+                                   d.markov ? static_cast<const bf16_t*>(in->markov_w2) : nullptr,
+                                   teacher != kNone ? T : nullptr, in->target_ids, rs,
+                                   teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
+                                   out->d_draft_logits, ghi, d.markov ? glo : nullptr, s));
+    }
     if (d.direct_bwd) {
       // G as dz (hi) and its bf16 remainder (lo), row-major; both products
       // read G, W2 and E in place.
-      DSPARK_STAGE(kGradSweep, launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs,
-                                                 teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
-                                                 out->d_draft_logits, ghi, glo, nullptr, s));
+      if (!d.bias_path)
+        DSPARK_STAGE(kGradSweep, launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs,
+                                                   teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
+                                                   out->d_draft_logits, ghi, glo, nullptr, s));
       {  // dE partials = [G hi | G lo] . [W2 | W2] over vocabulary splits
         Operand A{}, B{};
         A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.Vd; A.kpad = d.Vd;
@@ -410,7 +475,7 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
                                                   in->target_ids, rs, teacher != kNone, g,
                                                   hp->ce_alpha, hp->l1_alpha, out->d_draft_logits,
                                                   ghi, glo, bhi, blo, s));
-    } else {
+    } else if (!d.bias_path) {
       DSPARK_STAGE(kGradSweep, launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs,
                                                  teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
                                                  out->d_draft_logits, nullptr, nullptr, nullptr,

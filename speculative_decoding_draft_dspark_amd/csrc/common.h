@@ -62,6 +62,21 @@ __device__ __forceinline__ float dexp(float x) { return __builtin_amdgcn_exp2f(x
 
 __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
 
+// exp(x - m) for x <= m in the fixed point (2^31 scale) of the tile
+// exp-sums, as 2^(x log2 e + 31 - m log2 e) truncated to an integer (one fma,
+// one exp2, one conversion).  At x = m the exponent is 31 plus the rounding
+// error of m log2 e, far below 32 for any finite logit, so 32 bits hold it.
+// Sums of these integers do not depend on the order of the columns, and every
+// kernel that produces tile statistics uses this one routine, so equal rows
+// give bitwise-equal statistics.
+__device__ __forceinline__ float fix_exp_offset(float m) { return 31.f - m * kLog2e; }
+__device__ __forceinline__ uint32_t fix_exp32o(float x, float off) {
+  return static_cast<uint32_t>(__builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, off)));
+}
+__device__ __forceinline__ uint32_t fix_exp32(float x, float m) {
+  return fix_exp32o(x, fix_exp_offset(m));
+}
+
 // ---- reductions -----------------------------------------------------------
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -97,12 +97,8 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// exp(x - m) in the fixed point (2^31 scale) of the tile exp-sums: integer
-// adds make a row's sum independent of the order of its columns, so every
-// epilogue that produces statistics gives bitwise-equal results for equal rows.
-__device__ __forceinline__ uint64_t fix_exp(float x, float m) {
-  return static_cast<uint64_t>(rintf(dexp(x - m) * kFixScale));
-}
+// exp(x - m) in the fixed point of the tile exp-sums, widened for summing.
+__device__ __forceinline__ uint64_t fix_exp(float x, float m) { return fix_exp32(x, m); }
 
 // ------------------------------------------------------------------ accumulators
 

@@ -33,6 +33,9 @@ hipError_t launch_gather_embed(int dtype, int64_t R, int64_t rank, int64_t Vt, c
 hipError_t launch_l1_sweep(int64_t R, int64_t V, const float* Zp, const float* Tt,
                            const float2* sz, const float2* st, int64_t nstat, const uint8_t* mask,
                            const int32_t* tid, int has_teacher, RowState rs, hipStream_t s);
+// lse_z, lse_t of supervised rows from tile statistics (0 on the others).
+hipError_t launch_lse_rows(int64_t R, const float2* sz, const float2* st, int64_t nstat,
+                           const uint8_t* mask, int has_teacher, RowState rs, hipStream_t s);
 hipError_t launch_finalize_rows(int dtype, int64_t R, int64_t Hd, int64_t rank,
                                 int with_markov_conf, int has_conf, const void* hd, const void* E,
                                 const void* Wc, const void* bc, RowState rs, float* accept_out,

@@ -181,6 +181,32 @@ __global__ __launch_bounds__(kSweepThreads) void l1_sweep_kernel(
   }
 }
 
+// Per supervised row: log-sum-exp of the corrected draft logits and of the
+// teacher logits from their tile statistics (the same merge as l1_sweep_kernel).
+__global__ __launch_bounds__(kSweepThreads) void lse_rows_kernel(const float2* sz, const float2* st,
+                                                                 int64_t nstat, const uint8_t* mask,
+                                                                 int has_teacher, float* lse_z,
+                                                                 float* lse_t) {
+  __shared__ float fscr[kSweepThreads / kWave];
+  __shared__ double dscr[kSweepThreads / kWave];
+  const int64_t r = blockIdx.x;
+  if (!mask[r]) {
+    if (threadIdx.x == 0) { lse_z[r] = 0.f; lse_t[r] = 0.f; }
+    return;
+  }
+  const float lz = merge_lse(sz + r * nstat, nstat, fscr, dscr);
+  const float lt = has_teacher ? merge_lse(st + r * nstat, nstat, fscr, dscr) : 0.f;
+  if (threadIdx.x == 0) { lse_z[r] = lz; lse_t[r] = lt; }
+}
+
+hipError_t launch_lse_rows(int64_t R, const float2* sz, const float2* st, int64_t nstat,
+                           const uint8_t* mask, int has_teacher, RowState rs, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_rows_kernel, dim3(static_cast<uint32_t>(R)), dim3(kSweepThreads), 0, s, sz,
+                     st, nstat, mask, has_teacher, rs.lse_z, rs.lse_t);
+  return hipGetLastError();
+}
+
 hipError_t launch_l1_sweep(int64_t R, int64_t V, const float* Zp, const float* Tt,
                            const float2* sz, const float2* st, int64_t nstat, const uint8_t* mask,
                            const int32_t* tid, int has_teacher, RowState rs, hipStream_t s) {

@@ -96,7 +96,8 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
-def make_shape(b: DSparkBatch, grad_dtype: Optional[torch.dtype] = None) -> capi.Shape:
+def make_shape(b: DSparkBatch, grad_dtype: Optional[torch.dtype] = None,
+               options: int = 0) -> capi.Shape:
     z = b.draft_logits
     Vd = z.shape[-1]
     dt = _DT.get(z.dtype)
@@ -107,7 +108,8 @@ def make_shape(b: DSparkBatch, grad_dtype: Optional[torch.dtype] = None) -> capi
     H = b.lm_head.shape[1] if (b.lm_head is not None and b.target_hidden is not None) else 0
     Hd = 0 if b.conf_hidden is None else b.conf_hidden.shape[-1]
     gd = _DT[grad_dtype] if grad_dtype is not None else dt
-    return capi.Shape(b.B, b.N, b.K, Vd, Vt, H, Hd, r, int(b.with_markov_conf and r > 0), dt, gd, 0)
+    return capi.Shape(b.B, b.N, b.K, Vd, Vt, H, Hd, r, int(b.with_markov_conf and r > 0), dt, gd,
+                      options)
 
 
 def _inputs(b: DSparkBatch) -> capi.InputsC:
@@ -118,8 +120,13 @@ def _inputs(b: DSparkBatch) -> capi.InputsC:
                         _ptr(b.conf_b))
 
 
-def dspark_workspace_size(b: DSparkBatch, grad_dtype: Optional[torch.dtype] = None) -> int:
-    sh = make_shape(b, grad_dtype)
+def _options(recompute_bias: bool) -> int:
+    return capi.OPT_RECOMPUTE_BIAS if recompute_bias else 0
+
+
+def dspark_workspace_size(b: DSparkBatch, grad_dtype: Optional[torch.dtype] = None,
+                          recompute_bias: bool = False) -> int:
+    sh = make_shape(b, grad_dtype, _options(recompute_bias))
     n = capi.lib().dspark_workspace_size(C.byref(sh))
     if n == 0:
         raise capi.DSparkError("invalid shape for dspark_workspace_size")
@@ -141,6 +148,7 @@ class FwdResult:
     flags: torch.Tensor          # [1] int32 (uint32 bits)
     workspace: torch.Tensor = field(repr=False)
     grad_dtype: Optional[torch.dtype] = None
+    options: int = 0
 
     def report(self) -> dict:
         return {k: self.pairs[i] for i, k in enumerate(REPORT_KEYS)}
@@ -148,10 +156,13 @@ class FwdResult:
 
 def dspark_loss_fwd(b: DSparkBatch, hp: HParams = HParams(), *, workspace=None,
                     grad_dtype: Optional[torch.dtype] = None, row_outputs: bool = True,
-                    stream=None) -> FwdResult:
-    """Forward of the DSpark loss (``dspark_loss_fwd`` of the C ABI)."""
+                    recompute_bias: bool = False, stream=None) -> FwdResult:
+    """Forward of the DSpark loss (``dspark_loss_fwd`` of the C ABI).
+
+    ``recompute_bias`` sets DSPARK_OPT_RECOMPUTE_BIAS (smaller workspace)."""
     dev = b.draft_logits.device
-    sh = make_shape(b, grad_dtype)
+    opts = _options(recompute_bias)
+    sh = make_shape(b, grad_dtype, opts)
     L = capi.lib()
     need = L.dspark_workspace_size(C.byref(sh))
     if workspace is None:
@@ -168,14 +179,14 @@ def dspark_loss_fwd(b: DSparkBatch, hp: HParams = HParams(), *, workspace=None,
     st = L.dspark_loss_fwd(C.byref(sh), C.byref(hpc), C.byref(inp), _ptr(workspace),
                            workspace.numel(), C.byref(out), _stream(stream))
     capi.check(st, "dspark_loss_fwd")
-    return FwdResult(loss, ntok, pairs, acc, rt, flags, workspace, grad_dtype)
+    return FwdResult(loss, ntok, pairs, acc, rt, flags, workspace, grad_dtype, opts)
 
 
 def dspark_loss_bwd(b: DSparkBatch, hp: HParams, fwd: FwdResult, grad_scale: float = 1.0, *,
                     conf_hidden_grad: bool = False, stream=None, out: Optional[dict] = None) -> dict:
     """Backward (``dspark_loss_bwd``): gradients of grad_scale * loss, overwritten."""
     dev = b.draft_logits.device
-    sh = make_shape(b, fwd.grad_dtype)
+    sh = make_shape(b, fwd.grad_dtype, fwd.options)
     gdt = fwd.grad_dtype or b.draft_logits.dtype
     f32 = torch.float32
     if out is None:

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(L):
 def _shape(**kw):
     d = dict(batch=2, num_blocks=3, block_size=7, draft_vocab=512, target_vocab=600, hidden=64,
              conf_hidden=32, markov_rank=16, with_markov_conf=1, dtype=1, grad_dtype=1,
-             reserved=0)
+             options=0)
     d.update(kw)
     return capi.Shape(**d)
 
@@ -46,9 +46,23 @@ def test_workspace_size(L):
     assert n >= 2 * R * V * 4            # fp32 teacher + corrected draft logits
     assert n % 256 == 0
     for bad in (dict(batch=0), dict(draft_vocab=1001), dict(markov_rank=12), dict(dtype=7),
-                dict(hidden=-8), dict(target_vocab=0)):
+                dict(hidden=-8), dict(target_vocab=0), dict(options=2), dict(options=-1)):
         assert L.dspark_workspace_size(C.byref(_shape(**bad))) == 0, bad
     assert L.dspark_workspace_size(None) == 0
+
+
+def test_recompute_bias_option_drops_the_corrected_logits_buffer(L):
+    """DSPARK_OPT_RECOMPUTE_BIAS: no fp32 [R, Vd] z' in the workspace where it applies
+    (bf16, supported rank, R and Vd multiples of 32); ignored for fp32 inputs."""
+    R, V = 2 * 16 * 7, 512
+    kw = dict(num_blocks=16, markov_rank=64)
+    base = L.dspark_workspace_size(C.byref(_shape(**kw)))
+    low = L.dspark_workspace_size(C.byref(_shape(options=capi.OPT_RECOMPUTE_BIAS, **kw)))
+    assert base > 0 and low > 0
+    assert base - low >= R * V * 4 - (2 * 8 + 4) * R - 3 * 256  # minus per-row partials
+    f32 = dict(kw, dtype=0, grad_dtype=0)
+    assert (L.dspark_workspace_size(C.byref(_shape(options=capi.OPT_RECOMPUTE_BIAS, **f32)))
+            == L.dspark_workspace_size(C.byref(_shape(**f32))))
 
 
 FAKE = 0x10000  # aligned host address; never dereferenced (validation fails first)

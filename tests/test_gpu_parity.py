@@ -27,9 +27,11 @@ DEV = "cuda:0"
 GS = 0.0125  # upstream gradient of the loss numerator
 
 
-def _full_parity(d, hp, tol, grad_tol=None, teacher="hidden", conf=True, grad_dtype=None):
+def _full_parity(d, hp, tol, grad_tol=None, teacher="hidden", conf=True, grad_dtype=None,
+                 recompute_bias=False):
     grad_tol = grad_tol or tol
-    b, f, g = run_gpu(d, hp, GS, teacher=teacher, conf=conf, grad_dtype=grad_dtype)
+    b, f, g = run_gpu(d, hp, GS, teacher=teacher, conf=conf, grad_dtype=grad_dtype,
+                      recompute_bias=recompute_bias)
     inp = oracle_inputs(d, teacher=teacher, conf=conf)
     fw = oracle.forward(inp, ohp(hp))
     compare_forward(f, fw, tol)
@@ -52,19 +54,39 @@ def test_tiny_fp32_full_parity():
     _full_parity(d, HParams(), TOL["f32"])
 
 
-def test_small_bf16_full_parity():
+@pytest.mark.parametrize("recompute", [False, True], ids=["stored", "recompute"])
+def test_small_bf16_full_parity(recompute):
     wl = get_workload(1)
-    say(f"[parity] {wl.name}")
+    say(f"[parity] {wl.name} recompute_bias={recompute}")
     d = make_inputs(wl, DEV)
-    _full_parity(d, HParams(), TOL["bf16"])
+    _full_parity(d, HParams(), TOL["bf16"], recompute_bias=recompute)
 
 
-def test_small_bf16_fp32_grads():
+@pytest.mark.parametrize("recompute", [False, True], ids=["stored", "recompute"])
+def test_small_bf16_fp32_grads(recompute):
     wl = get_workload(1)
-    say(f"[parity] {wl.name} fp32 grads")
+    say(f"[parity] {wl.name} fp32 grads recompute_bias={recompute}")
     d = make_inputs(wl, DEV)
     _full_parity(d, HParams(ce_alpha=0.3, l1_alpha=0.7, confidence_alpha=0.5),
-                 TOL["bf16"], grad_tol=TOL["bf16"], grad_dtype=torch.float32)
+                 TOL["bf16"], grad_tol=TOL["bf16"], grad_dtype=torch.float32,
+                 recompute_bias=recompute)
+
+
+def test_recompute_bias_matches_stored_path():
+    """The two draft-logit paths agree with each other (beyond both meeting the oracle):
+    same token count, loss within bf16 tolerance, identical flags."""
+    wl = get_workload(1)
+    say(f"[parity] {wl.name} stored vs recompute")
+    d = make_inputs(wl, DEV)
+    hp = HParams()
+    _, f0, g0 = run_gpu(d, hp, GS)
+    _, f1, g1 = run_gpu(d, hp, GS, recompute_bias=True)
+    assert f1.workspace.numel() < f0.workspace.numel()
+    assert int(f0.num_tokens.item()) == int(f1.num_tokens.item())
+    assert int(f0.flags.item()) == int(f1.flags.item()) == 0
+    assert_scalar("loss", f1.loss.item(), f0.loss.item(), 1e-4)
+    assert_norm("row terms", to_np(f1.row_terms), to_np(f0.row_terms), 1e-4)
+    assert_norm("dz", to_np(g1["d_draft_logits"]), to_np(g0["d_draft_logits"]), TOL["bf16"])
 
 
 def _ragged(dtype="f32", V=1000, r=24, H=40, B=1, N=5, seed=11, Vt=None):
@@ -195,11 +217,12 @@ def _edge_checks(d, f, wl):
     assert np.all(rt[inval] == 0.0) and np.all(acc[inval] == 1.0)
 
 
-def test_edge_distributions_full_parity():
+@pytest.mark.parametrize("recompute", [False, True], ids=["stored", "recompute"])
+def test_edge_distributions_full_parity(recompute):
     wl = get_workload(4)
-    say(f"[parity] {wl.name}")
+    say(f"[parity] {wl.name} recompute_bias={recompute}")
     d = make_inputs(wl, DEV)
-    f, g, fw, gr = _full_parity(d, HParams(), TOL["bf16"])
+    f, g, fw, gr = _full_parity(d, HParams(), TOL["bf16"], recompute_bias=recompute)
     _edge_checks(d, f, wl)
     assert int(f.flags.item()) == 0
 
@@ -209,14 +232,14 @@ def _sampled_blocks(wl, count, seed):
     return np.sort(rng.choice(wl.B * wl.N, size=count, replace=False))
 
 
-@pytest.mark.parametrize("idx,count", [(2, 24), (3, 24)])
-def test_full_size_sampled_rows(idx, count):
+@pytest.mark.parametrize("idx,count,recompute", [(2, 24, False), (3, 24, False), (3, 16, True)])
+def test_full_size_sampled_rows(idx, count, recompute):
     """Full-size launch; sampled whole blocks checked against the oracle row by row."""
     wl = get_workload(idx)
-    say(f"[parity] {wl.name} full size, {count} sampled blocks")
+    say(f"[parity] {wl.name} full size, {count} sampled blocks, recompute_bias={recompute}")
     d = make_inputs(wl, DEV)
     hp = HParams()
-    b, f, g = run_gpu(d, hp, GS)
+    b, f, g = run_gpu(d, hp, GS, recompute_bias=recompute)
     blocks = _sampled_blocks(wl, count, 100 + idx)
     sub = subset_blocks(d, blocks)
     inp = oracle_inputs(sub)
