@@ -42,13 +42,15 @@ def _gpu_leg(args):
           flush=True)
     b = DSparkBatch.from_workload(d)
     hp = HParams()
-    ws = torch.empty(dspark_workspace_size(b), dtype=torch.uint8, device=dev)
+    sd = args.store_draft_logits
+    ws = torch.empty(dspark_workspace_size(b, store_draft_logits=sd), dtype=torch.uint8,
+                     device=dev)
     gs = 1.0 / wl.R
-    fwd = dspark_loss_fwd(b, hp, workspace=ws)
+    fwd = dspark_loss_fwd(b, hp, workspace=ws, store_draft_logits=sd)
     grads = dspark_loss_bwd(b, hp, fwd, gs)
 
     def step():
-        f = dspark_loss_fwd(b, hp, workspace=ws)
+        f = dspark_loss_fwd(b, hp, workspace=ws, store_draft_logits=sd)
         dspark_loss_bwd(b, hp, f, gs, out=grads)
         return f
 
@@ -151,6 +153,9 @@ def main():
     ap.add_argument("--workload", default="large-batch-r14336-v151936")
     ap.add_argument("--cpu-blocks", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--store-draft-logits", action="store_true",
+                    help="DSPARK_OPT_STORE_DRAFT_LOGITS: materialise the fp32 corrected draft "
+                         "logits instead of recomputing the Markov bias in each sweep")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (rocprofv3 byte-counter calibration)")
     args = ap.parse_args()
@@ -168,19 +173,31 @@ def main():
     ms_step = 1000.0 * elapsed / args.steps
     rows_per_s = R * args.steps / elapsed
 
+    stored = args.store_draft_logits
     gemm_ms = _avg_ms(stages, "logits_gemm", args.steps)
-    gemm_flops = 2.0 * R * V * (H + r)   # teacher projection (K = H) + Markov bias (K = r)
+    if stored:  # teacher projection (K = H) + the materialised Markov bias (K = r)
+        gemm_flops = 2.0 * R * V * (H + r)
+        kname = "logits_gemm (lm_head projection + Markov-corrected draft logits, bf16 MFMA)"
+    else:       # the teacher projection alone: the bias is recomputed in the sweeps
+        gemm_flops = 2.0 * R * V * H
+        kname = "logits_gemm (lm_head projection, bf16 MFMA, tile statistics epilogue)"
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma",
-                "kernel": "logits_gemm (lm_head projection + Markov-corrected draft logits, bf16 MFMA)",
+    roofline = {"bound": "mfma", "kernel": kname,
                 "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": _traffic("logits_gemm"),
+                "traffic": None if stored else _traffic("logits_gemm"),
                 "flops_per_launch": gemm_flops, "avg_ms": round(gemm_ms, 4)}
 
-    # row sweeps: algorithmic bytes per launch / average duration
+    # vocabulary sweeps: algorithmic HBM bytes per (row, column) / average
+    # duration.  Stored path: z' and T fp32 in, dz bf16 + G lo bf16 out.
+    # Recompute path: z bf16 instead of z' (the bias comes from W2 in L2 and E
+    # in registers, not counted), statistics read z alone.
+    if stored:
+        per_elem = (("l1_sweep", 8), ("grad_sweep", 12))
+    else:
+        per_elem = (("bias_stats", 2), ("l1_sweep", 6), ("grad_sweep", 10))
     sweeps = {}
-    for name, bytes_per_elem in (("l1_sweep", 8), ("grad_sweep", 16)):
+    for name, bytes_per_elem in per_elem:
         ms = _avg_ms(stages, name, args.steps)
         if ms:
             gbs = bytes_per_elem * R * V / (ms * 1e-3) / 1e9
@@ -202,7 +219,9 @@ def main():
         "config": {"workload": wl.name, "rows": R, "batch": wl.B, "num_blocks": wl.N,
                    "block_size": wl.K, "draft_vocab": V, "target_vocab": wl.Vt, "hidden": H,
                    "markov_rank": r, "confidence_head": "with_markov", "gamma": wl.gamma,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "corrected_draft_logits": ("stored fp32" if args.store_draft_logits
+                                              else "recomputed per sweep")},
         "roofline": roofline,
         "sweeps": sweeps,
         "stage_ms": stage_ms,

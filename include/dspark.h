@@ -69,13 +69,17 @@ enum {
 /* Bits of dspark_shape.options; an unknown bit makes the shape invalid
  * (DSPARK_ERR_SHAPE, workspace size 0). */
 enum {
-  /* Do not store the fp32 Markov-corrected draft logits z + W2 W1[prev]: each
-   * vocabulary sweep (softmax statistics, L1, gradient) recomputes the rank-r
-   * bias from W2 and the gathered W1 rows on bf16 MFMA.  The workspace shrinks
-   * by 4 R Vd bytes, for a few per cent more time.  Applies to bf16 inputs with
-   * markov_rank in {32, 64, 128, 256} and R, Vd multiples of 32; ignored
-   * elsewhere.  (Without a Markov head the sweeps always read z directly.) */
-  DSPARK_OPT_RECOMPUTE_BIAS = 1u
+  /* By default, for bf16 inputs with markov_rank in {32, 64, 128, 256}, R and
+   * Vd multiples of 32 and Vd < 2^24, the fp32 Markov-corrected draft logits
+   * z + W2 W1[prev] are never stored: each vocabulary sweep (softmax
+   * statistics, L1, gradient) recomputes the rank-r bias from W2 and the
+   * gathered W1 rows on bf16 MFMA.  This bit instead materialises them once
+   * (a GEMM epilogue) in the workspace, 4 R Vd bytes more, and sweeps the
+   * stored values: slower on MI355X at the shapes measured, kept for
+   * comparison.  Ignored where the default does not apply (fp32 inputs, other
+   * ranks: the logits are always stored there) and without a Markov head
+   * (the sweeps read z directly). */
+  DSPARK_OPT_STORE_DRAFT_LOGITS = 1u
 };
 
 /* Bits of the device word dspark_fwd_out.flags (OR-ed, never cleared by bwd). */
@@ -146,8 +150,9 @@ typedef struct {
 } dspark_bwd_out;
 
 /* Bytes of device workspace fwd + bwd need for `shape` (0 on an invalid shape).
- * It holds the fp32 teacher logits, the fp32 Markov-corrected draft logits,
- * per-tile softmax statistics, per-row state and the backward scratch. */
+ * It holds the fp32 teacher logits, the fp32 Markov-corrected draft logits
+ * where they are stored (see DSPARK_OPT_STORE_DRAFT_LOGITS), per-tile softmax
+ * statistics, per-row state and the backward scratch. */
 size_t dspark_workspace_size(const dspark_shape *shape);
 
 /* Forward: loss numerator, token count, report pairs, optional per-row terms.

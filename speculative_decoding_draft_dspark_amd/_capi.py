@@ -17,7 +17,7 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_NO_TARGET",
           -5: "ERR_WORKSPACE", -6: "ERR_ALIGN", -7: "ERR_HIP"}
 FLAG_TARGET_ID_RANGE, FLAG_PREV_ID_RANGE, FLAG_NONFINITE, FLAG_NO_TEACHER = 1, 2, 4, 8
-OPT_RECOMPUTE_BIAS = 1
+OPT_STORE_DRAFT_LOGITS = 1
 
 
 class Shape(C.Structure):

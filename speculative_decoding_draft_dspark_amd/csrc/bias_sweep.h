@@ -11,33 +11,36 @@
 
 namespace dspark {
 
-// Ranks the bias sweeps handle (0 = no Markov head: z' = z).
-bool bias_sweep_rank_ok(int64_t rank);
+// Shapes the bias sweeps handle: vocabulary V (a multiple of 8, below 2^24)
+// and rank in {0, 32, 64, 128, 256} (0 = no Markov head: z' = z).
+bool bias_sweep_ok(int64_t V, int64_t rank);
 
-// Row tiles of 128 rows x vocabulary splits of `vsplit` columns (a multiple of
-// 256) each sweep launches.
+// Row tiles of 256 rows x vocabulary splits of `vsplit` columns (a multiple of
+// 64) each sweep launches.
 struct BiasGrid {
   int64_t row_tiles, splits, vsplit;
 };
 BiasGrid bias_grid(int64_t R, int64_t V);
 
-// Per (row, 256-column tile) maximum and fixed-point exp-sum of z' into sz
+// Per (row, 64-column tile) maximum and fixed-point exp-sum of z' into sz
 // [R, nstat], computed exactly as the logits GEMM epilogue computes them for T.
 // z [R, V] bf16, E [R, rank] bf16 (zero rows on unsupervised slots), W2 [V, rank] bf16.
 hipError_t launch_bias_stats(int64_t R, int64_t V, int64_t rank, const bf16_t* z, const bf16_t* E,
                              const bf16_t* W2, float2* sz, int64_t nstat, hipStream_t s);
 
 // On supervised rows, per vocabulary split: sum |p - q| and sum p sign(p - q)
-// (fp64 partials [splits, R] each; 0 without a teacher, T == nullptr), and
-// z'_y of the target column (zy [R]), with p = exp(z' - lse_z), q = exp(T - lse_t).
+// (fp64 partials [splits, R] each), with p = exp(z' - lse_z), q = exp(T - lse_t).
+// Without a teacher (T == nullptr) there is nothing to sweep: no launch.
 hipError_t launch_bias_l1(int64_t R, int64_t V, int64_t rank, const bf16_t* z, const bf16_t* E,
                           const bf16_t* W2, const float* T, const int32_t* tid, RowState rs,
-                          double* part_l1, double* part_s, float* zy, hipStream_t s);
+                          double* part_l1, double* part_s, hipStream_t s);
 
-// Per row: L1, S and CE from the split partials and z'_y (masked rows: 0).
-hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int splits, const double* part_l1,
-                                 const double* part_s, const float* zy, RowState rs,
-                                 hipStream_t s);
+// Per row: L1 and S from the split partials (0 without a teacher) and
+// CE = lse_z - z'_y with z'_y = z_y + E_row . W2_y (masked rows: 0).
+hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int64_t rank, int splits, int has_teacher,
+                                 const double* part_l1, const double* part_s, const bf16_t* z,
+                                 const bf16_t* E, const bf16_t* W2, const int32_t* tid,
+                                 RowState rs, hipStream_t s);
 
 // G = g w [ce_a (p - [v = y]) + l1_a p (sign(p - q) - S)] (0 on unsupervised rows):
 // dz in the gradient dtype (grad_dtype 1 = bf16: dz is the bf16 high part),

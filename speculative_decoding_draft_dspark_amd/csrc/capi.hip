@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/dspark.h"
+#include "common.h"
 #include "internal.h"
 #include "bias_sweep.h"
 #include "rowwise.h"
@@ -39,7 +40,7 @@ struct Dims {
 
 struct Layout {
   size_t Zp, T, sz, st, E, mask, rowf, ghi, glo, g32, dEpart, dE, confpart;
-  size_t pl1, ps, zy;  // bias path: L1 / S split partials, z'_y
+  size_t pl1, ps;  // bias path: L1 / S split partials
   size_t w2t, eblk, blkhi, blklo, dw2part;  // bf16 backward operands
   size_t total;
 };
@@ -56,7 +57,7 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   if (sh->markov_rank < 0 || sh->markov_rank % 8) return DSPARK_ERR_SHAPE;
   if (sh->hidden < 0 || sh->hidden % 8) return DSPARK_ERR_SHAPE;
   if (sh->conf_hidden < 0) return DSPARK_ERR_SHAPE;
-  if (sh->options & ~static_cast<int32_t>(DSPARK_OPT_RECOMPUTE_BIAS)) return DSPARK_ERR_SHAPE;
+  if (sh->options & ~static_cast<int32_t>(DSPARK_OPT_STORE_DRAFT_LOGITS)) return DSPARK_ERR_SHAPE;
   if (sh->markov_rank > 0 && sh->target_vocab <= 0) return DSPARK_ERR_SHAPE;
   if (sh->draft_vocab > (int64_t{1} << 26) || sh->hidden > (int64_t{1} << 20) ||
       sh->markov_rank > 4096)
@@ -71,7 +72,7 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   d->markov = d->r > 0;
   d->conf = d->Hd > 0;
   d->conf_markov = d->conf && d->markov && sh->with_markov_conf != 0;
-  d->nstat = (d->Vd + 255) / 256;
+  d->nstat = (d->Vd + kStatTile - 1) / kStatTile;
   const int64_t nM = (d->R + 255) / 256;
   int64_t sp = 640 / nM;
   const int64_t kmax = 2 * gemm_kpad(d->Vd, d->esize) / (8 * 64);  // at least 8 K-tiles per split
@@ -101,11 +102,12 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   }
   d->splits = d->markov ? sp : 0;
   // Sweeps that rebuild z' from z instead of reading a stored fp32 z': always
-  // without a Markov head (z' = z), on request with one (slower: the bias is
-  // recomputed in each of the three sweeps, but the R x Vd fp32 buffer goes).
-  d->bias_path = d->dtype == DSPARK_BF16 && bias_sweep_rank_ok(d->r) &&
+  // without a Markov head (z' = z); with one unless the caller asks for the
+  // stored logits (the bias is recomputed in each of the three sweeps, which
+  // measures faster than writing and twice reading the R x Vd fp32 buffer).
+  d->bias_path = d->dtype == DSPARK_BF16 && bias_sweep_ok(d->Vd, d->r) &&
                  (!d->markov ||
-                  (d->direct_bwd && (sh->options & DSPARK_OPT_RECOMPUTE_BIAS) != 0));
+                  (d->direct_bwd && (sh->options & DSPARK_OPT_STORE_DRAFT_LOGITS) == 0));
   d->bsplits = d->bias_path ? bias_grid(d->R, d->Vd).splits : 0;
   d->conf_chunks = d->R < 256 ? static_cast<int>(d->R) : 256;
   d->F = d->Hd + (d->conf_markov ? d->r : 0);
@@ -119,11 +121,10 @@ Layout make_layout(const Dims& d) {
   const size_t RV = static_cast<size_t>(d.R) * d.Vd;
   L.Zp = o;
   if (!d.bias_path) o = up(o + RV * 4);
-  L.pl1 = L.ps = L.zy = o;
+  L.pl1 = L.ps = o;
   if (d.bias_path) {
     L.pl1 = o; o = up(o + static_cast<size_t>(d.bsplits) * d.R * 8);
     L.ps = o; o = up(o + static_cast<size_t>(d.bsplits) * d.R * 8);
-    L.zy = o; o = up(o + static_cast<size_t>(d.R) * 4);
   }
   L.T = o; o = up(o + RV * 4);
   L.sz = o; o = up(o + static_cast<size_t>(d.R) * d.nstat * 8);
@@ -338,13 +339,13 @@ int dspark_loss_fwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     const bf16_t* W2 = d.markov ? static_cast<const bf16_t*>(in->markov_w2) : nullptr;
     double* pl1 = reinterpret_cast<double*>(ws + L.pl1);
     double* ps = reinterpret_cast<double*>(ws + L.ps);
-    float* zy = reinterpret_cast<float*>(ws + L.zy);
     DSPARK_STAGE(kBiasStats, launch_bias_stats(d.R, d.Vd, d.r, z, Eb, W2, sz, d.nstat, s));
     DSPARK_STAGE(kL1Sweep, launch_lse_rows(d.R, sz, stt, d.nstat, rs.mask, teacher != kNone, rs, s));
     DSPARK_STAGE(kL1Sweep, launch_bias_l1(d.R, d.Vd, d.r, z, Eb, W2, teacher != kNone ? T : nullptr,
-                                          in->target_ids, rs, pl1, ps, zy, s));
-    DSPARK_STAGE(kL1Sweep, launch_bias_l1_finish(d.R, d.Vd, static_cast<int>(d.bsplits), pl1, ps,
-                                                 zy, rs, s));
+                                          in->target_ids, rs, pl1, ps, s));
+    DSPARK_STAGE(kL1Sweep, launch_bias_l1_finish(d.R, d.Vd, d.r, static_cast<int>(d.bsplits),
+                                                 teacher != kNone, pl1, ps, z, Eb, W2,
+                                                 in->target_ids, rs, s));
   } else {
   // Corrected draft logits z' = z + E W2^T and teacher logits T (both fp32),
   // each with per-tile softmax statistics, over the same [R, Vd] tile grid.

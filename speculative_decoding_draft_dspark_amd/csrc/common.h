@@ -11,7 +11,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 
 constexpr int kWave = 64;
-constexpr int kStatTile = 256;  // vocab columns per softmax-statistics tile
+constexpr int kStatTile = 64;   // vocab columns per softmax-statistics tile
+constexpr int kGemmTileN = 256;  // output columns of a logits GEMM tile (4 statistics tiles)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFixScale = 2147483648.0f;  // 2^31: fixed-point scale of tile exp-sums
 
@@ -61,6 +62,14 @@ template <> struct Elem<bf16_t> {
 __device__ __forceinline__ float dexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
 __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
+// sign(d) for a difference of two probabilities, as clamp(d 2^126, -1, 1):
+// one multiply and one median, no compare masks.  Exact for d = 0 and for
+// |d| >= 2^-126; a smaller nonzero d needs both probabilities below about
+// 2^-102 (fp32 spacing), where the fraction it returns multiplies a p that
+// small.
+__device__ __forceinline__ float sgn_prob(float d) {
+  return __builtin_amdgcn_fmed3f(d * 0x1p126f, -1.f, 1.f);
+}
 
 // exp(x - m) for x <= m in the fixed point (2^31 scale) of the tile
 // exp-sums, as 2^(x log2 e + 31 - m log2 e) truncated to an integer (one fma,

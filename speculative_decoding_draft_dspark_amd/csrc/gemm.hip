@@ -29,6 +29,7 @@
 namespace dspark {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <typename T> struct Mfma;
@@ -214,39 +215,47 @@ __device__ __forceinline__ void row_epilogue(const AccT& acc, int wr, int wc, fl
         v[i].x += x.x; v[i].y += x.y; v[i].z += x.z; v[i].w += x.w;
       }
       if (q + 1 < BM / kChunkRows) load_x(q + 1);
-      float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < kVecs; ++i) {
         const int64_t col = n0 + sub * 4 + 32 * i;
-        if (col < N) {  // N % 4 == 0: the 4 columns are all in or all out
-          if (rowok) *reinterpret_cast<float4*>(C + row * ep.ldc + col) = v[i];
-          mx = fmaxf(mx, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
-        }
+        if (col < N && rowok) *reinterpret_cast<float4*>(C + row * ep.ldc + col) = v[i];
       }
+      // statistics per 64-column tile: lane sub holds columns 4 sub + 32 i,
+      // so tile s (i = 2 s, 2 s + 1) spans the row's 8 lanes
 #pragma unroll
-      for (int o = 1; o < kLanesPerRow; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-      // fixed-point sum of exp(x - max): exact integer adds, so the result does
-      // not depend on the order in which the columns are visited
-      uint64_t sum = 0;
-      if (mx != -INFINITY) {
+      for (int st = 0; st < BN / kStatTile; ++st) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < kVecs; ++i) {
+        for (int i = 2 * st; i < 2 * st + 2; ++i) {
           const int64_t col = n0 + sub * 4 + 32 * i;
-          if (col < N) {
-            sum += fix_exp(v[i].x, mx) + fix_exp(v[i].y, mx) + fix_exp(v[i].z, mx) +
-                   fix_exp(v[i].w, mx);
+          if (col < N)  // N % 4 == 0: the 4 columns are all in or all out
+            mx = fmaxf(mx, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
+        }
+#pragma unroll
+        for (int o = 1; o < kLanesPerRow; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        // fixed-point sum of exp(x - max): exact integer adds, so the result
+        // does not depend on the order in which the columns are visited
+        uint64_t sum = 0;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int i = 2 * st; i < 2 * st + 2; ++i) {
+            const int64_t col = n0 + sub * 4 + 32 * i;
+            if (col < N) {
+              sum += fix_exp(v[i].x, mx) + fix_exp(v[i].y, mx) + fix_exp(v[i].z, mx) +
+                     fix_exp(v[i].w, mx);
+            }
           }
         }
-      }
 #pragma unroll
-      for (int o = 1; o < kLanesPerRow; o <<= 1) {
-        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(sum), o, kWave);
-        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(sum >> 32), o, kWave);
-        sum += (static_cast<uint64_t>(hi) << 32) | lo;
-      }
-      if (sub == 0 && rowok) {
-        const float l = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
-        ep.stats[row * ep.nstat + tn] = make_float2(mx, l);
+        for (int o = 1; o < kLanesPerRow; o <<= 1) {
+          const uint32_t lo = __shfl_xor(static_cast<uint32_t>(sum), o, kWave);
+          const uint32_t hi = __shfl_xor(static_cast<uint32_t>(sum >> 32), o, kWave);
+          sum += (static_cast<uint64_t>(hi) << 32) | lo;
+        }
+        if (sub == 0 && rowok && n0 + kStatTile * st < N) {
+          const float l = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
+          ep.stats[row * ep.nstat + tn * (BN / kStatTile) + st] = make_float2(mx, l);
+        }
       }
     } else if (rowok) {
 #pragma unroll
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(int64_t M, int64_t
   constexpr int A_CH = BM * 8, B_CH = BN * 8;
   constexpr int A_PER = A_CH / NT, B_PER = B_CH / NT;
   static_assert(A_CH % NT == 0 && B_CH % NT == 0, "tile / thread mismatch");
-  static_assert(EPI != EPI_STATS || BN == kStatTile, "stats epilogue needs BN == stat tile");
+  static_assert(EPI != EPI_STATS || BN == kGemmTileN, "stats epilogue needs BN == 256");
 
   __shared__ u32x4 lds[2 * (A_CH + B_CH)];
   const TileCoord tc = tile_coord(M, N, BM, BN, group_m);
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int
                                                                   int64_t kper, GemmJob j0,
                                                                   GemmJob j1, int njobs,
                                                                   int group_m) {
-  static_assert(EPI != EPI_STATS || BN == kStatTile, "stats epilogue needs BN == stat tile");
+  static_assert(EPI != EPI_STATS || BN == kGemmTileN, "stats epilogue needs BN == 256");
   __shared__ u32x4 lds[4 * (BM * 4 + BN * 4)];
   const TileCoord tc = tile_coord(M, N, BM, BN, group_m);
   dma_job<BM, BN, WM, WN, EPI, AL, BL>(j0, M, N, kper, tc, lds);
@@ -930,77 +939,133 @@ __device__ __forceinline__ uint64_t row16_sum(uint64_t v) {
 }
 
 
-__device__ __forceinline__ void w4_epilogue(const f32x16_v (&acc)[4][4], int64_t M, int64_t N,
-                                            int64_t m0, int64_t n0, int64_t tn,
-                                            const EpiParams& ep, float4* ea, float4* eb) {
+// Rows of the row phase: wave w handles rows wrow(w, i) + 4 p + (lane >> 4),
+// p = 0..3, of 32-row block i; every global access goes through a buffer
+// resource based at the first of those rows, so offsets stay below 2^30 for
+// any leading dimension below 2^26, and out-of-range lanes get an offset past
+// the resource (loads read zero, stores are dropped) instead of a branch:
+// with no branches the compiler's wait counts are exact and the addends of
+// the next block stay in flight while this block is processed.
+__device__ __forceinline__ int64_t w4_erow(int64_t m0, int i, int p) {
+  // wave-uniform (scalar) so the buffer resources built from it are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return m0 + (wave >> 1) * 128 + 32 * i + 16 * (wave & 1) + 4 * p;
+}
+
+// Queue the bf16 addends of block i: lane (row, sub) reads columns
+// 4 sub + 64 t .. + 3 of its row, t = 0..3.
+__device__ __forceinline__ void w4_x_issue(uint2 (&xv)[4][4], const EpiParams& ep, int64_t M,
+                                           int64_t N, int64_t m0, int64_t n0, int i) {
+  const int lane = threadIdx.x & 63, sub = lane & 15, rl = lane >> 4;
+  const bf16_t* X = static_cast<const bf16_t*>(ep.X);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int64_t r0 = w4_erow(m0, i, p);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + r0 * ep.ldx + n0);
+    const bool rok = r0 + rl < M;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = 4 * sub + 64 * t;
+      const uint32_t off = (rok && n0 + c < N)
+                               ? static_cast<uint32_t>((rl * ep.ldx + c) * 2)
+                               : kOutOfRange;
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
+      xv[p][t] = make_uint2(v.x, v.y);
+    }
+  }
+}
+
+// Block i of the epilogue: stage the accumulators of the block's rows, then
+// 16 lanes per row add the addends, store the row's 256 columns and reduce
+// the row's maximum and fixed-point exp-sum.
+template <bool HAS_X>
+__device__ __forceinline__ void w4_eblock(const f32x16_v (&acc)[4][4], int i,
+                                          const uint2 (&xv)[4][4], int64_t M, int64_t N,
+                                          int64_t m0, int64_t n0, int64_t tn, const EpiParams& ep,
+                                          float4* ea, float4* eb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r = lane & 31;
-  const int sub = lane & 15;                   // 16 lanes per row in the row phase
-  const int chunk = wave >> 1;                 // row phase: wave-row half this wave reads
-  const int rbase = 16 * (wave & 1) + (lane >> 4);  // + 4 p: row within the 32-row block
-  const bf16_t* X = static_cast<const bf16_t*>(ep.X);
+  const int sub = lane & 15, rl = lane >> 4;
+  const int rbase = 16 * (wave & 1) + rl;  // + 4 p: row within the 32-row block
   float4* mine = wm == 0 ? ea : eb;
-  const float4* src = chunk == 0 ? ea : eb;
+  const float4* src = (wave >> 1) == 0 ? ea : eb;
+  lds_barrier();  // the stages are free (main-loop reads or the previous block's reads done)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {  // unrolled: acc[.][i] must stay in registers
-    // addends of this block's rows, issued before the barrier so they are in
-    // flight while the accumulators are staged
-    uint2 xv[4][4];
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int64_t row = m0 + chunk * 128 + 32 * i + rbase + 4 * p;
+    for (int q = 0; q < 4; ++q)
+      mine[w4_eslot(r, wn * 32 + 8 * j + 2 * q + h)] =
+          make_float4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                      acc[j][i][4 * q + 3]);
+  lds_barrier();
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t col = n0 + 4 * sub + 64 * t;
-        xv[p][t] = (X && row < M && col < N)
-                       ? *reinterpret_cast<const uint2*>(X + row * ep.ldx + col)
-                       : uint2{0u, 0u};
-      }
-    }
-    lds_barrier();  // the stages are free (main-loop reads or the previous block's reads done)
+  for (int p = 0; p < 4; ++p) {
+    const int64_t r0 = w4_erow(m0, i, p);
+    const bool rok = r0 + rl < M;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(ep.C + r0 * ep.ldc + n0);
+    float4 v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        mine[w4_eslot(r, wn * 32 + 8 * j + 2 * q + h)] =
-            make_float4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
-                        acc[j][i][4 * q + 3]);
-    lds_barrier();
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int rr = rbase + 4 * p;
-      const int64_t row = m0 + chunk * 128 + 32 * i + rr;
-      float4 v[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[t] = src[w4_eslot(rr, sub + 16 * t)];
+    for (int t = 0; t < 4; ++t) {
+      v[t] = src[w4_eslot(rbase + 4 * p, sub + 16 * t)];
+      if (HAS_X) {
         v[t].x += __uint_as_float(xv[p][t].x << 16);
         v[t].y += __uint_as_float(xv[p][t].x & 0xffff0000u);
         v[t].z += __uint_as_float(xv[p][t].y << 16);
         v[t].w += __uint_as_float(xv[p][t].y & 0xffff0000u);
-        const int64_t col = n0 + 4 * sub + 64 * t;
-        if (col < N) {  // N % 4 == 0: the lane's 4 columns are all in or all out
-          if (row < M) *reinterpret_cast<float4*>(ep.C + row * ep.ldc + col) = v[t];
-          mx = fmaxf(mx, fmaxf(fmaxf(v[t].x, v[t].y), fmaxf(v[t].z, v[t].w)));
-        }
       }
-      mx = row16_max(mx);
-      uint64_t sum = 0;
-      if (mx != -INFINITY) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (n0 + 4 * sub + 64 * t < N)
-            sum += fix_exp(v[t].x, mx) + fix_exp(v[t].y, mx) + fix_exp(v[t].z, mx) +
-                   fix_exp(v[t].w, mx);
-      }
-      sum = row16_sum(sum);
-      if (sub == 0 && row < M) {
-        const float l = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
-        ep.stats[row * ep.nstat + tn] = make_float2(mx, l);
-      }
+      const int c = 4 * sub + 64 * t;
+      const bool cok = n0 + c < N;  // N % 4 == 0: the lane's 4 columns are all in or all out
+      const u32x4 w = {__float_as_uint(v[t].x), __float_as_uint(v[t].y), __float_as_uint(v[t].z),
+                       __float_as_uint(v[t].w)};
+      __builtin_amdgcn_raw_buffer_store_b128(
+          w, rc, (rok && cok) ? static_cast<uint32_t>((rl * ep.ldc + c) * 4) : kOutOfRange, 0, 0);
     }
+    // statistics of the 4 tiles of 64 columns (tile t = the lanes' t-th
+    // vector): maximum and fixed-point exp-sum over the row's 16 lanes; the
+    // columns past N contribute nothing, and a tile with no column in range
+    // (mx = -inf) is not stored
+    float mx[4], lt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float m4 = fmaxf(fmaxf(v[t].x, v[t].y), fmaxf(v[t].z, v[t].w));
+      mx[t] = row16_max(n0 + 4 * sub + 64 * t < N ? m4 : -INFINITY);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float off = fix_exp_offset(mx[t]);
+      uint64_t t4 = static_cast<uint64_t>(fix_exp32o(v[t].x, off)) + fix_exp32o(v[t].y, off) +
+                    (static_cast<uint64_t>(fix_exp32o(v[t].z, off)) + fix_exp32o(v[t].w, off));
+      t4 = (n0 + 4 * sub + 64 * t < N) ? t4 : 0ull;
+      const uint64_t sum = row16_sum(t4);
+      lt[t] = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
+    }
+    // lane sub < 4 stores tile sub
+    const float ms = sub == 0 ? mx[0] : (sub == 1 ? mx[1] : (sub == 2 ? mx[2] : mx[3]));
+    const float ls = sub == 0 ? lt[0] : (sub == 1 ? lt[1] : (sub == 2 ? lt[2] : lt[3]));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ep.stats + r0 * ep.nstat + 4 * tn);
+    const u32x2 sv = {__float_as_uint(ms), __float_as_uint(ls)};
+    const bool sok = sub < 4 && rok && n0 + kStatTile * sub < N;
+    __builtin_amdgcn_raw_buffer_store_b64(
+        sv, rs, sok ? static_cast<uint32_t>((rl * ep.nstat + sub) * 8) : kOutOfRange, 0, 0);
   }
+}
+
+template <bool HAS_X>
+__device__ __forceinline__ void w4_epilogue(const f32x16_v (&acc)[4][4], int64_t M, int64_t N,
+                                            int64_t m0, int64_t n0, int64_t tn,
+                                            const EpiParams& ep, float4* ea, float4* eb) {
+  // two named addend buffers, one block ahead (loop unrolled: static names)
+  uint2 xa[4][4], xb[4][4];
+  if (HAS_X) {
+    w4_x_issue(xa, ep, M, N, m0, n0, 0);
+    w4_x_issue(xb, ep, M, N, m0, n0, 1);
+  }
+  w4_eblock<HAS_X>(acc, 0, xa, M, N, m0, n0, tn, ep, ea, eb);
+  if (HAS_X) w4_x_issue(xa, ep, M, N, m0, n0, 2);
+  w4_eblock<HAS_X>(acc, 1, xb, M, N, m0, n0, tn, ep, ea, eb);
+  if (HAS_X) w4_x_issue(xb, ep, M, N, m0, n0, 3);
+  w4_eblock<HAS_X>(acc, 2, xa, M, N, m0, n0, tn, ep, ea, eb);
+  w4_eblock<HAS_X>(acc, 3, xb, M, N, m0, n0, tn, ep, ea, eb);
 }
 
 // One logits job over the 256 x 256 output tile grid.  Persistent: one
@@ -1050,7 +1115,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(int64_t M, int64_t N, G
     const TileCoord tnext = tile_coord_of(more ? vn : v, M, N, 256, 256, group_m);
     lds_barrier();  // every wave has read its last fragments of this tile
     if (more) w4_queue(J, tnext, M, N, o, ring);
-    w4_epilogue(acc, M, N, tc.m0, tc.n0, tc.tn, J.ep, ea, eb);
+    w4_epilogue<TAG == 0>(acc, M, N, tc.m0, tc.n0, tc.tn, J.ep, ea, eb);
     if (!more) break;
     lds_barrier();  // stage 2 is read for the last time
     w4_queue_third(J, tnext, o, ring);
@@ -1191,8 +1256,7 @@ hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const 
         return launch_dma<EPI_PARTIAL, LAYOUT_KB, LAYOUT_KB, 3>(M, N, j, j, 1, splits, s);
     } else {
       if (epi == EPI_STATS)
-        return tag == 1 ? launch_w4<1>(M, N, j, s)
-                        : launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, j, j, 1, 1, s);
+        return tag == 1 ? launch_w4<1>(M, N, j, s) : launch_w4<0>(M, N, j, s);
       if (epi == EPI_PARTIAL)
         return launch_dma<EPI_PARTIAL, LAYOUT_KC, LAYOUT_KC, 2>(M, N, j, j, 1, splits, s);
     }
@@ -1217,7 +1281,7 @@ hipError_t launch_logits(int dtype, int64_t M, int64_t N, const Operand* A, cons
     if (j[i].K > 0 && !dma_ok(A[i], B[i])) dma = false;
   }
   if (dma) {
-    hipError_t e = launch_dma<EPI_STATS, LAYOUT_KC, LAYOUT_KC, 0>(M, N, j[0], j[0], 1, 1, s);
+    hipError_t e = launch_w4<0>(M, N, j[0], s);
     if (e == hipSuccess && njobs == 2) e = launch_w4<1>(M, N, j[1], s);
     return e;
   }

@@ -120,13 +120,13 @@ def _inputs(b: DSparkBatch) -> capi.InputsC:
                         _ptr(b.conf_b))
 
 
-def _options(recompute_bias: bool) -> int:
-    return capi.OPT_RECOMPUTE_BIAS if recompute_bias else 0
+def _options(store_draft_logits: bool) -> int:
+    return capi.OPT_STORE_DRAFT_LOGITS if store_draft_logits else 0
 
 
 def dspark_workspace_size(b: DSparkBatch, grad_dtype: Optional[torch.dtype] = None,
-                          recompute_bias: bool = False) -> int:
-    sh = make_shape(b, grad_dtype, _options(recompute_bias))
+                          store_draft_logits: bool = False) -> int:
+    sh = make_shape(b, grad_dtype, _options(store_draft_logits))
     n = capi.lib().dspark_workspace_size(C.byref(sh))
     if n == 0:
         raise capi.DSparkError("invalid shape for dspark_workspace_size")
@@ -156,12 +156,13 @@ class FwdResult:
 
 def dspark_loss_fwd(b: DSparkBatch, hp: HParams = HParams(), *, workspace=None,
                     grad_dtype: Optional[torch.dtype] = None, row_outputs: bool = True,
-                    recompute_bias: bool = False, stream=None) -> FwdResult:
+                    store_draft_logits: bool = False, stream=None) -> FwdResult:
     """Forward of the DSpark loss (``dspark_loss_fwd`` of the C ABI).
 
-    ``recompute_bias`` sets DSPARK_OPT_RECOMPUTE_BIAS (smaller workspace)."""
+    ``store_draft_logits`` sets DSPARK_OPT_STORE_DRAFT_LOGITS (materialise the
+    fp32 corrected draft logits instead of recomputing the Markov bias)."""
     dev = b.draft_logits.device
-    opts = _options(recompute_bias)
+    opts = _options(store_draft_logits)
     sh = make_shape(b, grad_dtype, opts)
     L = capi.lib()
     need = L.dspark_workspace_size(C.byref(sh))

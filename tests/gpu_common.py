@@ -21,9 +21,9 @@ def say(msg):
 
 
 def run_gpu(d: dict, hp: HParams, grad_scale: float = 1.0, teacher: str = "hidden",
-            conf: bool = True, grad_dtype=None, bwd: bool = True, recompute_bias: bool = False):
+            conf: bool = True, grad_dtype=None, bwd: bool = True, stored: bool = False):
     b = DSparkBatch.from_workload(d, teacher=teacher, conf=conf)
-    f = dspark_loss_fwd(b, hp, grad_dtype=grad_dtype, recompute_bias=recompute_bias)
+    f = dspark_loss_fwd(b, hp, grad_dtype=grad_dtype, store_draft_logits=stored)
     g = dspark_loss_bwd(b, hp, f, grad_scale, conf_hidden_grad=conf) if bwd else None
     torch.cuda.synchronize()
     return b, f, g

@@ -51,17 +51,18 @@ def test_workspace_size(L):
     assert L.dspark_workspace_size(None) == 0
 
 
-def test_recompute_bias_option_drops_the_corrected_logits_buffer(L):
-    """DSPARK_OPT_RECOMPUTE_BIAS: no fp32 [R, Vd] z' in the workspace where it applies
-    (bf16, supported rank, R and Vd multiples of 32); ignored for fp32 inputs."""
+def test_store_draft_logits_option_adds_the_corrected_logits_buffer(L):
+    """DSPARK_OPT_STORE_DRAFT_LOGITS: an fp32 [R, Vd] z' in the workspace where the
+    recompute sweeps are the default (bf16, supported rank, R and Vd multiples of 32);
+    fp32 inputs always store it, so the bit changes nothing there."""
     R, V = 2 * 16 * 7, 512
     kw = dict(num_blocks=16, markov_rank=64)
-    base = L.dspark_workspace_size(C.byref(_shape(**kw)))
-    low = L.dspark_workspace_size(C.byref(_shape(options=capi.OPT_RECOMPUTE_BIAS, **kw)))
-    assert base > 0 and low > 0
-    assert base - low >= R * V * 4 - (2 * 8 + 4) * R - 3 * 256  # minus per-row partials
+    low = L.dspark_workspace_size(C.byref(_shape(**kw)))
+    big = L.dspark_workspace_size(C.byref(_shape(options=capi.OPT_STORE_DRAFT_LOGITS, **kw)))
+    assert big > 0 and low > 0
+    assert big - low >= R * V * 4 - (2 * 8) * R - 3 * 256  # minus per-row partials
     f32 = dict(kw, dtype=0, grad_dtype=0)
-    assert (L.dspark_workspace_size(C.byref(_shape(options=capi.OPT_RECOMPUTE_BIAS, **f32)))
+    assert (L.dspark_workspace_size(C.byref(_shape(options=capi.OPT_STORE_DRAFT_LOGITS, **f32)))
             == L.dspark_workspace_size(C.byref(_shape(**f32))))
 
 
