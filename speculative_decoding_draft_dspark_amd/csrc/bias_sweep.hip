@@ -333,26 +333,19 @@ struct Sweep {
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float off = fix_exp_offset(mx);
-      uint64_t sum = 0;
+      uint32_t sum = 0;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const bool ok = cs + 32 * h + 8 * g < vlen;
-        uint64_t s8 = 0;
+        uint32_t s8 = 0;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2)
-          s8 += static_cast<uint64_t>(fix_exp32o(zp[h][rb][i], off)) +
-                fix_exp32o(zp[h][rb][i + 1], off);
-        sum += ok ? s8 : 0ull;
+        for (int i = 0; i < 8; ++i) s8 += fix_exp32o(zp[h][rb][i], off);
+        sum += ok ? s8 : 0u;
       }
-      sum = mx == -INFINITY ? 0ull : sum;
-#pragma unroll
-      for (int o = 16; o < 64; o <<= 1) {
-        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(sum), o, kWave);
-        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(sum >> 32), o, kWave);
-        sum += (static_cast<uint64_t>(hi) << 32) | lo;
-      }
-      out[rb] = make_float2(
-          mx, static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0)));
+      sum = mx == -INFINITY ? 0u : sum;
+      sum += __shfl_xor(sum, 16, kWave);
+      sum += __shfl_xor(sum, 32, kWave);
+      out[rb] = make_float2(mx, fix_to_float(sum));
     }
     // lane g = rb stores row block rb's tile (s < nsl: the tile has columns)
     const int rb = g & 1;

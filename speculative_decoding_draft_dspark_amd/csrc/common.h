@@ -14,7 +14,6 @@ constexpr int kWave = 64;
 constexpr int kStatTile = 64;   // vocab columns per softmax-statistics tile
 constexpr int kGemmTileN = 256;  // output columns of a logits GEMM tile (4 statistics tiles)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kFixScale = 2147483648.0f;  // 2^31: fixed-point scale of tile exp-sums
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -71,19 +70,26 @@ __device__ __forceinline__ float sgn_prob(float d) {
   return __builtin_amdgcn_fmed3f(d * 0x1p126f, -1.f, 1.f);
 }
 
-// exp(x - m) for x <= m in the fixed point (2^31 scale) of the tile
-// exp-sums, as 2^(x log2 e + 31 - m log2 e) truncated to an integer (one fma,
-// one exp2, one conversion).  At x = m the exponent is 31 plus the rounding
-// error of m log2 e, far below 32 for any finite logit, so 32 bits hold it.
-// Sums of these integers do not depend on the order of the columns, and every
-// kernel that produces tile statistics uses this one routine, so equal rows
+// exp(x - m) for x <= m in the fixed point (2^25 scale) of the tile
+// exp-sums, as 2^(x log2 e + 25 - m log2 e) truncated to an integer (one fma,
+// one exp2, one conversion).  At x = m the exponent is 25 plus the rounding
+// error of m log2 e (below 1/2 for |m| < 10^7), so a 64-column statistics
+// tile sums to less than 64 x 2^25.5 < 2^32: every tile sum is one 32-bit
+// integer, exact and independent of the order of the columns.  The
+// truncation costs at most 64 x 2^-25 of a sum that is at least 1.  Every
+// kernel that produces tile statistics uses these routines, so equal rows
 // give bitwise-equal statistics.
-__device__ __forceinline__ float fix_exp_offset(float m) { return 31.f - m * kLog2e; }
+constexpr float kFixBits = 25.f;
+__device__ __forceinline__ float fix_exp_offset(float m) { return kFixBits - m * kLog2e; }
 __device__ __forceinline__ uint32_t fix_exp32o(float x, float off) {
   return static_cast<uint32_t>(__builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, off)));
 }
 __device__ __forceinline__ uint32_t fix_exp32(float x, float m) {
   return fix_exp32o(x, fix_exp_offset(m));
+}
+// A tile's fixed-point exp-sum as the float sum of exp(x - max).
+__device__ __forceinline__ float fix_to_float(uint32_t s) {
+  return static_cast<float>(s) * 0x1p-25f;
 }
 
 // ---- reductions -----------------------------------------------------------

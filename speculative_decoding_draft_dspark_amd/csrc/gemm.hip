@@ -99,7 +99,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // exp(x - m) in the fixed point of the tile exp-sums, widened for summing.
-__device__ __forceinline__ uint64_t fix_exp(float x, float m) { return fix_exp32(x, m); }
+__device__ __forceinline__ uint32_t fix_exp(float x, float m) { return fix_exp32(x, m); }
 
 // ------------------------------------------------------------------ accumulators
 
@@ -235,7 +235,7 @@ __device__ __forceinline__ void row_epilogue(const AccT& acc, int wr, int wc, fl
         for (int o = 1; o < kLanesPerRow; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
         // fixed-point sum of exp(x - max): exact integer adds, so the result
         // does not depend on the order in which the columns are visited
-        uint64_t sum = 0;
+        uint32_t sum = 0;
         if (mx != -INFINITY) {
 #pragma unroll
           for (int i = 2 * st; i < 2 * st + 2; ++i) {
@@ -247,15 +247,9 @@ __device__ __forceinline__ void row_epilogue(const AccT& acc, int wr, int wc, fl
           }
         }
 #pragma unroll
-        for (int o = 1; o < kLanesPerRow; o <<= 1) {
-          const uint32_t lo = __shfl_xor(static_cast<uint32_t>(sum), o, kWave);
-          const uint32_t hi = __shfl_xor(static_cast<uint32_t>(sum >> 32), o, kWave);
-          sum += (static_cast<uint64_t>(hi) << 32) | lo;
-        }
-        if (sub == 0 && rowok && n0 + kStatTile * st < N) {
-          const float l = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
-          ep.stats[row * ep.nstat + tn * (BN / kStatTile) + st] = make_float2(mx, l);
-        }
+        for (int o = 1; o < kLanesPerRow; o <<= 1) sum += __shfl_xor(sum, o, kWave);
+        if (sub == 0 && rowok && n0 + kStatTile * st < N)
+          ep.stats[row * ep.nstat + tn * (BN / kStatTile) + st] = make_float2(mx, fix_to_float(sum));
       }
     } else if (rowok) {
 #pragma unroll
@@ -923,19 +917,26 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, row_ror<2>(v));
   return fmaxf(v, row_ror<1>(v));
 }
-template <int ROR>
-__device__ __forceinline__ uint64_t row_ror64(uint64_t v) {
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      0, static_cast<int>(static_cast<uint32_t>(v)), 0x120 + ROR, 0xf, 0xf, false));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      0, static_cast<int>(static_cast<uint32_t>(v >> 32)), 0x120 + ROR, 0xf, 0xf, false));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ uint64_t row16_sum(uint64_t v) {
-  v += row_ror64<8>(v);
-  v += row_ror64<4>(v);
-  v += row_ror64<2>(v);
-  return v + row_ror64<1>(v);
+// Sums of the four per-lane values p[0..3] over each row of 16 lanes,
+// transposed: lane sub returns the row's total of p[sub >> 2].  Exchange with
+// lane sub ^ 8 (row_ror:8), keeping values 2 b3, 2 b3 + 1 (b3 = bit 3 of sub);
+// then with the mirror lane of the half row (row_half_mirror), keeping value
+// 2 b3 + b2; then within the quad (quad_perm xor 1, xor 2).  The four partial
+// sets of a quad's lanes tile the 16 lanes.  11 VALU operations where four
+// separate 16-lane reductions take 16.
+__device__ __forceinline__ uint32_t quad_tile_sums(const uint32_t (&p)[4], int sub) {
+  const bool b3 = (sub & 8) != 0, b2 = (sub & 4) != 0;
+  const uint32_t k0 = b3 ? p[2] : p[0], k1 = b3 ? p[3] : p[1];
+  const uint32_t s0 = b3 ? p[0] : p[2], s1 = b3 ? p[1] : p[3];
+  const uint32_t a0 = k0 + dpp_u32<0x128>(s0), a1 = k1 + dpp_u32<0x128>(s1);
+  uint32_t c = (b2 ? a1 : a0) + dpp_u32<0x141>(b2 ? a0 : a1);
+  c += dpp_u32<0xB1>(c);  // quad_perm [1, 0, 3, 2]
+  return c + dpp_u32<0x4E>(c);  // quad_perm [2, 3, 0, 1]
 }
 
 
@@ -1021,10 +1022,12 @@ __device__ __forceinline__ void w4_eblock(const f32x16_v (&acc)[4][4], int i,
           w, rc, (rok && cok) ? static_cast<uint32_t>((rl * ep.ldc + c) * 4) : kOutOfRange, 0, 0);
     }
     // statistics of the 4 tiles of 64 columns (tile t = the lanes' t-th
-    // vector): maximum and fixed-point exp-sum over the row's 16 lanes; the
-    // columns past N contribute nothing, and a tile with no column in range
-    // (mx = -inf) is not stored
-    float mx[4], lt[4];
+    // vector): maximum (every lane gets all four) and fixed-point exp-sum
+    // (the lanes of quad q get tile q's) over the row's 16 lanes; the columns
+    // past N contribute nothing, and a tile with no column in range is not
+    // stored
+    float mx[4];
+    uint32_t ps[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float m4 = fmaxf(fmaxf(v[t].x, v[t].y), fmaxf(v[t].z, v[t].w));
@@ -1033,20 +1036,19 @@ __device__ __forceinline__ void w4_eblock(const f32x16_v (&acc)[4][4], int i,
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float off = fix_exp_offset(mx[t]);
-      uint64_t t4 = static_cast<uint64_t>(fix_exp32o(v[t].x, off)) + fix_exp32o(v[t].y, off) +
-                    (static_cast<uint64_t>(fix_exp32o(v[t].z, off)) + fix_exp32o(v[t].w, off));
-      t4 = (n0 + 4 * sub + 64 * t < N) ? t4 : 0ull;
-      const uint64_t sum = row16_sum(t4);
-      lt[t] = static_cast<float>(static_cast<double>(sum) * (1.0 / 2147483648.0));
+      const uint32_t s4 = fix_exp32o(v[t].x, off) + fix_exp32o(v[t].y, off) +
+                          fix_exp32o(v[t].z, off) + fix_exp32o(v[t].w, off);
+      ps[t] = (n0 + 4 * sub + 64 * t < N) ? s4 : 0u;
     }
-    // lane sub < 4 stores tile sub
-    const float ms = sub == 0 ? mx[0] : (sub == 1 ? mx[1] : (sub == 2 ? mx[2] : mx[3]));
-    const float ls = sub == 0 ? lt[0] : (sub == 1 ? lt[1] : (sub == 2 ? lt[2] : lt[3]));
+    const uint32_t tot = quad_tile_sums(ps, sub);
+    // lane 4 q of the row stores tile q
+    const int q = sub >> 2;
+    const float ms = q == 0 ? mx[0] : (q == 1 ? mx[1] : (q == 2 ? mx[2] : mx[3]));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(ep.stats + r0 * ep.nstat + 4 * tn);
-    const u32x2 sv = {__float_as_uint(ms), __float_as_uint(ls)};
-    const bool sok = sub < 4 && rok && n0 + kStatTile * sub < N;
+    const u32x2 sv = {__float_as_uint(ms), __float_as_uint(fix_to_float(tot))};
+    const bool sok = (sub & 3) == 0 && rok && n0 + kStatTile * q < N;
     __builtin_amdgcn_raw_buffer_store_b64(
-        sv, rs, sok ? static_cast<uint32_t>((rl * ep.nstat + sub) * 8) : kOutOfRange, 0, 0);
+        sv, rs, sok ? static_cast<uint32_t>((rl * ep.nstat + q) * 8) : kOutOfRange, 0, 0);
   }
 }
 
