@@ -32,6 +32,10 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 // past the end read as zero and stores there are dropped, so every load and
 // store is issued unconditionally and the compiler's wait counts stay exact.
 constexpr uint32_t kOOB = 0xffffffffu;
+// Cache policy of the statistics sweep's z stream: non-temporal, so it does
+// not evict the W2 slices every row tile re-reads (measured faster there; the
+// L1 and gradient sweeps' streams measured faster with the default policy).
+constexpr int kStream = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
                                            0x00020000);
@@ -80,7 +84,11 @@ struct BiasEngine {
 
   u32x4 e[2][KS];  // [row block][k step]
 
-  __device__ static int slot(int v, int c) { return v * CPR + (c ^ (v & SWM)); }
+  // LDS slot of chunk c of W2 row v: the chunk index is XORed with the MFMA
+  // lane cl that reads row v (vcol(b, cl) = v), so the 16 rows one quarter
+  // wave reads at the same k land in 16 distinct 16-byte bank groups.
+  __device__ static int lane_of(int v) { return (v & 3) | ((v >> 1) & 12); }
+  __device__ static int slot(int v, int c) { return v * CPR + (c ^ (lane_of(v) & SWM)); }
 
   // E fragments: lane (g, cl) holds row r0 + 16 rb + cl at rank 32 ks + 8 g .. + 7.
   __device__ void load_e(const bf16_t* E, int64_t r0, int64_t R) {
@@ -100,7 +108,7 @@ struct BiasEngine {
   // Queue W2 rows [v0, v0 + 64) into a ring stage (rows past vend read zero):
   // the wave's p-th load fills chunks [(wave kPer + p) 64, + 64) of the stage,
   // lane l the one at + l, i.e. row idx / CPR, slot idx % CPR, which holds
-  // chunk slot ^ (row & SWM).  kPer loads per thread, always issued.
+  // chunk slot ^ (lane_of(row) & SWM).  kPer loads per thread, always issued.
   __device__ void dma(const bf16_t* W2, int64_t v0, int64_t vend, u32x4* stage) const {
     if (RANK == 0) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -109,7 +117,7 @@ struct BiasEngine {
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
       const int idx = (wave * kPer + p) * 64 + lane;
-      const int v = idx / CPR, c = (idx % CPR) ^ (v & SWM);
+      const int v = idx / CPR, c = (idx % CPR) ^ (lane_of(v) & SWM);
       const uint32_t off = (idx < kChunks && v0 + v < vend)
                                ? static_cast<uint32_t>((v * RANK + 8 * c) * 2)
                                : kOOB;
@@ -272,7 +280,8 @@ struct Sweep {
         const int col = cs + 32 * h + 8 * g;
         const bool ok = rowok[rb] && col < vlen;
         const uint32_t e = ebase[rb] + static_cast<uint32_t>(col);
-        d.z[h][rb] = __builtin_amdgcn_raw_buffer_load_b128(rz, ok ? e * 2 : kOOB, 0, 0);
+        d.z[h][rb] = __builtin_amdgcn_raw_buffer_load_b128(rz, ok ? e * 2 : kOOB, 0,
+                                                           MODE == kStats ? kStream : 0);
         if (TEACHER) {
 #pragma unroll
           for (int q = 0; q < 2; ++q)

@@ -56,6 +56,10 @@ template <> struct Mfma<float> {
 constexpr int kNumRecords = 0x7fffffff;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache policy of buffer accesses that stream data used once (the logits
+// tiles): non-temporal, so they do not evict the operand panels other tiles
+// re-read from L2 and the memory-side cache.
+constexpr int kStreamPolicy = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, kNumRecords, kRsrcWord3);
@@ -970,7 +974,7 @@ __device__ __forceinline__ void w4_x_issue(uint2 (&xv)[4][4], const EpiParams& e
       const uint32_t off = (rok && n0 + c < N)
                                ? static_cast<uint32_t>((rl * ep.ldx + c) * 2)
                                : kOutOfRange;
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, kStreamPolicy);
       xv[p][t] = make_uint2(v.x, v.y);
     }
   }
@@ -1019,7 +1023,8 @@ __device__ __forceinline__ void w4_eblock(const f32x16_v (&acc)[4][4], int i,
       const u32x4 w = {__float_as_uint(v[t].x), __float_as_uint(v[t].y), __float_as_uint(v[t].z),
                        __float_as_uint(v[t].w)};
       __builtin_amdgcn_raw_buffer_store_b128(
-          w, rc, (rok && cok) ? static_cast<uint32_t>((rl * ep.ldc + c) * 4) : kOutOfRange, 0, 0);
+          w, rc, (rok && cok) ? static_cast<uint32_t>((rl * ep.ldc + c) * 4) : kOutOfRange, 0,
+          kStreamPolicy);
     }
     // statistics of the 4 tiles of 64 columns (tile t = the lanes' t-th
     // vector): maximum (every lane gets all four) and fixed-point exp-sum
