@@ -168,7 +168,11 @@ int dspark_loss_fwd(const dspark_shape *shape, const dspark_hparams *hp, const d
 /* Backward of `loss` with upstream gradient `grad_scale` (Megatron-Core scales
  * by 1 / global num_tokens).  Outputs are overwritten, not accumulated.  The
  * teacher gets no gradient (API page: the teacher is "already detached"), and
- * the BCE label is treated as a constant. */
+ * the BCE label is treated as a constant.  With bf16 inputs the Markov weight
+ * gradients contract the logit gradient G at the precision of d_draft_logits:
+ * grad_dtype bf16 -> the bf16 G that is written out (as a bf16 autograd would;
+ * about 2^-10 normwise, like dz itself; R and Vd multiples of 32), grad_dtype
+ * fp32 -> G as bf16 high + low parts (about 2^-18). */
 int dspark_loss_bwd(const dspark_shape *shape, const dspark_hparams *hp, const dspark_inputs *in,
                     void *workspace, size_t workspace_bytes, float grad_scale,
                     dspark_bwd_out *out, dspark_stream_t stream);

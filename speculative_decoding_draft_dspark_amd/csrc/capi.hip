@@ -32,6 +32,11 @@ struct Dims {
   // bf16 backward products read G, W2 and E in place (row counts and the
   // vocabulary multiples of 32); otherwise through transposed / k-blocked copies
   bool direct_bwd;
+  // The Markov weight products take G as bf16 hi + bf16 lo (two K segments).
+  // Not with bf16 draft-logit gradients on the in-place backward: there the
+  // products take the bf16 dz itself, as a bf16 autograd does (their error is
+  // then that of dz's own rounding, about 2^-10 normwise).
+  bool g_lo;
   // bf16 corrected draft logits never stored: every vocabulary sweep rebuilds
   // z' = z + E W2^T (ranks the bias sweeps support, with the in-place backward)
   bool bias_path;
@@ -81,6 +86,7 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   if (sp < 1) sp = 1;
   d->direct_bwd = d->dtype == DSPARK_BF16 && d->markov && d->R % 32 == 0 && d->Vd % 32 == 0;
   d->dw2_splits = 2;
+  d->g_lo = d->markov && !(d->direct_bwd && d->gdtype == DSPARK_BF16);
   if (d->direct_bwd) {
     // Split counts of the in-place products: the smallest whose tiles x
     // splits workgroups fill whole waves of the 256 CUs within 2 %, each
@@ -95,9 +101,9 @@ int make_dims(const dspark_shape* sh, Dims* d) {
       }
       return best;
     };
-    sp = pick(nM, 2 * d->Vd / 32);
-    // dW2: one split per hi / lo half of the rows (more splits measured slower:
-    // the partial-sum traffic outweighs the better wave fill)
+    sp = pick(nM, (d->g_lo ? 2 : 1) * d->Vd / 32);
+    // dW2: two K splits (the hi and lo halves, or two halves of the rows; more
+    // splits measured slower: the partial-sum traffic outweighs the wave fill)
     d->dw2_splits = 2 * d->R / 32 >= 16 ? 2 : 1;
   }
   d->splits = d->markov ? sp : 0;
@@ -135,7 +141,7 @@ Layout make_layout(const Dims& d) {
   L.ghi = L.glo = L.g32 = L.w2t = L.eblk = L.blkhi = L.blklo = L.dw2part = 0;
   if (d.dtype == DSPARK_BF16) {
     if (d.gdtype != DSPARK_BF16) { L.ghi = o; o = up(o + RV * 2); }
-    L.glo = o; o = up(o + RV * 2);
+    if (d.g_lo) { L.glo = o; o = up(o + RV * 2); }
     if (d.markov && d.direct_bwd) {
       L.dw2part = o; o = up(o + static_cast<size_t>(d.dw2_splits) * d.Vd * d.r * 4);
     } else if (d.markov) {
@@ -422,7 +428,8 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     // dE = G . W2 (contraction over the vocabulary) and k-blocked by 8 rows for
     // dW2 = G^T . E (contraction over rows).
     bf16_t* ghi = d.gdtype == DSPARK_BF16 ? nullptr : reinterpret_cast<bf16_t*>(ws + L.ghi);
-    bf16_t* glo = reinterpret_cast<bf16_t*>(ws + L.glo);
+    bf16_t* glo = d.g_lo ? reinterpret_cast<bf16_t*>(ws + L.glo) : nullptr;
+    const int gseg = d.g_lo ? 2 : 1;  // K segments of the products: G hi (, G lo)
     const void* gA = ghi ? static_cast<const void*>(ghi) : out->d_draft_logits;
     bf16_t* bhi = reinterpret_cast<bf16_t*>(ws + L.blkhi);
     bf16_t* blo = reinterpret_cast<bf16_t*>(ws + L.blklo);
@@ -436,21 +443,22 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
                                    d.markov ? static_cast<const bf16_t*>(in->markov_w2) : nullptr,
                                    teacher != kNone ? T : nullptr, in->target_ids, rs,
                                    teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
-                                   out->d_draft_logits, ghi, d.markov ? glo : nullptr, s));
+                                   out->d_draft_logits, ghi, glo, s));
     }
     if (d.direct_bwd) {
-      // G as dz (hi) and its bf16 remainder (lo), row-major; both products
-      // read G, W2 and E in place.
+      // G as dz (hi) and, with fp32 dz, its bf16 remainder (lo), row-major;
+      // both products read G, W2 and E in place.
       if (!d.bias_path)
         DSPARK_STAGE(kGradSweep, launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs,
                                                    teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
                                                    out->d_draft_logits, ghi, glo, nullptr, s));
-      {  // dE partials = [G hi | G lo] . [W2 | W2] over vocabulary splits
+      {  // dE partials = [G hi | G lo] . [W2 | W2] (or G . W2) over vocabulary splits
         Operand A{}, B{};
-        A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.Vd; A.kpad = d.Vd;
-        A.ld = d.Vd; A.layout = LAYOUT_KC; A.nseg = 2;
+        A.seg[0] = gA; A.seg[1] = glo ? static_cast<const void*>(glo) : gA;
+        A.kseg = d.Vd; A.kpad = d.Vd;
+        A.ld = d.Vd; A.layout = LAYOUT_KC; A.nseg = gseg;
         B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.Vd; B.kpad = d.Vd; B.ld = d.r;
-        B.layout = LAYOUT_MK; B.nseg = 2;
+        B.layout = LAYOUT_MK; B.nseg = gseg;
         DSPARK_STAGE(kDeGemm, launch_gemm_w4p(2, d.R, d.r, A, B, static_cast<int>(d.splits),
                                               dEpart, d.r, s));
       }
@@ -460,13 +468,14 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
       DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
       DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
                                             out->d_markov_w1, s));
-      {  // dW2 = [G hi ; G lo]^T . [E ; E] over row splits, then summed
+      {  // dW2 = [G hi ; G lo]^T . [E ; E] (or G^T . E) over row splits, then summed
         float* part = reinterpret_cast<float*>(ws + L.dw2part);
         Operand A{}, B{};
-        A.seg[0] = gA; A.seg[1] = glo; A.kseg = d.R; A.kpad = d.R;
-        A.ld = d.Vd; A.layout = LAYOUT_MK; A.nseg = 2;
+        A.seg[0] = gA; A.seg[1] = glo ? static_cast<const void*>(glo) : gA;
+        A.kseg = d.R; A.kpad = d.R;
+        A.ld = d.Vd; A.layout = LAYOUT_MK; A.nseg = gseg;
         B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = d.R; B.ld = d.r;
-        B.layout = LAYOUT_MK; B.nseg = 2;
+        B.layout = LAYOUT_MK; B.nseg = gseg;
         const int sp = static_cast<int>(d.dw2_splits);
         DSPARK_STAGE(kDw2Gemm, launch_gemm_w4p(3, d.Vd, d.r, A, B, sp, part, d.r, s));
         DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, sp, part, out->d_markov_w2, s));
