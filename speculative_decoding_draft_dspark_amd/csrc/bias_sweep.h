@@ -29,11 +29,16 @@ hipError_t launch_bias_stats(int64_t R, int64_t V, int64_t rank, const bf16_t* z
                              const bf16_t* W2, float2* sz, int64_t nstat, hipStream_t s);
 
 // On supervised rows, per vocabulary split: sum |p - q| and sum p sign(p - q)
-// (fp64 partials [splits, R] each), with p = exp(z' - lse_z), q = exp(T - lse_t).
-// Without a teacher (T == nullptr) there is nothing to sweep: no launch.
+// (fp64 partials [splits, R] each), with p = exp(z' - lse_z), q = exp(T - lse_t);
+// and sign(p - q) of every element as two bits (p > q, p < q) into `signs`
+// (bias_signs_words() uint2 words) for the gradient pass.  Without a teacher
+// (T == nullptr) there is nothing to sweep: no launch.
 hipError_t launch_bias_l1(int64_t R, int64_t V, int64_t rank, const bf16_t* z, const bf16_t* E,
                           const bf16_t* W2, const float* T, const int32_t* tid, RowState rs,
-                          double* part_l1, double* part_s, hipStream_t s);
+                          double* part_l1, double* part_s, uint2* signs, hipStream_t s);
+
+// uint2 words of the sign bits launch_bias_l1 writes.
+int64_t bias_signs_words(int64_t R, int64_t V);
 
 // Per row: L1 and S from the split partials (0 without a teacher) and
 // CE = lse_z - z'_y with z'_y = z_y + E_row . W2_y (masked rows: 0).
@@ -45,9 +50,11 @@ hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int64_t rank, int splits,
 // G = g w [ce_a (p - [v = y]) + l1_a p (sign(p - q) - S)] (0 on unsupervised rows):
 // dz in the gradient dtype (grad_dtype 1 = bf16: dz is the bf16 high part),
 // ghi = bf16(G) when dz is fp32, glo = bf16(G - bf16(G)).
+// With a teacher, sign(p - q) comes from the bits launch_bias_l1 wrote (T is
+// not read again).
 hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, const bf16_t* z,
-                            const bf16_t* E, const bf16_t* W2, const float* T, const int32_t* tid,
-                            RowState rs, int has_teacher, float g, float ce_a, float l1_a, void* dz,
-                            bf16_t* ghi, bf16_t* glo, hipStream_t s);
+                            const bf16_t* E, const bf16_t* W2, const uint2* signs,
+                            const int32_t* tid, RowState rs, int has_teacher, float g, float ce_a,
+                            float l1_a, void* dz, bf16_t* ghi, bf16_t* glo, hipStream_t s);
 
 }  // namespace dspark

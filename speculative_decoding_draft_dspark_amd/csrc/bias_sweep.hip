@@ -87,11 +87,11 @@ struct BiasEngine {
   // LDS slot of chunk c of W2 row v: the chunk index is XORed with the MFMA
   // lane cl that reads row v (vcol(b, cl) = v), so the 16 rows one quarter
   // wave reads at the same k land in 16 distinct 16-byte bank groups.
-  __device__ static int lane_of(int v) { return (v & 3) | ((v >> 1) & 12); }
-  __device__ static int slot(int v, int c) { return v * CPR + (c ^ (lane_of(v) & SWM)); }
+  __device__ __forceinline__ static int lane_of(int v) { return (v & 3) | ((v >> 1) & 12); }
+  __device__ __forceinline__ static int slot(int v, int c) { return v * CPR + (c ^ (lane_of(v) & SWM)); }
 
   // E fragments: lane (g, cl) holds row r0 + 16 rb + cl at rank 32 ks + 8 g .. + 7.
-  __device__ void load_e(const bf16_t* E, int64_t r0, int64_t R) {
+  __device__ __forceinline__ void load_e(const bf16_t* E, int64_t r0, int64_t R) {
     const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -109,7 +109,7 @@ struct BiasEngine {
   // the wave's p-th load fills chunks [(wave kPer + p) 64, + 64) of the stage,
   // lane l the one at + l, i.e. row idx / CPR, slot idx % CPR, which holds
   // chunk slot ^ (lane_of(row) & SWM).  kPer loads per thread, always issued.
-  __device__ void dma(const bf16_t* W2, int64_t v0, int64_t vend, u32x4* stage) const {
+  __device__ __forceinline__ void dma(const bf16_t* W2, int64_t v0, int64_t vend, u32x4* stage) const {
     if (RANK == 0) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const __amdgpu_buffer_rsrc_t rs =
@@ -128,7 +128,7 @@ struct BiasEngine {
   // Bias of vocabulary blocks 2 h, 2 h + 1 of the slice in buf for both row
   // blocks: acc[bb][rb]; four independent MFMA chains, the next k step's W2
   // fragments read while the current step's MFMAs run.
-  __device__ void bias_pair(const u32x4* buf, int h, f32x4_v (&acc)[2][2]) const {
+  __device__ __forceinline__ void bias_pair(const u32x4* buf, int h, f32x4_v (&acc)[2][2]) const {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -157,12 +157,13 @@ struct BiasEngine {
   }
 };
 
-// The lane's z (bf16) and T (fp32) of one slice: per block pair h and row
-// block rb, the 8 columns 32 h + 8 g .. + 7.
-template <bool TEACHER>
+// The lane's z (bf16), T (fp32, L1 pass) and sign bits (gradient pass) of
+// one slice: per block pair h and row block rb, the 8 columns 32 h + 8 g .. + 7.
+template <bool LOADT, bool LOADS>
 struct SliceData {
   u32x4 z[2][2];
-  u32x4 t[TEACHER ? 2 : 1][2][2];  // [h][rb][half]
+  u32x4 t[LOADT ? 2 : 1][2][2];  // [h][rb][half]
+  u32x2 sg;                      // [p > q, p < q], bit (2 h + rb) 8 + i
 };
 
 // z' of the lane's 8 columns (h, rb): z + the bias blocks 2 h (columns
@@ -190,6 +191,7 @@ struct SweepParams {
   float2* sz;
   double* part_l1;
   double* part_s;
+  u32x2* signs;  // [row tiles x 8 waves][nstat][64 lanes]
   void* dz;
   bf16_t* ghi;
   bf16_t* glo;
@@ -197,14 +199,18 @@ struct SweepParams {
 };
 
 // State of one sweep over a workgroup's 256 rows and vocabulary range.
+// TEACHER: a teacher exists (the L1 pass reads T and writes the sign bits of
+// p - q; the gradient pass reads those bits instead of T).
 template <int RANK, int MODE, bool TEACHER, typename GT>
 struct Sweep {
   using Eng = BiasEngine<RANK>;
-  using SD = SliceData<TEACHER>;
-  static constexpr int kZT = TEACHER ? 12 : 4;  // z / T loads per lane per slice
+  static constexpr bool kLoadT = TEACHER && MODE == kL1;
+  static constexpr bool kLoadS = TEACHER && MODE == kGrad;
+  using SD = SliceData<kLoadT, kLoadS>;
+  static constexpr int kZT = 4 + (kLoadT ? 8 : 0) + (kLoadS ? 1 : 0);  // loads per lane per slice
   // slices of z / T in flight ahead of the one in use: 2 without T, 1 with T
   // (three register sets of z and T would not fit two waves per SIMD)
-  static constexpr int kLead = TEACHER ? 1 : 2;
+  static constexpr int kLead = kLoadT ? 1 : 2;
   const SweepParams& P;
   u32x4* ring;  // kStages x Eng::kStageCh
   Eng eng;
@@ -214,14 +220,17 @@ struct Sweep {
   int g, cl;
   int vlen;        // columns in the range
   bool rowok[2], sup[2];
-  float lz[2], lt[2], Sr[2], cc[2], cl1[2];
+  float lz[2], lt[2], Sr[2], cc[2], cl1[2];  // lz, lt: lse_z, lse_t times log2 e
   int yl[2];          // target column within the range, -1 if outside
   uint32_t ebase[2];  // element offset of (row r0 + 16 rb + cl, column vb) from row r0
   __amdgpu_buffer_rsrc_t rz, rt;      // z and T from row r0
   __amdgpu_buffer_rsrc_t rd, rh, rl;  // dz, G hi, G lo from row r0
+  __amdgpu_buffer_rsrc_t rsg;         // the wave's sign words
   double a_l1[2], a_s[2];  // L1 pass accumulators
+  uint32_t wgt, wlt;       // L1 pass: sign words of the slice in progress
+  float c0[2];             // gradient: g w (ce_a - l1_a S); + / - g w l1_a for sign +1 / -1
 
-  __device__ Sweep(const SweepParams& p, u32x4* rg) : P(p), ring(rg) {
+  __device__ __forceinline__ Sweep(const SweepParams& p, u32x4* rg) : P(p), ring(rg) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     g = lane >> 4;
@@ -235,7 +244,9 @@ struct Sweep {
     vlen = static_cast<int>(ve > vb ? ve - vb : 0);
     const uint32_t span = static_cast<uint32_t>(kRowsPerWave * P.V);  // elements
     rz = rsrc_of(P.z + r0 * P.V, span * 2);
-    rt = rsrc_of(TEACHER ? P.T + r0 * P.V : P.T, TEACHER ? span * 4 : 0);
+    rt = rsrc_of(kLoadT ? P.T + r0 * P.V : P.T, kLoadT ? span * 4 : 0);
+    rsg = rsrc_of(TEACHER ? P.signs + (r0 / kRowsPerWave) * P.nstat * 64 : P.signs,
+                  TEACHER ? static_cast<uint32_t>(P.nstat * 64 * 8) : 0);
     if (MODE == kGrad) {
       rd = rsrc_of(static_cast<char*>(P.dz) + r0 * P.V * sizeof(GT), span * sizeof(GT));
       rh = rsrc_of(P.ghi ? P.ghi + r0 * P.V : P.ghi, P.ghi ? span * 2 : 0);
@@ -246,16 +257,18 @@ struct Sweep {
       const int64_t row = r0 + 16 * rb + cl;
       rowok[rb] = row < P.R;
       sup[rb] = MODE != kStats && rowok[rb] && P.rs.mask[row] != 0;
-      lz[rb] = lt[rb] = Sr[rb] = cc[rb] = cl1[rb] = 0.f;
+      lz[rb] = lt[rb] = Sr[rb] = cc[rb] = cl1[rb] = c0[rb] = 0.f;
       int64_t y = -1;
       if (MODE != kStats && sup[rb]) {
-        lz[rb] = P.rs.lse_z[row];
-        lt[rb] = P.rs.lse_t[row];
+        // exp(x - lse) as exp2(x log2 e - lse log2 e): one fma per element
+        lz[rb] = P.rs.lse_z[row] * kLog2e;
+        lt[rb] = P.rs.lse_t[row] * kLog2e;
         if (MODE == kGrad) {
           const float gw = P.g * P.rs.w[row];
           cc[rb] = gw * P.ce_a;
           cl1[rb] = gw * P.l1_a;
           Sr[rb] = P.rs.S[row];
+          c0[rb] = cc[rb] - cl1[rb] * Sr[rb];
         }
         const int64_t t = P.tid[row];
         y = t < 0 ? 0 : (t >= P.V ? P.V - 1 : t);
@@ -266,12 +279,12 @@ struct Sweep {
     }
   }
 
-  __device__ int64_t col0(int s) const { return vb + static_cast<int64_t>(s) * kSliceV; }
-  __device__ u32x4* stage(int t) const { return ring + (t % kStages) * Eng::kStageCh; }
+  __device__ __forceinline__ int64_t col0(int s) const { return vb + static_cast<int64_t>(s) * kSliceV; }
+  __device__ __forceinline__ u32x4* stage(int t) const { return ring + (t % kStages) * Eng::kStageCh; }
 
   // The lane's z and T of the slice at column cs of the range (columns past
   // the range, rows past R read zero).
-  __device__ void load(SD& d, int cs) const {
+  __device__ __forceinline__ void load(SD& d, int cs) const {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -282,13 +295,20 @@ struct Sweep {
         const uint32_t e = ebase[rb] + static_cast<uint32_t>(col);
         d.z[h][rb] = __builtin_amdgcn_raw_buffer_load_b128(rz, ok ? e * 2 : kOOB, 0,
                                                            MODE == kStats ? kStream : 0);
-        if (TEACHER) {
+        if (kLoadT) {
 #pragma unroll
           for (int q = 0; q < 2; ++q)
             d.t[h][rb][q] =
                 __builtin_amdgcn_raw_buffer_load_b128(rt, ok ? (e + 4 * q) * 4 : kOOB, 0, 0);
         }
       }
+    if (kLoadS) {
+      // slices past the range: an offset past the buffer, reads zeros
+      const int tn = (static_cast<int>(vb) + cs) / kSliceV;
+      const int lane = threadIdx.x & 63;
+      d.sg = __builtin_amdgcn_raw_buffer_load_b64(
+          rsg, cs < vlen ? static_cast<uint32_t>((tn * 64 + lane) * 8) : kOOB, 0, 0);
+    }
   }
 
   // Slice s, whose z / T are in `cur`; queues W2 of slice s + 3 into the ring
@@ -297,7 +317,7 @@ struct Sweep {
   // wait on loads still in flight.  Loads past the range read zeros and are
   // always issued, and the per-element conditions are selects, so every wait
   // count is static.
-  __device__ void step(int s, const SD& cur, SD& nxt) {
+  __device__ __forceinline__ void step(int s, const SD& cur, SD& nxt) {
     // W2 of slice s landed: it was queued in step s - 3 (the prologue drains
     // its own), followed by that step's z / T loads and two more steps' DMA
     // and z / T loads (stores only add to the count)
@@ -308,10 +328,11 @@ struct Sweep {
     // otherwise loop strength reduction keeps one induction variable per
     // (slice of the unrolled loop, element) column test, far more registers
     // than recomputing the columns from cs each step
-    int cs = s * kSliceV;
+    int cs = __builtin_amdgcn_readfirstlane(s * kSliceV);
     asm volatile("" : "+s"(cs));
     load(nxt, cs + kLead * kSliceV);
     float zp[2][2][8];  // [h][rb][column]
+    wgt = wlt = 0u;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4_v acc[2][2];
@@ -322,11 +343,17 @@ struct Sweep {
       if (MODE == kGrad) grad_work(cs, h, cur, zp[h]);
     }
     if (MODE == kStats) stats_work(cs, zp);
+    if (MODE == kL1) {  // every slice's words, stored unconditionally
+      const int tn = (static_cast<int>(vb) + cs) / kSliceV;
+      const int lane = threadIdx.x & 63;
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{wgt, wlt}, rsg,
+                                            static_cast<uint32_t>((tn * 64 + lane) * 8), 0, 0);
+    }
   }
 
   // Statistics of the slice (one 64-column tile) for both row blocks: the
   // maximum, then the fixed-point exp-sum, over the row's 4 lanes (g).
-  __device__ void stats_work(int cs, const float (&zp)[2][2][8]) {
+  __device__ __forceinline__ void stats_work(int cs, const float (&zp)[2][2][8]) {
     float2 out[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -369,13 +396,15 @@ struct Sweep {
   }
 
   // The lane's column i of 8 holding the row's target, or -1.
-  __device__ static int target_in(int yl_, int col) {
+  __device__ __forceinline__ static int target_in(int yl_, int col) {
     const int d = yl_ - col;
     return static_cast<unsigned>(d) < 8u ? d : -1;
   }
 
-  // L1 pass on block pair h: sum |p - q| and sum p sign(p - q).
-  __device__ void l1_work(int cs, int h, const SD& cur, const float (&zh)[2][8]) {
+  // L1 pass on block pair h: sum |p - q| and sum p sign(p - q), and the
+  // signs as bits for the gradient pass: p > q from the sign of q - p, p < q
+  // from the sign of p - q (both +0 on a tie: sign(0) = 0).
+  __device__ __forceinline__ void l1_work(int cs, int h, const SD& cur, const float (&zh)[2][8]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int col = cs + 32 * h + 8 * g;  // within the range
@@ -384,9 +413,15 @@ struct Sweep {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float t = __uint_as_float(cur.t[h][rb][i >> 2][i & 3]);
-        const float p = dexp(zh[rb][i] - lz[rb]), q = dexp(t - lt[rb]);
-        s1 += fabsf(p - q);
-        s2 += p * sgn_prob(p - q);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zh[rb][i], kLog2e, -lz[rb]));
+        const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(t, kLog2e, -lt[rb]));
+        const float d = p - q, e = q - p;
+        const uint32_t gt = __float_as_uint(e) >> 31, ltb = __float_as_uint(d) >> 31;
+        const int k = (2 * h + rb) * 8 + i;
+        wgt |= gt << k;
+        wlt |= ltb << k;
+        s1 += fabsf(d);
+        s2 += gt ? p : (ltb ? -p : 0.f);
       }
       a_l1[rb] += ok ? s1 : 0.f;
       a_s[rb] += ok ? s2 : 0.f;
@@ -394,7 +429,7 @@ struct Sweep {
   }
 
   // Gradient on block pair h: G = g w [ce_a (p - [v = y]) + l1_a p (sign(p - q) - S)].
-  __device__ void grad_work(int cs, int h, const SD& cur, const float (&zh)[2][8]) {
+  __device__ __forceinline__ void grad_work(int cs, int h, const SD& cur, const float (&zh)[2][8]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int col = cs + 32 * h + 8 * g;  // within the range
@@ -402,11 +437,12 @@ struct Sweep {
       float G[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = dexp(zh[rb][i] - lz[rb]);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zh[rb][i], kLog2e, -lz[rb]));
         float v;
-        if (TEACHER) {
-          const float q = dexp(__uint_as_float(cur.t[h][rb][i >> 2][i & 3]) - lt[rb]);
-          v = p * (cc[rb] + cl1[rb] * (sgn_prob(p - q) - Sr[rb]));
+        if (TEACHER) {  // g w p [ce_a + l1_a (sign(p - q) - S)], the sign from the L1 pass
+          const int k = (2 * h + rb) * 8 + i;
+          const bool gt = (cur.sg.x >> k) & 1u, ltb = (cur.sg.y >> k) & 1u;
+          v = p * (gt ? c0[rb] + cl1[rb] : (ltb ? c0[rb] - cl1[rb] : c0[rb]));
         } else {
           v = p * cc[rb];
         }
@@ -445,7 +481,7 @@ struct Sweep {
     }
   }
 
-  __device__ void finish() {
+  __device__ __forceinline__ void finish() {
     if (MODE != kL1 || !TEACHER) return;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -566,6 +602,12 @@ bool bias_sweep_ok(int64_t V, int64_t rank) {
          V % 8 == 0 && V < (int64_t{1} << 24);
 }
 
+int64_t bias_signs_words(int64_t R, int64_t V) {
+  // one word per lane, slice and wave row of every launched row tile
+  const int64_t waves = (R + kRowsPerWG - 1) / kRowsPerWG * kWaves;
+  return waves * ((V + kSliceV - 1) / kSliceV) * 64;
+}
+
 BiasGrid bias_grid(int64_t R, int64_t V) {
   // 7 workgroups per CU over the 256 CUs, each vocabulary range a whole
   // number of 64-column slices and at least 8 of them
@@ -592,10 +634,12 @@ hipError_t launch_bias_stats(int64_t R, int64_t V, int64_t rank, const bf16_t* z
 
 hipError_t launch_bias_l1(int64_t R, int64_t V, int64_t rank, const bf16_t* z, const bf16_t* E,
                           const bf16_t* W2, const float* T, const int32_t* tid, RowState rs,
-                          double* part_l1, double* part_s, hipStream_t s) {
+                          double* part_l1, double* part_s, uint2* signs, hipStream_t s) {
   if (R <= 0 || T == nullptr) return hipSuccess;
   SweepParams P = base_params(R, V, z, E, W2);
   P.T = T; P.tid = tid; P.rs = rs; P.part_l1 = part_l1; P.part_s = part_s;
+  P.signs = reinterpret_cast<u32x2*>(signs);
+  P.nstat = (V + kSliceV - 1) / kSliceV;
   return launch_mode<kL1, true, bf16_t>(rank, bias_grid(R, V), P, s);
 }
 
@@ -610,12 +654,14 @@ hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int64_t rank, int splits,
 }
 
 hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, const bf16_t* z,
-                            const bf16_t* E, const bf16_t* W2, const float* T, const int32_t* tid,
-                            RowState rs, int has_teacher, float g, float ce_a, float l1_a, void* dz,
-                            bf16_t* ghi, bf16_t* glo, hipStream_t s) {
+                            const bf16_t* E, const bf16_t* W2, const uint2* signs,
+                            const int32_t* tid, RowState rs, int has_teacher, float g, float ce_a,
+                            float l1_a, void* dz, bf16_t* ghi, bf16_t* glo, hipStream_t s) {
   if (R <= 0) return hipSuccess;
   SweepParams P = base_params(R, V, z, E, W2);
-  P.T = T; P.tid = tid; P.rs = rs; P.dz = dz; P.ghi = ghi; P.glo = glo;
+  P.tid = tid; P.rs = rs; P.dz = dz; P.ghi = ghi; P.glo = glo;
+  P.signs = reinterpret_cast<u32x2*>(const_cast<uint2*>(signs));
+  P.nstat = (V + kSliceV - 1) / kSliceV;
   P.g = g; P.ce_a = ce_a; P.l1_a = l1_a;
   const BiasGrid gr = bias_grid(R, V);
   if (grad_dtype == 1)

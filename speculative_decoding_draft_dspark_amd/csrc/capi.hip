@@ -46,6 +46,7 @@ struct Dims {
 struct Layout {
   size_t Zp, T, sz, st, E, mask, rowf, ghi, glo, g32, dEpart, dE, confpart;
   size_t pl1, ps;  // bias path: L1 / S split partials
+  size_t sg;       // bias path: sign bits of p - q (L1 pass -> gradient pass)
   size_t w2t, eblk, blkhi, blklo, dw2part;  // bf16 backward operands
   size_t total;
 };
@@ -127,10 +128,11 @@ Layout make_layout(const Dims& d) {
   const size_t RV = static_cast<size_t>(d.R) * d.Vd;
   L.Zp = o;
   if (!d.bias_path) o = up(o + RV * 4);
-  L.pl1 = L.ps = o;
+  L.pl1 = L.ps = L.sg = o;
   if (d.bias_path) {
     L.pl1 = o; o = up(o + static_cast<size_t>(d.bsplits) * d.R * 8);
     L.ps = o; o = up(o + static_cast<size_t>(d.bsplits) * d.R * 8);
+    L.sg = o; o = up(o + static_cast<size_t>(bias_signs_words(d.R, d.Vd)) * 8);
   }
   L.T = o; o = up(o + RV * 4);
   L.sz = o; o = up(o + static_cast<size_t>(d.R) * d.nstat * 8);
@@ -348,7 +350,8 @@ int dspark_loss_fwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     DSPARK_STAGE(kBiasStats, launch_bias_stats(d.R, d.Vd, d.r, z, Eb, W2, sz, d.nstat, s));
     DSPARK_STAGE(kL1Sweep, launch_lse_rows(d.R, sz, stt, d.nstat, rs.mask, teacher != kNone, rs, s));
     DSPARK_STAGE(kL1Sweep, launch_bias_l1(d.R, d.Vd, d.r, z, Eb, W2, teacher != kNone ? T : nullptr,
-                                          in->target_ids, rs, pl1, ps, s));
+                                          in->target_ids, rs, pl1, ps,
+                                          reinterpret_cast<uint2*>(ws + L.sg), s));
     DSPARK_STAGE(kL1Sweep, launch_bias_l1_finish(d.R, d.Vd, d.r, static_cast<int>(d.bsplits),
                                                  teacher != kNone, pl1, ps, z, Eb, W2,
                                                  in->target_ids, rs, s));
@@ -441,7 +444,7 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
                                    static_cast<const bf16_t*>(in->draft_logits),
                                    d.markov ? static_cast<const bf16_t*>(E) : nullptr,
                                    d.markov ? static_cast<const bf16_t*>(in->markov_w2) : nullptr,
-                                   teacher != kNone ? T : nullptr, in->target_ids, rs,
+                                   reinterpret_cast<const uint2*>(ws + L.sg), in->target_ids, rs,
                                    teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
                                    out->d_draft_logits, ghi, glo, s));
     }
