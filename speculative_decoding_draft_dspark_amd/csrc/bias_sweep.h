@@ -48,8 +48,9 @@ hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int64_t rank, int splits,
                                  RowState rs, hipStream_t s);
 
 // G = g w [ce_a (p - [v = y]) + l1_a p (sign(p - q) - S)] (0 on unsupervised rows):
-// dz in the gradient dtype (grad_dtype 1 = bf16: dz is the bf16 high part),
-// ghi = bf16(G) when dz is fp32, glo = bf16(G - bf16(G)).
+// dz in the gradient dtype, and with fp32 dz (grad_dtype 0) ghi = bf16(G) and,
+// if not null, glo = bf16(G - bf16(G)).  With bf16 dz (grad_dtype 1) dz is
+// bf16(G) itself and ghi, glo must be null.
 // With a teacher, sign(p - q) comes from the bits launch_bias_l1 wrote (T is
 // not read again).
 hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, const bf16_t* z,

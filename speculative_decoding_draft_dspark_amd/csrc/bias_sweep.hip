@@ -15,9 +15,10 @@
 // read from LDS feeds two MFMAs.  The W2 rows of a block are permuted so that
 // lane (g, cl) ends up with the 8 consecutive columns 32 h + 8 g .. + 7 of
 // its row for each block pair h: z (bf16) arrives as one 16-byte load per
-// (h, row block), T (fp32) as two.  Every sweep computes the bias with the
-// same instruction sequence, so all three see the same z'.  A slice is one
-// softmax-statistics tile (64 columns).
+// (h, row block), T (fp32) as two.  z, widened to fp32, is the initial
+// accumulator of the MFMA chains, so they end at z' itself.  Every sweep
+// computes z' with the same instruction sequence, so all three see the same
+// values.  A slice is one softmax-statistics tile (64 columns).
 #include "bias_sweep.h"
 
 #include "common.h"
@@ -125,14 +126,11 @@ struct BiasEngine {
                                                off, 0, 0, 0);
     }
   }
-  // Bias of vocabulary blocks 2 h, 2 h + 1 of the slice in buf for both row
-  // blocks: acc[bb][rb]; four independent MFMA chains, the next k step's W2
-  // fragments read while the current step's MFMAs run.
+  // Adds the bias of vocabulary blocks 2 h, 2 h + 1 of the slice in buf for
+  // both row blocks to acc[bb][rb] (z on entry, so the chains end at z'); four
+  // independent MFMA chains, the next k step's W2 fragments read while the
+  // current step's MFMAs run.
   __device__ __forceinline__ void bias_pair(const u32x4* buf, int h, f32x4_v (&acc)[2][2]) const {
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) acc[bb][rb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
     if (RANK == 0) return;
     const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
     u32x4 w[KS][2];  // fully unrolled: registers, read one k step ahead of their MFMAs
@@ -163,21 +161,16 @@ template <bool LOADT, bool LOADS>
 struct SliceData {
   u32x4 z[2][2];
   u32x4 t[LOADT ? 2 : 1][2][2];  // [h][rb][half]
-  u32x2 sg;                      // [p > q, p < q], bit (2 h + rb) 8 + i
+  u32x2 sg;  // sign(p - q) of block pair h in word h: bits 2 (8 rb + i), +1 / -1 / 0 as 01 / 11 / 00
 };
 
-// z' of the lane's 8 columns (h, rb): z + the bias blocks 2 h (columns
-// 0..3) and 2 h + 1 (columns 4..7).
-__device__ __forceinline__ void zprime8(float (&v)[8], const u32x4& zz, const f32x4_v& b0,
-                                        const f32x4_v& b1) {
-  v[0] = __uint_as_float(zz.x << 16) + b0[0];
-  v[1] = __uint_as_float(zz.x & 0xffff0000u) + b0[1];
-  v[2] = __uint_as_float(zz.y << 16) + b0[2];
-  v[3] = __uint_as_float(zz.y & 0xffff0000u) + b0[3];
-  v[4] = __uint_as_float(zz.z << 16) + b1[0];
-  v[5] = __uint_as_float(zz.z & 0xffff0000u) + b1[1];
-  v[6] = __uint_as_float(zz.w << 16) + b1[2];
-  v[7] = __uint_as_float(zz.w & 0xffff0000u) + b1[3];
+// z of the lane's 8 columns (h, rb) as the accumulators of bias blocks 2 h
+// (columns 0..3) and 2 h + 1 (columns 4..7).
+__device__ __forceinline__ void z_acc(const u32x4& zz, f32x4_v& b0, f32x4_v& b1) {
+  b0 = f32x4_v{__uint_as_float(zz.x << 16), __uint_as_float(zz.x & 0xffff0000u),
+               __uint_as_float(zz.y << 16), __uint_as_float(zz.y & 0xffff0000u)};
+  b1 = f32x4_v{__uint_as_float(zz.z << 16), __uint_as_float(zz.z & 0xffff0000u),
+               __uint_as_float(zz.w << 16), __uint_as_float(zz.w & 0xffff0000u)};
 }
 
 struct SweepParams {
@@ -227,7 +220,7 @@ struct Sweep {
   __amdgpu_buffer_rsrc_t rd, rh, rl;  // dz, G hi, G lo from row r0
   __amdgpu_buffer_rsrc_t rsg;         // the wave's sign words
   double a_l1[2], a_s[2];  // L1 pass accumulators
-  uint32_t wgt, wlt;       // L1 pass: sign words of the slice in progress
+  uint32_t wsg[2];         // L1 pass: sign words of the slice in progress
   float c0[2];             // gradient: g w (ce_a - l1_a S); + / - g w l1_a for sign +1 / -1
 
   __device__ __forceinline__ Sweep(const SweepParams& p, u32x4* rg) : P(p), ring(rg) {
@@ -332,13 +325,17 @@ struct Sweep {
     asm volatile("" : "+s"(cs));
     load(nxt, cs + kLead * kSliceV);
     float zp[2][2][8];  // [h][rb][column]
-    wgt = wlt = 0u;
+    wsg[0] = wsg[1] = 0u;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4_v acc[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) z_acc(cur.z[h][rb], acc[0][rb], acc[1][rb]);
       eng.bias_pair(stage(s), h, acc);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) zprime8(zp[h][rb], cur.z[h][rb], acc[0][rb], acc[1][rb]);
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zp[h][rb][i] = acc[i >> 2][rb][i & 3];
       if (MODE == kL1) l1_work(cs, h, cur, zp[h]);
       if (MODE == kGrad) grad_work(cs, h, cur, zp[h]);
     }
@@ -346,7 +343,7 @@ struct Sweep {
     if (MODE == kL1) {  // every slice's words, stored unconditionally
       const int tn = (static_cast<int>(vb) + cs) / kSliceV;
       const int lane = threadIdx.x & 63;
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{wgt, wlt}, rsg,
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{wsg[0], wsg[1]}, rsg,
                                             static_cast<uint32_t>((tn * 64 + lane) * 8), 0, 0);
     }
   }
@@ -402,8 +399,9 @@ struct Sweep {
   }
 
   // L1 pass on block pair h: sum |p - q| and sum p sign(p - q), and the
-  // signs as bits for the gradient pass: p > q from the sign of q - p, p < q
-  // from the sign of p - q (both +0 on a tie: sign(0) = 0).
+  // signs as 2-bit two's-complement fields for the gradient pass.  sign(p - q)
+  // is the sign bit of q - p minus that of p - q: a tie makes both +0, so
+  // sign(0) = 0.
   __device__ __forceinline__ void l1_work(int cs, int h, const SD& cur, const float (&zh)[2][8]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -416,12 +414,11 @@ struct Sweep {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zh[rb][i], kLog2e, -lz[rb]));
         const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(t, kLog2e, -lt[rb]));
         const float d = p - q, e = q - p;
-        const uint32_t gt = __float_as_uint(e) >> 31, ltb = __float_as_uint(d) >> 31;
-        const int k = (2 * h + rb) * 8 + i;
-        wgt |= gt << k;
-        wlt |= ltb << k;
+        const int sg = static_cast<int>(__float_as_uint(e) >> 31) -
+                       static_cast<int>(__float_as_uint(d) >> 31);
+        wsg[h] |= static_cast<uint32_t>(sg & 3) << (2 * (8 * rb + i));
         s1 += fabsf(d);
-        s2 += gt ? p : (ltb ? -p : 0.f);
+        s2 = __builtin_fmaf(p, static_cast<float>(sg), s2);
       }
       a_l1[rb] += ok ? s1 : 0.f;
       a_s[rb] += ok ? s2 : 0.f;
@@ -440,9 +437,9 @@ struct Sweep {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zh[rb][i], kLog2e, -lz[rb]));
         float v;
         if (TEACHER) {  // g w p [ce_a + l1_a (sign(p - q) - S)], the sign from the L1 pass
-          const int k = (2 * h + rb) * 8 + i;
-          const bool gt = (cur.sg.x >> k) & 1u, ltb = (cur.sg.y >> k) & 1u;
-          v = p * (gt ? c0[rb] + cl1[rb] : (ltb ? c0[rb] - cl1[rb] : c0[rb]));
+          const uint32_t w = h == 0 ? cur.sg.x : cur.sg.y;
+          const int sg = static_cast<int>(w << (30 - 2 * (8 * rb + i))) >> 30;
+          v = p * __builtin_fmaf(cl1[rb], static_cast<float>(sg), c0[rb]);
         } else {
           v = p * cc[rb];
         }
@@ -450,20 +447,15 @@ struct Sweep {
       }
       // cc = 0 on unsupervised rows: G_y -= g w ce_a leaves their zeros
       const int ti = target_in(yl[rb], col);
-      if (ti >= 0) {  // one lane of the row, once per sweep
+      // one lane of the row, once per sweep: a wave-uniform branch, so the
+      // other slices pay no per-element select
+      if (__builtin_amdgcn_ballot_w64(ti >= 0) != 0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) G[i] = i == ti ? G[i] - cc[rb] : G[i];
       }
-      uint32_t hb[8], lb[8];
+      u32x4 hv;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hb[i] = f32_to_bf16(G[i]);
-        lb[i] = f32_to_bf16(G[i] - bf16_to_f32(static_cast<bf16_t>(hb[i])));
-      }
-      const u32x4 hv = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                        hb[6] | (hb[7] << 16)};
-      const u32x4 lv = {lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
-                        lb[6] | (lb[7] << 16)};
+      for (int j = 0; j < 4; ++j) hv[j] = pack_bf16x2(G[2 * j], G[2 * j + 1]);
       const bool ok = rowok[rb] && col < vlen;
       const uint32_t e = ebase[rb] + static_cast<uint32_t>(col);
       if (sizeof(GT) == 2) {
@@ -476,8 +468,15 @@ struct Sweep {
           __builtin_amdgcn_raw_buffer_store_b128(gv, rd, ok ? (e + 4 * q) * 4 : kOOB, 0, 0);
         }
         __builtin_amdgcn_raw_buffer_store_b128(hv, rh, ok ? e * 2 : kOOB, 0, 0);
+        if (P.glo) {  // G - hi, rounded: the second K segment of the weight products
+          u32x4 lv;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            lv[j] = pack_bf16x2(G[2 * j] - __uint_as_float(hv[j] << 16),
+                                G[2 * j + 1] - __uint_as_float(hv[j] & 0xffff0000u));
+          __builtin_amdgcn_raw_buffer_store_b128(lv, rl, ok ? e * 2 : kOOB, 0, 0);
+        }
       }
-      if (P.glo) __builtin_amdgcn_raw_buffer_store_b128(lv, rl, ok ? e * 2 : kOOB, 0, 0);
     }
   }
 
@@ -664,6 +663,7 @@ hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, 
   P.nstat = (V + kSliceV - 1) / kSliceV;
   P.g = g; P.ce_a = ce_a; P.l1_a = l1_a;
   const BiasGrid gr = bias_grid(R, V);
+  if (grad_dtype == 1 && (ghi || glo)) return hipErrorInvalidValue;  // bf16 dz is G itself
   if (grad_dtype == 1)
     return has_teacher ? launch_mode<kGrad, true, bf16_t>(rank, gr, P, s)
                        : launch_mode<kGrad, false, bf16_t>(rank, gr, P, s);

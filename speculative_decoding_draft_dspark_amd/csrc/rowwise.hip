@@ -393,8 +393,8 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 }
 __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
   uint2 u;
-  u.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-  u.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+  u.x = pack_bf16x2(a, b);
+  u.y = pack_bf16x2(c, d);
   *reinterpret_cast<uint2*>(p) = u;
 }
 __device__ __forceinline__ float bf16_round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
