@@ -191,11 +191,13 @@ def main():
     # vocabulary sweeps: algorithmic HBM bytes per (row, column) / average
     # duration.  Stored path: z' and T fp32 in, dz bf16 + G lo bf16 out.
     # Recompute path: z bf16 instead of z' (the bias comes from W2 in L2 and E
-    # in registers, not counted), statistics read z alone.
+    # in registers, not counted); statistics read z alone; the L1 pass reads z
+    # and T and writes sign(p - q) as 2-bit fields (0.25 byte), which the
+    # gradient pass reads with z before writing dz bf16.
     if stored:
         per_elem = (("l1_sweep", 8), ("grad_sweep", 12))
     else:
-        per_elem = (("bias_stats", 2), ("l1_sweep", 6), ("grad_sweep", 10))
+        per_elem = (("bias_stats", 2), ("l1_sweep", 6.25), ("grad_sweep", 4.25))
     sweeps = {}
     for name, bytes_per_elem in per_elem:
         ms = _avg_ms(stages, name, args.steps)

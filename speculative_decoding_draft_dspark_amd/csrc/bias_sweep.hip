@@ -65,6 +65,23 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// Reductions over the lanes l, l ^ 16, l ^ 32, l ^ 48 (a row's four lanes g)
+// with the gfx950 lane swaps: with both operands x, permlane16_swap leaves
+// {x[l], x[l ^ 16]} in its two results and permlane32_swap {x[l], x[l ^ 32]},
+// so one swap and one operation per step, no LDS round trip.
+__device__ __forceinline__ float max_g4(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ uint32_t sum_g4(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = r[0] + r[1];
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return r[0] + r[1];
+}
+
 // Column within the slice of output m (0..15) of vocabulary block b (0..3):
 // lane (g, cl) receives outputs 4 g .. 4 g + 3, i.e. columns
 // 32 (b >> 1) + 8 g + 4 (b & 1) + 0..3.
@@ -201,6 +218,9 @@ struct Sweep {
   static constexpr bool kLoadS = TEACHER && MODE == kGrad;
   using SD = SliceData<kLoadT, kLoadS>;
   static constexpr int kZT = 4 + (kLoadT ? 8 : 0) + (kLoadS ? 1 : 0);  // loads per lane per slice
+  // stores issued unconditionally per slice: the statistics tile, the sign
+  // words, or dz (bf16: one per (h, rb); fp32: two, plus G hi)
+  static constexpr int kST = MODE == kStats ? 1 : (MODE == kL1 ? 1 : (sizeof(GT) == 2 ? 4 : 12));
   // slices of z / T in flight ahead of the one in use: 2 without T, 1 with T
   // (three register sets of z and T would not fit two waves per SIMD)
   static constexpr int kLead = kLoadT ? 1 : 2;
@@ -312,9 +332,13 @@ struct Sweep {
   // count is static.
   __device__ __forceinline__ void step(int s, const SD& cur, SD& nxt) {
     // W2 of slice s landed: it was queued in step s - 3 (the prologue drains
-    // its own), followed by that step's z / T loads and two more steps' DMA
-    // and z / T loads (stores only add to the count)
-    wait_vm<2 * Eng::kPer + 3 * kZT>();
+    // its own), followed by that step's z / T loads and stores and two more
+    // steps' DMA, loads and stores.  The vector memory counter retires loads
+    // and stores in issue order, so counting the stores too leaves them in
+    // flight instead of waiting for their writes every step (the G lo store
+    // is conditional and not counted: the count stays a lower bound).
+    static_assert(2 * Eng::kPer + 3 * kZT + 3 * kST < 64, "vmcnt range");
+    wait_vm<2 * Eng::kPer + 3 * kZT + 3 * kST>();
     lds_sync();  // every wave's W2 slice s is in LDS; slice s - 1's stage is free
     eng.dma(P.W2, col0(s + 3), ve, stage(s + 3));
     // first column of the slice within the range, opaque to the optimizer:
@@ -363,8 +387,7 @@ struct Sweep {
         for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, zp[h][rb][i]);
         mx = ok ? fmaxf(mx, m8) : mx;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = max_g4(mx);
       const float off = fix_exp_offset(mx);
       uint32_t sum = 0;
 #pragma unroll
@@ -376,8 +399,7 @@ struct Sweep {
         sum += ok ? s8 : 0u;
       }
       sum = mx == -INFINITY ? 0u : sum;
-      sum += __shfl_xor(sum, 16, kWave);
-      sum += __shfl_xor(sum, 32, kWave);
+      sum = sum_g4(sum);
       out[rb] = make_float2(mx, fix_to_float(sum));
     }
     // lane g = rb stores row block rb's tile (s < nsl: the tile has columns)

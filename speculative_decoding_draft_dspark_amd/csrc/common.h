@@ -67,15 +67,6 @@ template <> struct Elem<bf16_t> {
 __device__ __forceinline__ float dexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
 __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
-// sign(d) for a difference of two probabilities, as clamp(d 2^126, -1, 1):
-// one multiply and one median, no compare masks.  Exact for d = 0 and for
-// |d| >= 2^-126; a smaller nonzero d needs both probabilities below about
-// 2^-102 (fp32 spacing), where the fraction it returns multiplies a p that
-// small.
-__device__ __forceinline__ float sgn_prob(float d) {
-  return __builtin_amdgcn_fmed3f(d * 0x1p126f, -1.f, 1.f);
-}
-
 // exp(x - m) for x <= m in the fixed point (2^25 scale) of the tile
 // exp-sums, as 2^(x log2 e + 25 - m log2 e) truncated to an integer (one fma,
 // one exp2, one conversion).  At x = m the exponent is 25 plus the rounding
