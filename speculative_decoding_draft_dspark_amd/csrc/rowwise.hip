@@ -746,15 +746,17 @@ __global__ void conf_bwd_partial_kernel(int64_t R, int64_t Hd, int64_t rank, int
   const int64_t r0 = blockIdx.y * rows_per;
   const int64_t r1 = (r0 + rows_per) < R ? (r0 + rows_per) : R;
   if (f > F) return;
+  // rows unrolled with a select for unsupervised ones (no branch), so the
+  // loads of several rows are in flight together; the select follows the
+  // product, so whatever an unsupervised row holds contributes nothing
+  const T* src = f < Hd ? hd + f : (f < F ? E + (f - Hd) : nullptr);
+  const int64_t ld = f < Hd ? Hd : rank;
   float acc = 0.f;
+#pragma unroll 8
   for (int64_t r = r0; r < r1; ++r) {
-    if (!rs.mask[r]) continue;
-    const float dc = g * rs.w[r] * c_a * rs.dcoef[r];
-    float x;
-    if (f < Hd) x = Elem<T>::to_f32(hd[r * Hd + f]);
-    else if (f < F) x = Elem<T>::to_f32(E[r * rank + (f - Hd)]);
-    else x = 1.f;
-    acc += dc * x;
+    const float x = src ? Elem<T>::to_f32(src[r * ld]) : 1.f;
+    const float t = g * rs.w[r] * c_a * rs.dcoef[r] * x;
+    acc += rs.mask[r] ? t : 0.f;
   }
   part[blockIdx.y * (F + 1) + f] = acc;
 }
