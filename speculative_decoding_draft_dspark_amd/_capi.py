@@ -78,6 +78,21 @@ def lib():
     L.dspark_accept_report.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_void_p, C.c_void_p]
     L.dspark_accept_report.restype = C.c_int
+    L.dspark_markov_logits_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int32]
+    L.dspark_markov_logits_workspace_size.restype = C.c_size_t
+    L.dspark_markov_logits.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int32,
+                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                       C.c_void_p]
+    L.dspark_markov_logits.restype = C.c_int
+    L.dspark_confidence_logits_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_int32,
+                                                          C.c_int32]
+    L.dspark_confidence_logits_workspace_size.restype = C.c_size_t
+    L.dspark_confidence_logits.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                           C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    L.dspark_confidence_logits.restype = C.c_int
     L.dspark_status_string.argtypes = [C.c_int]
     L.dspark_status_string.restype = C.c_char_p
     L.dspark_last_hip_error.argtypes = []

@@ -190,6 +190,29 @@ int hip_status(hipError_t e) {
 
 enum Teacher { kNone = 0, kHidden = 1, kAligned = 2 };
 
+// ---- standalone head ops
+// Shape checks shared by the two head ops (the loss's own limits).
+int head_dims(int64_t rows, int64_t vocab, int64_t target_vocab, int64_t rank, int32_t dtype) {
+  if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (rows < 0 || rows > (int64_t{1} << 31) - 1) return DSPARK_ERR_SHAPE;
+  if (vocab < 0 || vocab % 8 || vocab > (int64_t{1} << 26)) return DSPARK_ERR_SHAPE;
+  if (rank < 0 || rank % 8 || rank > 4096) return DSPARK_ERR_SHAPE;
+  if (rank > 0 && target_vocab <= 0) return DSPARK_ERR_SHAPE;
+  return DSPARK_OK;
+}
+struct HeadLayout {
+  size_t E, st, total;
+};
+HeadLayout head_layout(int64_t rows, int64_t vocab, int64_t rank, int32_t dtype) {
+  const size_t esize = dtype == DSPARK_BF16 ? 2 : 4;
+  HeadLayout L{};
+  size_t o = 0;
+  L.E = o; o = up(o + static_cast<size_t>(rows) * rank * esize);
+  L.st = o; o = up(o + static_cast<size_t>(rows) * ((vocab + kStatTile - 1) / kStatTile) * 8);
+  L.total = o;
+  return L;
+}
+
 // ---- per-stage timers (tracing aid)
 enum Stage {
   kPrep, kGather, kLogitsGemm, kBiasStats, kL1Sweep, kFinalize, kReduce, kGradSweep, kOperandPrep,
@@ -616,6 +639,106 @@ int dspark_profile_read(double* ms, int64_t* counts, int n) {
 
 const char* dspark_stage_name(int stage) {
   return (stage >= 0 && stage < kStages) ? kStageNames[stage] : "";
+}
+
+size_t dspark_markov_logits_workspace_size(int64_t rows, int64_t draft_vocab,
+                                           int64_t markov_rank, int32_t dtype) {
+  if (head_dims(rows, draft_vocab, markov_rank > 0 ? 1 : 0, markov_rank, dtype) != DSPARK_OK ||
+      draft_vocab == 0)
+    return 0;
+  return head_layout(rows, draft_vocab, markov_rank, dtype).total;
+}
+
+int dspark_markov_logits(int64_t rows, int64_t draft_vocab, int64_t target_vocab,
+                         int64_t markov_rank, int32_t dtype, const void* draft_logits,
+                         const int32_t* prev_ids, const uint8_t* valid_mask,
+                         const void* markov_w1, const void* markov_w2, float* out,
+                         void* workspace, size_t workspace_bytes, dspark_stream_t stream) {
+  int st = head_dims(rows, draft_vocab, target_vocab, markov_rank, dtype);
+  if (st) return st;
+  if (draft_vocab == 0) return DSPARK_ERR_SHAPE;
+  if (!draft_logits || !out || !workspace) return DSPARK_ERR_NULL;
+  if (markov_rank > 0 && (!prev_ids || !markov_w1 || !markov_w2)) return DSPARK_ERR_NULL;
+  if (misaligned(draft_logits) || misaligned(out) || misaligned(workspace) ||
+      misaligned(prev_ids) || misaligned(markov_w1) || misaligned(markov_w2))
+    return DSPARK_ERR_ALIGN;
+  const HeadLayout L = head_layout(rows, draft_vocab, markov_rank, dtype);
+  if (workspace_bytes < L.total) return DSPARK_ERR_WORKSPACE;
+  if (rows == 0) return DSPARK_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int esize = dtype == DSPARK_BF16 ? 2 : 4;
+  // valid_mask NULL: every slot valid (a ones mask in the statistics area,
+  // which the projection overwrites afterwards)
+  const uint8_t* mask = valid_mask;
+  if (markov_rank > 0) {
+    if (!mask) {
+      DSPARK_TRY(launch_fill_u32(ws + L.st, (rows + 3) / 4, 0x01010101u, s));
+      mask = reinterpret_cast<const uint8_t*>(ws + L.st);
+    }
+    DSPARK_TRY(launch_gather_embed(dtype, rows, markov_rank, target_vocab, prev_ids, mask,
+                                   markov_w1, ws + L.E, s));
+  }
+  // z' = z + E W2^T: the loss's logits projection with z as the epilogue
+  // addend (K = 0 without a Markov head: z' = z)
+  Operand A{}, B{};
+  A.seg[0] = A.seg[1] = ws + L.E; A.kseg = markov_rank;
+  A.kpad = gemm_kpad(markov_rank, esize); A.ld = markov_rank; A.layout = LAYOUT_KC; A.nseg = 1;
+  B.seg[0] = B.seg[1] = markov_w2; B.kseg = markov_rank; B.kpad = A.kpad; B.ld = markov_rank;
+  B.layout = LAYOUT_KC; B.nseg = 1;
+  EpiParams ep{};
+  ep.C = out; ep.ldc = draft_vocab; ep.X = draft_logits; ep.ldx = draft_vocab;
+  ep.stats = reinterpret_cast<float2*>(ws + L.st);
+  ep.nstat = (draft_vocab + kStatTile - 1) / kStatTile;
+  DSPARK_TRY(launch_logits(dtype, rows, draft_vocab, &A, &B, &ep, 1, s));
+  return DSPARK_OK;
+}
+
+size_t dspark_confidence_logits_workspace_size(int64_t rows, int64_t markov_rank,
+                                               int32_t with_markov_conf, int32_t dtype) {
+  if (head_dims(rows, 0, markov_rank > 0 ? 1 : 0, markov_rank, dtype) != DSPARK_OK) return 0;
+  if (with_markov_conf == 0 || markov_rank == 0) return 0;
+  const size_t esize = dtype == DSPARK_BF16 ? 2 : 4;
+  // embeddings, then room for a ones mask when the caller passes none
+  return up(static_cast<size_t>(rows) * markov_rank * esize) + up(static_cast<size_t>(rows) + 3);
+}
+
+int dspark_confidence_logits(int64_t rows, int64_t draft_hidden, int64_t target_vocab,
+                             int64_t markov_rank, int32_t with_markov_conf, int32_t dtype,
+                             const void* hidden, const int32_t* prev_ids,
+                             const uint8_t* valid_mask, const void* markov_w1,
+                             const void* conf_w, const void* conf_b, float* out,
+                             void* workspace, size_t workspace_bytes, dspark_stream_t stream) {
+  const bool wm = with_markov_conf != 0 && markov_rank > 0;
+  int st = head_dims(rows, 0, target_vocab, wm ? markov_rank : 0, dtype);
+  if (st) return st;
+  if (draft_hidden < 1 || draft_hidden > (int64_t{1} << 20)) return DSPARK_ERR_SHAPE;
+  if (!hidden || !conf_w || !conf_b || !out) return DSPARK_ERR_NULL;
+  if (wm && (!prev_ids || !markov_w1 || !workspace)) return DSPARK_ERR_NULL;
+  if (misaligned(hidden) || misaligned(out) || misaligned(prev_ids) || misaligned(markov_w1) ||
+      misaligned(workspace))
+    return DSPARK_ERR_ALIGN;
+  const size_t esize = dtype == DSPARK_BF16 ? 2 : 4;
+  const size_t eb = up(static_cast<size_t>(rows) * markov_rank * esize);
+  if (workspace_bytes < dspark_confidence_logits_workspace_size(rows, markov_rank,
+                                                                with_markov_conf, dtype))
+    return DSPARK_ERR_WORKSPACE;
+  if (rows == 0) return DSPARK_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (wm) {
+    // valid_mask NULL: every slot valid (a ones mask after the embeddings)
+    const uint8_t* mask = valid_mask;
+    if (!mask) {
+      char* mz = static_cast<char*>(workspace) + eb;
+      DSPARK_TRY(launch_fill_u32(mz, (rows + 3) / 4, 0x01010101u, s));
+      mask = reinterpret_cast<const uint8_t*>(mz);
+    }
+    DSPARK_TRY(launch_gather_embed(dtype, rows, markov_rank, target_vocab, prev_ids, mask,
+                                   markov_w1, workspace, s));
+  }
+  DSPARK_TRY(launch_conf_logits(dtype, rows, draft_hidden, wm ? markov_rank : 0, wm ? 1 : 0, hidden,
+                                workspace, conf_w, conf_b, out, s));
+  return DSPARK_OK;
 }
 
 int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,

@@ -30,6 +30,10 @@ hipError_t launch_prep_rows(int64_t R, int K, const uint8_t* eval, const uint8_t
                             uint32_t* flags, hipStream_t s);
 hipError_t launch_gather_embed(int dtype, int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
                                const uint8_t* mask, const void* W1, void* E, hipStream_t s);
+// c_r = W_c . [h_r ; e_r] + b for every row (E unused unless with_markov_conf).
+hipError_t launch_conf_logits(int dtype, int64_t R, int64_t Hd, int64_t rank, int with_markov_conf,
+                              const void* hd, const void* E, const void* Wc, const void* bc,
+                              float* out, hipStream_t s);
 hipError_t launch_l1_sweep(int64_t R, int64_t V, const float* Zp, const float* Tt,
                            const float2* sz, const float2* st, int64_t nstat, const uint8_t* mask,
                            const int32_t* tid, int has_teacher, RowState rs, hipStream_t s);

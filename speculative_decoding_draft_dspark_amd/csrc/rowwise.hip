@@ -219,6 +219,24 @@ hipError_t launch_l1_sweep(int64_t R, int64_t V, const float* Zp, const float* T
 
 // ---------------------------------------------------------------- per-row finalize
 
+// Confidence logit of row r, W_c . [h ; e] + b, by one wave (lane strides,
+// then a fixed butterfly): the loss and the standalone head op share it, so
+// both give the same value for a row.
+template <typename T>
+__device__ __forceinline__ float conf_logit_wave(int64_t r, int64_t Hd, int64_t rank,
+                                                 int with_markov_conf, const T* hd, const T* E,
+                                                 const T* Wc, const T* bc, int lane) {
+  float acc = 0.f;
+  const T* h = hd + r * Hd;
+  for (int64_t i = lane; i < Hd; i += 64) acc += Elem<T>::to_f32(h[i]) * Elem<T>::to_f32(Wc[i]);
+  if (with_markov_conf) {
+    const T* e = E + r * rank;
+    for (int64_t j = lane; j < rank; j += 64)
+      acc += Elem<T>::to_f32(e[j]) * Elem<T>::to_f32(Wc[Hd + j]);
+  }
+  return wave_sumf(acc) + Elem<T>::to_f32(bc[0]);
+}
+
 // One wave per row: confidence logit c = W_c . [h ; e] + b (0 on invalid
 // slots), accept = clamp(1 - L1/2, 0, 1) (1 on invalid slots), BCE(c, accept)
 // with the label held constant, and the outputs the caller asked for.
@@ -232,17 +250,7 @@ __global__ __launch_bounds__(256) void finalize_rows_kernel(
   if (r >= R) return;
   const bool m = rs.mask[r] != 0;
   float c = 0.f;
-  if (m && has_conf) {
-    float acc = 0.f;
-    const T* h = hd + r * Hd;
-    for (int64_t i = lane; i < Hd; i += 64) acc += Elem<T>::to_f32(h[i]) * Elem<T>::to_f32(Wc[i]);
-    if (with_markov_conf) {
-      const T* e = E + r * rank;
-      for (int64_t j = lane; j < rank; j += 64)
-        acc += Elem<T>::to_f32(e[j]) * Elem<T>::to_f32(Wc[Hd + j]);
-    }
-    c = wave_sumf(acc) + Elem<T>::to_f32(bc[0]);
-  }
+  if (m && has_conf) c = conf_logit_wave(r, Hd, rank, with_markov_conf, hd, E, Wc, bc, lane);
   if (lane != 0) return;
   float accept = 1.f, bce = 0.f, ce = 0.f, l1 = 0.f, dco = 0.f;
   if (m) {
@@ -808,6 +816,40 @@ hipError_t launch_conf_bwd(int dtype, int64_t R, int64_t Hd, int64_t rank, int c
   else
     hipLaunchKernelGGL(conf_dh_kernel<float>, g2, dim3(256), 0, s, R, Hd,
                        static_cast<const float*>(Wc), rs, g, c_a, dh);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- head ops
+
+// Standalone confidence head: c_r = W_c . [h_r ; e_r] + b for every row (e
+// is the Markov embedding, zero on invalid slots, when with_markov_conf).
+template <typename T>
+__global__ __launch_bounds__(256) void conf_logits_kernel(int64_t R, int64_t Hd, int64_t rank,
+                                                          int with_markov_conf, const T* hd,
+                                                          const T* E, const T* Wc, const T* bc,
+                                                          float* out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float c = conf_logit_wave(r, Hd, rank, with_markov_conf, hd, E, Wc, bc, lane);
+  if (lane == 0) out[r] = c;
+}
+
+hipError_t launch_conf_logits(int dtype, int64_t R, int64_t Hd, int64_t rank, int with_markov_conf,
+                              const void* hd, const void* E, const void* Wc, const void* bc,
+                              float* out, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>((R + 3) / 4));
+  if (dtype == 1)
+    hipLaunchKernelGGL(conf_logits_kernel<bf16_t>, grid, dim3(256), 0, s, R, Hd, rank,
+                       with_markov_conf, static_cast<const bf16_t*>(hd),
+                       static_cast<const bf16_t*>(E), static_cast<const bf16_t*>(Wc),
+                       static_cast<const bf16_t*>(bc), out);
+  else
+    hipLaunchKernelGGL(conf_logits_kernel<float>, grid, dim3(256), 0, s, R, Hd, rank,
+                       with_markov_conf, static_cast<const float*>(hd),
+                       static_cast<const float*>(E), static_cast<const float*>(Wc),
+                       static_cast<const float*>(bc), out);
   return hipGetLastError();
 }
 

@@ -223,6 +223,60 @@ def dspark_accept_report(accept_rate: torch.Tensor, eval_mask: torch.Tensor,
     return out4
 
 
+def _u8_mask(m: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if m is None:
+        return None
+    return m if m.dtype == torch.uint8 else m.to(torch.uint8)
+
+
+def markov_logits(draft_logits: torch.Tensor, prev_ids: Optional[torch.Tensor] = None,
+                  markov_w1: Optional[torch.Tensor] = None,
+                  markov_w2: Optional[torch.Tensor] = None,
+                  valid_mask: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``dspark_markov_logits``: the Markov head's corrected logits (fp32)
+    z + W2 W1[prev] on valid slots, z elsewhere; no head (W1 None): z."""
+    z = draft_logits.reshape(-1, draft_logits.shape[-1])
+    rows, V = z.shape
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    Vt = 0 if markov_w1 is None else markov_w1.shape[0]
+    dt = _DT[z.dtype]
+    mask = _u8_mask(None if valid_mask is None else valid_mask.reshape(-1))
+    out = torch.empty(rows, V, dtype=torch.float32, device=z.device)
+    nbytes = capi.lib().dspark_markov_logits_workspace_size(rows, V, r, dt)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=z.device)
+    pid = None if prev_ids is None else prev_ids.reshape(-1)
+    st = capi.lib().dspark_markov_logits(rows, V, Vt, r, dt, _ptr(z), _ptr(pid), _ptr(mask),
+                                         _ptr(markov_w1), _ptr(markov_w2), _ptr(out), _ptr(ws),
+                                         nbytes, _stream(stream))
+    capi.check(st, "dspark_markov_logits")
+    return out.reshape(*draft_logits.shape[:-1], V)
+
+
+def confidence_logits(draft_hidden: torch.Tensor, conf_w: torch.Tensor, conf_b: torch.Tensor,
+                      prev_ids: Optional[torch.Tensor] = None,
+                      markov_w1: Optional[torch.Tensor] = None,
+                      valid_mask: Optional[torch.Tensor] = None,
+                      with_markov: bool = False, stream=None) -> torch.Tensor:
+    """``dspark_confidence_logits``: W_c . [h ; W1[prev]] + b per slot (fp32);
+    the embedding is zero on invalid slots and left out unless with_markov."""
+    h = draft_hidden.reshape(-1, draft_hidden.shape[-1])
+    rows, Hd = h.shape
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    Vt = 0 if markov_w1 is None else markov_w1.shape[0]
+    dt = _DT[h.dtype]
+    mask = _u8_mask(None if valid_mask is None else valid_mask.reshape(-1))
+    out = torch.empty(rows, dtype=torch.float32, device=h.device)
+    nbytes = capi.lib().dspark_confidence_logits_workspace_size(rows, r, int(with_markov), dt)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=h.device)
+    pid = None if prev_ids is None else prev_ids.reshape(-1)
+    st = capi.lib().dspark_confidence_logits(rows, Hd, Vt, r, int(with_markov), dt, _ptr(h),
+                                             _ptr(pid), _ptr(mask), _ptr(markov_w1),
+                                             _ptr(conf_w), _ptr(conf_b), _ptr(out), _ptr(ws),
+                                             nbytes, _stream(stream))
+    capi.check(st, "dspark_confidence_logits")
+    return out.reshape(draft_hidden.shape[:-1])
+
+
 def dspark_loss(b: DSparkBatch, hp: HParams = HParams(), **kw):
     """The API page's 3-tuple: (loss numerator, num_tokens, {metric: [num, den]})."""
     f = dspark_loss_fwd(b, hp, **kw)

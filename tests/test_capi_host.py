@@ -137,3 +137,39 @@ def test_missing_library_is_a_loud_error(monkeypatch, tmp_path):
     monkeypatch.setattr(capi, "LIB_PATH", str(tmp_path / "libdspark.so"))
     with pytest.raises(DSparkError):
         capi.lib()
+
+
+def test_head_ops_validation_codes(L):
+    """The standalone head ops reject bad arguments on the host (no HIP call)."""
+    E = {v: k for k, v in capi.STATUS.items()}
+    ok = L.dspark_markov_logits_workspace_size(100, 512, 64, 1)
+    assert ok > 0
+    assert L.dspark_markov_logits_workspace_size(100, 500, 64, 1) == 0   # vocab % 8
+    assert L.dspark_markov_logits_workspace_size(100, 512, 12, 1) == 0   # rank % 8
+    assert L.dspark_markov_logits_workspace_size(100, 512, 64, 7) == 0   # dtype
+    fake = C.c_void_p(4096)  # never dereferenced: every call below fails validation
+    # markov: null output, bad dtype, bad shape, missing Markov weights, short workspace
+    assert L.dspark_markov_logits(100, 512, 600, 64, 1, fake, fake, None, fake, fake, None,
+                                  fake, ok, None) == E["ERR_NULL"]
+    assert L.dspark_markov_logits(100, 512, 600, 64, 5, fake, fake, None, fake, fake, fake,
+                                  fake, ok, None) == E["ERR_DTYPE"]
+    assert L.dspark_markov_logits(100, 510, 600, 64, 1, fake, fake, None, fake, fake, fake,
+                                  fake, ok, None) == E["ERR_SHAPE"]
+    assert L.dspark_markov_logits(100, 512, 0, 64, 1, fake, fake, None, fake, fake, fake,
+                                  fake, ok, None) == E["ERR_SHAPE"]
+    assert L.dspark_markov_logits(100, 512, 600, 64, 1, fake, None, None, fake, fake, fake,
+                                  fake, ok, None) == E["ERR_NULL"]
+    assert L.dspark_markov_logits(100, 512, 600, 64, 1, fake, fake, None, fake, fake, fake,
+                                  fake, ok - 1, None) == E["ERR_WORKSPACE"]
+    assert L.dspark_markov_logits(100, 512, 600, 64, 1, C.c_void_p(4100), fake, None, fake,
+                                  fake, fake, fake, ok, None) == E["ERR_ALIGN"]
+    # confidence: no Markov features need no workspace; with them, the size rule holds
+    assert L.dspark_confidence_logits_workspace_size(100, 64, 0, 1) == 0
+    cw = L.dspark_confidence_logits_workspace_size(100, 64, 1, 1)
+    assert cw >= 100 * 64 * 2 + 100
+    assert L.dspark_confidence_logits(100, 0, 600, 64, 1, 1, fake, fake, None, fake, fake, fake,
+                                      fake, fake, cw, None) == E["ERR_SHAPE"]
+    assert L.dspark_confidence_logits(100, 32, 600, 64, 1, 1, None, fake, None, fake, fake,
+                                      fake, fake, fake, cw, None) == E["ERR_NULL"]
+    assert L.dspark_confidence_logits(100, 32, 600, 64, 1, 1, fake, fake, None, fake, fake,
+                                      fake, fake, fake, cw - 1, None) == E["ERR_WORKSPACE"]

@@ -1,0 +1,118 @@
+"""GPU parity of the standalone head ops (dspark_markov_logits,
+dspark_confidence_logits, through the C ABI) against the oracle's head
+functions: the Markov head's corrected logits z + W2 W1[prev] (zero bias on
+invalid slots) and the confidence head's logit W_c . [h ; e] + b.
+
+The inputs are rounded to the op's dtype before both sides see them, so the
+only differences are the kernels' fp32 accumulation orders: 1e-5 normwise,
+and exact equality wherever the bias is zero.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_draft_dspark_amd import confidence_logits, markov_logits
+from tests.common import oracle_inputs
+from tests.gpu_common import normwise, run_gpu, say, to_np
+from speculative_decoding_draft_dspark_amd import HParams
+from workloads import get_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+HEAD_TOL = 1e-5
+
+
+def _rand(shape, std, dtype, g):
+    return (torch.randn(shape, generator=g, dtype=torch.float64) * std).to(DT[dtype])
+
+
+def _f64(t):
+    return t.to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("dtype,rank", [("bf16", 64), ("bf16", 24), ("f32", 32), ("bf16", 0),
+                                        ("f32", 0)])
+def test_markov_logits_parity(dtype, rank):
+    # rows and vocabulary not multiples of the 256 x 256 tiles (ragged tails);
+    # rank 64 takes the LDS-DMA projection kernel, 24 and fp32 the generic one
+    R, V, Vt = 200, 1000, 777
+    g = torch.Generator().manual_seed(11 + rank)
+    say(f"[heads] markov logits {dtype} R={R} V={V} rank={rank}")
+    z = _rand((R, V), 2.0, dtype, g)
+    prev = torch.randint(0, Vt, (R,), generator=g, dtype=torch.int32)
+    valid = (torch.rand(R, generator=g) > 0.25).to(torch.uint8)
+    W1 = _rand((Vt, rank), 0.5, dtype, g) if rank else None
+    W2 = _rand((V, rank), 0.5, dtype, g) if rank else None
+    out = markov_logits(z.to(DEV), prev.to(DEV), None if W1 is None else W1.to(DEV),
+                        None if W2 is None else W2.to(DEV), valid.to(DEV))
+    got = to_np(out)
+    inp = oracle.Inputs(B=1, N=1, K=R, z=_f64(z), target_ids=np.zeros(R, np.int32),
+                        eval_mask=valid.numpy(), prev_ids=prev.numpy(),
+                        W1=None if W1 is None else _f64(W1), W2=None if W2 is None else _f64(W2))
+    rows = np.arange(R)
+    v = valid.numpy().astype(bool)
+    e = oracle.markov_embedding(inp, rows)
+    if e.shape[1]:
+        e[~v] = 0.0  # the head's bias is zero on invalid slots
+    ref = oracle.draft_logits_corrected(inp, rows, e)
+    err = normwise(got, ref)
+    assert err <= HEAD_TOL, f"z' normwise rel err {err:.3e}"
+    assert np.all(np.abs(got - ref) <= HEAD_TOL * (1.0 + np.abs(ref)))
+    # zero bias: exactly z
+    assert np.array_equal(got[~v], _f64(z)[~v])
+    if rank == 0:
+        assert np.array_equal(got, _f64(z))
+
+
+@pytest.mark.parametrize("dtype,with_markov,masked", [("bf16", True, True), ("bf16", False, True),
+                                                      ("f32", True, False), ("f32", False, True)])
+def test_confidence_logits_parity(dtype, with_markov, masked):
+    R, Hd, r, Vt = 300, 520, 32, 901
+    g = torch.Generator().manual_seed(5 + int(with_markov) + 2 * int(masked))
+    say(f"[heads] confidence logits {dtype} markov={with_markov} masked={masked}")
+    h = _rand((R, Hd), 1.0, dtype, g)
+    W1 = _rand((Vt, r), 0.5, dtype, g)
+    prev = torch.randint(0, Vt, (R,), generator=g, dtype=torch.int32)
+    Wc = _rand((1, Hd + (r if with_markov else 0)), 0.02, dtype, g)
+    bc = _rand((1,), 0.5, dtype, g)
+    valid = (torch.rand(R, generator=g) > 0.3).to(torch.uint8) if masked else None
+    out = confidence_logits(h.to(DEV), Wc.to(DEV), bc.to(DEV), prev.to(DEV), W1.to(DEV),
+                            None if valid is None else valid.to(DEV), with_markov=with_markov)
+    got = to_np(out)
+    v = np.ones(R, bool) if valid is None else valid.numpy().astype(bool)
+    inp = oracle.Inputs(B=1, N=1, K=R, z=np.zeros((R, 8)), target_ids=np.zeros(R, np.int32),
+                        eval_mask=v.astype(np.uint8), prev_ids=prev.numpy(), W1=_f64(W1),
+                        W2=np.zeros((8, r)), h_d=_f64(h), W_c=_f64(Wc), b_c=_f64(bc),
+                        with_markov_conf=with_markov)
+    rows = np.arange(R)
+    e = oracle.markov_embedding(inp, rows)
+    e[~v] = 0.0
+    ref = oracle.confidence_logit(inp, rows, e)
+    err = normwise(got, ref)
+    assert err <= HEAD_TOL, f"conf logit normwise rel err {err:.3e}"
+    assert np.all(np.abs(got - ref) <= 1e-4 * (1.0 + np.abs(ref)))
+
+
+def test_confidence_head_matches_the_loss_logits():
+    """On the loss's supervised slots the head op returns the loss's own
+    confidence logit bit for bit (one shared routine)."""
+    wl = get_workload(1)
+    say(f"[heads] confidence head vs loss on {wl.name}")
+    d = make_inputs(wl, DEV)
+    b, f, _ = run_gpu(d, HParams(), 1.0, bwd=False)
+    inp = oracle_inputs(d)
+    m = oracle.effective_mask(inp.eval_mask, inp.block_keep, inp.B, inp.N, inp.K).astype(bool)
+    mask = torch.from_numpy(m.astype(np.uint8)).to(DEV)
+    c = confidence_logits(d["h_d"], d["W_c"], d["b_c"], d["prev_ids"], d["W1"], mask,
+                          with_markov=bool(d.get("with_markov_conf", True)))
+    terms = f.row_terms
+    assert terms is not None
+    got = c.cpu().numpy()[m]
+    loss_c = terms[:, 3].cpu().numpy()[m]
+    assert np.array_equal(got, loss_c)
