@@ -420,3 +420,67 @@ def test_small_workloads_run_in_oracle(idx):
     assert np.isfinite(fw.loss) and fw.num_tokens == int(fw.m.sum()) > 0
     v = fw.m != 0
     assert np.all(fw.l1[v] <= 2) and np.all(fw.accept[v] >= 0)
+
+
+# --------------------------------------------------------------------------- batch construction
+
+def test_build_blocks_hand_example():
+    """A worked example, written out by hand from the definitions: tokens
+    10..19, loss mask on positions 2..7 and 9, block size 4."""
+    from oracle.batch import build_blocks, anchor_candidates
+    ids = np.arange(10, 20, dtype=np.int32)[None, :]            # position p holds 10 + p
+    lm = np.array([[0, 0, 1, 1, 1, 1, 1, 1, 0, 1]], dtype=np.uint8)
+    # anchors: 2 (full block), 5 (prefix cut at position 8), 1 (anchor not in
+    # the mask: dropped), 7 (first target 8 unsupervised: dropped), 9 (no target)
+    anchors = np.array([[2, 5, 1, 7, 9]], dtype=np.int32)
+    t, p, e, keep = build_blocks(ids, lm, anchors, 4)
+    assert keep.tolist() == [1, 1, 0, 0, 0]
+    # anchor 2: labels at 3..6, previous tokens at 2..5, all supervised
+    assert t[0:4].tolist() == [13, 14, 15, 16]
+    assert p[0:4].tolist() == [12, 13, 14, 15]
+    assert e[0:4].tolist() == [1, 1, 1, 1]
+    # anchor 5: labels at 6..9; position 8 is unsupervised, so slots 2 and 3
+    # (positions 8 and 9) are cut although position 9 itself is supervised
+    assert t[4:8].tolist() == [16, 17, 18, 19]
+    assert p[4:8].tolist() == [15, 16, 17, 18]
+    assert e[4:8].tolist() == [1, 1, 0, 0]
+    # dropped blocks emit zeros
+    assert t[8:].tolist() == [0] * 12 and p[8:].tolist() == [0] * 12 and e[8:].tolist() == [0] * 12
+    assert anchor_candidates(lm)[0].tolist() == [0, 0, 1, 1, 1, 1, 1, 0, 0, 0]
+
+
+def test_build_blocks_sequence_end():
+    """A block running past the end of the sequence (by hand): tokens 10..19,
+    every position supervised, anchor 8, block size 4."""
+    from oracle.batch import build_blocks
+    ids = np.arange(10, 20, dtype=np.int32)[None, :]
+    lm = np.ones((1, 10), dtype=np.uint8)
+    t, p, e, keep = build_blocks(ids, lm, np.array([[8]], dtype=np.int32), 4)
+    assert keep.tolist() == [1]
+    assert t.tolist() == [19, 0, 0, 0]
+    assert p.tolist() == [18, 19, 0, 0]
+    assert e.tolist() == [1, 0, 0, 0]
+
+
+def test_build_blocks_properties():
+    """Shift structure: slot k + 1's previous token is slot k's label; slot 0's
+    previous token is the anchor token; the eval mask is a prefix per block."""
+    from oracle.batch import build_blocks, anchor_candidates
+    rng = np.random.default_rng(3)
+    B, L, N, K = 3, 64, 6, 7
+    ids = rng.integers(0, 5000, (B, L), dtype=np.int32)
+    lm = (rng.random((B, L)) > 0.15).astype(np.uint8)
+    cand = anchor_candidates(lm)
+    anchors = np.stack([rng.choice(np.flatnonzero(cand[b]), N) for b in range(B)]).astype(np.int32)
+    t, p, e, keep = build_blocks(ids, lm, anchors, K)
+    assert keep.all()
+    t, p, e = t.reshape(B, N, K), p.reshape(B, N, K), e.reshape(B, N, K)
+    inside = (anchors[:, :, None] + np.arange(1, K)[None, None, :]) < L
+    assert np.array_equal(np.where(inside, p[:, :, 1:], 0), np.where(inside, t[:, :, :-1], 0))
+    for b in range(B):
+        for n in range(N):
+            a = anchors[b, n]
+            assert p[b, n, 0] == ids[b, a]
+            assert e[b, n, 0] == 1                    # the first target is valid by construction
+            run = np.cumprod(e[b, n])
+            assert np.array_equal(run, e[b, n])       # a contiguous prefix
