@@ -145,6 +145,57 @@ def _copy_probe(nbytes: int, reps: int = 3):
     print(json.dumps({"copy_probe_bytes": n * 4, "reps": reps}), flush=True)
 
 
+def _side_ops(args, reps: int = 20):
+    """Times the standalone ops beside the loss (head ops at the large-batch
+    shapes, batch construction for its rows) and prints one JSON line; not the
+    benchmark line."""
+    import torch
+
+    from speculative_decoding_draft_dspark_amd import (_capi, build_blocks, confidence_logits,
+                                                       markov_logits)
+    from workloads import get_workload, make_inputs
+
+    _capi.lib()
+    wl = get_workload(args.workload)
+    d = make_inputs(wl, "cuda:0")
+    R, V, r, Hd = wl.R, wl.Vd, wl.r, wl.Hd
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    L = 4096
+    ids = torch.randint(0, wl.Vt, (wl.B, L), device="cuda:0", dtype=torch.int32, generator=g)
+    lm = torch.ones(wl.B, L, device="cuda:0", dtype=torch.uint8)
+    anchors = torch.randint(0, L - 1, (wl.B, wl.N), device="cuda:0", dtype=torch.int32,
+                            generator=g)
+    valid = d["eval_mask"]
+    ops = {
+        "markov_logits": (lambda: markov_logits(d["z"], d["prev_ids"], d["W1"], d["W2"], valid),
+                          {"flops": 2.0 * R * V * r, "bytes": R * V * (2 + 4)}),
+        "confidence_logits": (lambda: confidence_logits(d["h_d"], d["W_c"], d["b_c"], d["prev_ids"],
+                                                        d["W1"], valid, with_markov=True),
+                              {"bytes": R * (Hd + r) * 2}),
+        "build_blocks": (lambda: build_blocks(ids, lm, anchors, wl.K, with_candidates=True),
+                         {"bytes": wl.B * L * 6 + R * 10}),
+    }
+    res = {}
+    for name, (fn, work) in ops.items():
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        e = {"avg_ms": round(ms, 4)}
+        if "flops" in work:
+            e["TFLOP/s"] = round(work["flops"] / (ms * 1e-3) / 1e12, 1)
+        e["GB/s"] = round(work["bytes"] / (ms * 1e-3) / 1e9, 1)
+        res[name] = e
+    print(json.dumps({"side_ops": res, "workload": wl.name, "reps": reps,
+                      "note": "host-side allocation of outputs included"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +207,8 @@ def main():
     ap.add_argument("--store-draft-logits", action="store_true",
                     help="DSPARK_OPT_STORE_DRAFT_LOGITS: materialise the fp32 corrected draft "
                          "logits instead of recomputing the Markov bias in each sweep")
+    ap.add_argument("--side-ops", action="store_true",
+                    help="only time the standalone head ops and batch construction")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (rocprofv3 byte-counter calibration)")
     args = ap.parse_args()
@@ -167,6 +220,9 @@ def main():
 
     if args.copy_probe:
         _copy_probe(args.copy_probe)
+        return
+    if args.side_ops:
+        _side_ops(args)
         return
     wl, elapsed, stages = _gpu_leg(args)
     R, V, H, r = wl.R, wl.Vd, wl.H, wl.r

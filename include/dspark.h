@@ -230,6 +230,29 @@ int dspark_confidence_logits(int64_t rows, int64_t draft_hidden, int64_t target_
                              const void *conf_w, const void *conf_b, float *out,
                              void *workspace, size_t workspace_bytes, dspark_stream_t stream);
 
+/* ---- batch construction (the step before the loss) --------------------------
+ * TorchSpec pull request #132, PR description: labels are the next tokens
+ * (slot k of a block predicts anchor + k + 1, every slot supervised), the eval
+ * mask is the contiguous supervised prefix (cumprod), the Markov previous
+ * token is anchor-seeded, and an anchor needs both itself and its first
+ * target to be valid.  "Valid" is the loss mask here: an anchor a is kept when
+ * 0 <= a, a + 1 < seq_len and loss_mask[a], loss_mask[a + 1] are nonzero.
+ * Inputs: input_ids [batch, seq_len] int32, loss_mask [batch, seq_len] (nonzero
+ * = supervised position), anchors [batch, num_blocks] int32 (the caller's
+ * random draws, e.g. from anchor_ok).  Outputs for row r = (b num_blocks + n)
+ * block_size + k: target_ids[r] = input_ids[b, a + k + 1], prev_ids[r] =
+ * input_ids[b, a + k] (0 past the end of the sequence), eval_mask[r] = product
+ * of loss_mask over positions a + 1 .. a + k + 1 (0 past the end);
+ * block_keep[b num_blocks + n]; a dropped block's rows are all 0.
+ * anchor_ok [batch, seq_len] (may be NULL): 1 where an anchor may be drawn.
+ * The outputs feed dspark_loss_fwd directly.  Errors: DSPARK_ERR_NULL,
+ * _SHAPE (a size < 1 or beyond 2^31 rows), _HIP.  Asynchronous on `stream`. */
+int dspark_build_blocks(int64_t batch, int64_t seq_len, int64_t num_blocks, int64_t block_size,
+                        const int32_t *input_ids, const uint8_t *loss_mask,
+                        const int32_t *anchors, int32_t *target_ids, int32_t *prev_ids,
+                        uint8_t *eval_mask, uint8_t *block_keep, uint8_t *anchor_ok,
+                        dspark_stream_t stream);
+
 const char *dspark_status_string(int status);
 const char *dspark_last_hip_error(void);
 

@@ -93,6 +93,9 @@ def lib():
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                            C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     L.dspark_confidence_logits.restype = C.c_int
+    L.dspark_build_blocks.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int64] + \
+        [C.c_void_p] * 9
+    L.dspark_build_blocks.restype = C.c_int
     L.dspark_status_string.argtypes = [C.c_int]
     L.dspark_status_string.restype = C.c_char_p
     L.dspark_last_hip_error.argtypes = []

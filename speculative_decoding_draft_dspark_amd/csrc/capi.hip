@@ -741,6 +741,24 @@ int dspark_confidence_logits(int64_t rows, int64_t draft_hidden, int64_t target_
   return DSPARK_OK;
 }
 
+int dspark_build_blocks(int64_t batch, int64_t seq_len, int64_t num_blocks, int64_t block_size,
+                        const int32_t* input_ids, const uint8_t* loss_mask,
+                        const int32_t* anchors, int32_t* target_ids, int32_t* prev_ids,
+                        uint8_t* eval_mask, uint8_t* block_keep, uint8_t* anchor_ok,
+                        dspark_stream_t stream) {
+  if (!input_ids || !loss_mask || !anchors || !target_ids || !prev_ids || !eval_mask ||
+      !block_keep)
+    return DSPARK_ERR_NULL;
+  if (batch < 1 || seq_len < 1 || num_blocks < 1 || block_size < 1 || block_size > 4096)
+    return DSPARK_ERR_SHAPE;
+  if (batch * num_blocks > (int64_t{1} << 31) / block_size || batch > (int64_t{1} << 40) / seq_len)
+    return DSPARK_ERR_SHAPE;
+  return hip_status(launch_build_blocks(batch, seq_len, num_blocks, static_cast<int>(block_size),
+                                        input_ids, loss_mask, anchors, target_ids, prev_ids,
+                                        eval_mask, block_keep, anchor_ok,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,
                          const float* accept_rate, const uint8_t* eval_mask,
                          const uint8_t* block_keep_mask, double* out4, dspark_stream_t stream) {

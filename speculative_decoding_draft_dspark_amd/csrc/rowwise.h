@@ -30,6 +30,13 @@ hipError_t launch_prep_rows(int64_t R, int K, const uint8_t* eval, const uint8_t
                             uint32_t* flags, hipStream_t s);
 hipError_t launch_gather_embed(int dtype, int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
                                const uint8_t* mask, const void* W1, void* E, hipStream_t s);
+// Loss rows of sampled anchors [B, N] over sequences [B, L] (labels, previous
+// tokens, contiguous eval mask, block keep) and, if cand is not null, the
+// anchor candidates [B, L].
+hipError_t launch_build_blocks(int64_t B, int64_t L, int64_t N, int K, const int32_t* ids,
+                               const uint8_t* lm, const int32_t* anchors, int32_t* target,
+                               int32_t* prev, uint8_t* evalm, uint8_t* keep, uint8_t* cand,
+                               hipStream_t s);
 // c_r = W_c . [h_r ; e_r] + b for every row (E unused unless with_markov_conf).
 hipError_t launch_conf_logits(int dtype, int64_t R, int64_t Hd, int64_t rank, int with_markov_conf,
                               const void* hd, const void* E, const void* Wc, const void* bc,

@@ -835,6 +835,71 @@ __global__ __launch_bounds__(256) void conf_logits_kernel(int64_t R, int64_t Hd,
   if (lane == 0) out[r] = c;
 }
 
+// ---------------------------------------------------------------- batch construction
+
+// One thread per (sequence b, anchor n): the block's K rows.  Slot k is
+// labelled by the token at a + k + 1 and its previous token is the one at
+// a + k (slot 0: the anchor); the eval mask is the running product of the
+// loss mask over the labels; a block whose anchor or first target is not in
+// the loss mask (or out of range) is dropped and emits zeros.
+__global__ void build_blocks_kernel(int64_t B, int64_t L, int64_t N, int K, const int32_t* ids,
+                                    const uint8_t* lm, const int32_t* anchors, int32_t* target,
+                                    int32_t* prev, uint8_t* evalm, uint8_t* keep) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= B * N) return;
+  const int64_t b = i / N;
+  const int64_t a = anchors[i];
+  const int32_t* row = ids + b * L;
+  const uint8_t* m = lm + b * L;
+  const bool ok = a >= 0 && a + 1 < L && m[a] != 0 && m[a + 1] != 0;
+  keep[i] = ok ? 1 : 0;
+  int run = 1;
+  for (int k = 0; k < K; ++k) {
+    const int64_t r = i * K + k;
+    int32_t t = 0, p = 0;
+    uint8_t e = 0;
+    if (ok) {
+      const int64_t pos = a + k + 1;
+      if (a + k < L) p = row[a + k];
+      if (pos < L) {
+        t = row[pos];
+        run &= m[pos] != 0 ? 1 : 0;
+      } else {
+        run = 0;
+      }
+      e = static_cast<uint8_t>(run);
+    }
+    target[r] = t;
+    prev[r] = p;
+    evalm[r] = e;
+  }
+}
+
+// Anchor candidates: position a of sequence b when a and a + 1 are both in
+// the loss mask.
+__global__ void anchor_candidates_kernel(int64_t B, int64_t L, const uint8_t* lm, uint8_t* out) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= B * L) return;
+  const int64_t a = i % L;
+  out[i] = (a + 1 < L && lm[i] != 0 && lm[i + 1] != 0) ? 1 : 0;
+}
+
+hipError_t launch_build_blocks(int64_t B, int64_t L, int64_t N, int K, const int32_t* ids,
+                               const uint8_t* lm, const int32_t* anchors, int32_t* target,
+                               int32_t* prev, uint8_t* evalm, uint8_t* keep, uint8_t* cand,
+                               hipStream_t s) {
+  if (B * N > 0) {
+    hipLaunchKernelGGL(build_blocks_kernel, dim3(static_cast<uint32_t>((B * N + 255) / 256)),
+                       dim3(256), 0, s, B, L, N, K, ids, lm, anchors, target, prev, evalm, keep);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (cand && B * L > 0)
+    hipLaunchKernelGGL(anchor_candidates_kernel, dim3(static_cast<uint32_t>((B * L + 255) / 256)),
+                       dim3(256), 0, s, B, L, lm, cand);
+  return hipGetLastError();
+}
+
 hipError_t launch_conf_logits(int dtype, int64_t R, int64_t Hd, int64_t rank, int with_markov_conf,
                               const void* hd, const void* E, const void* Wc, const void* bc,
                               float* out, hipStream_t s) {

@@ -223,6 +223,34 @@ def dspark_accept_report(accept_rate: torch.Tensor, eval_mask: torch.Tensor,
     return out4
 
 
+def build_blocks(input_ids: torch.Tensor, loss_mask: torch.Tensor, anchors: torch.Tensor,
+                 block_size: int, with_candidates: bool = False, stream=None) -> dict:
+    """``dspark_build_blocks``: the loss rows of sampled anchors.
+
+    input_ids [B, L] int32, loss_mask [B, L], anchors [B, N] int32 ->
+    {"target_ids", "prev_ids" [B*N*K] int32, "eval_mask" [B*N*K] uint8,
+    "block_keep" [B*N] uint8} (+ "anchor_ok" [B, L] uint8 when asked)."""
+    B, L = input_ids.shape
+    N = anchors.shape[1]
+    R = B * N * block_size
+    dev = input_ids.device
+    ids = input_ids.to(torch.int32).contiguous()
+    lm = _u8_mask(loss_mask).contiguous()
+    anc = anchors.to(torch.int32).contiguous()
+    out = {"target_ids": torch.empty(R, dtype=torch.int32, device=dev),
+           "prev_ids": torch.empty(R, dtype=torch.int32, device=dev),
+           "eval_mask": torch.empty(R, dtype=torch.uint8, device=dev),
+           "block_keep": torch.empty(B * N, dtype=torch.uint8, device=dev)}
+    if with_candidates:
+        out["anchor_ok"] = torch.empty(B, L, dtype=torch.uint8, device=dev)
+    st = capi.lib().dspark_build_blocks(B, L, N, block_size, _ptr(ids), _ptr(lm), _ptr(anc),
+                                        _ptr(out["target_ids"]), _ptr(out["prev_ids"]),
+                                        _ptr(out["eval_mask"]), _ptr(out["block_keep"]),
+                                        _ptr(out.get("anchor_ok")), _stream(stream))
+    capi.check(st, "dspark_build_blocks")
+    return out
+
+
 def _u8_mask(m: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     if m is None:
         return None

@@ -173,3 +173,13 @@ def test_head_ops_validation_codes(L):
                                       fake, fake, fake, cw, None) == E["ERR_NULL"]
     assert L.dspark_confidence_logits(100, 32, 600, 64, 1, 1, fake, fake, None, fake, fake,
                                       fake, fake, fake, cw - 1, None) == E["ERR_WORKSPACE"]
+
+
+def test_build_blocks_validation_codes(L):
+    E = {v: k for k, v in capi.STATUS.items()}
+    fake = C.c_void_p(4096)  # never dereferenced: every call below fails validation
+    args = [fake] * 7
+    assert L.dspark_build_blocks(2, 64, 4, 7, None, *args[:6], None, None) == E["ERR_NULL"]
+    assert L.dspark_build_blocks(2, 64, 4, 0, *args, None, None) == E["ERR_SHAPE"]
+    assert L.dspark_build_blocks(0, 64, 4, 7, *args, None, None) == E["ERR_SHAPE"]
+    assert L.dspark_build_blocks(2, 64, 1 << 40, 7, *args, None, None) == E["ERR_SHAPE"]
