@@ -484,3 +484,55 @@ def test_build_blocks_properties():
             assert e[b, n, 0] == 1                    # the first target is valid by construction
             run = np.cumprod(e[b, n])
             assert np.array_equal(run, e[b, n])       # a contiguous prefix
+
+
+# --------------------------------------------------------------------------- vocabulary shards
+
+@pytest.mark.parametrize("cuts", [(0, 64, 128), (0, 40, 72, 128), (0, 8, 16, 24, 128)])
+def test_vocab_shards_merge_to_the_unsplit_loss(cuts):
+    """Splitting the draft vocabulary into column ranges and merging the
+    exchanged partials reproduces the unsplit loss and gradient (fp64, to
+    rounding): lse, L1, S, CE per row and every dz column."""
+    from oracle import shard
+    inp = tiny_inputs(V=128, H=16, r=8, N=3, seed=21)
+    hp = oracle.HParams()
+    fw = oracle.forward(inp, hp)
+    gr = oracle.backward(inp, hp, grad_scale=0.5)
+    bounds = list(zip(cuts[:-1], cuts[1:]))
+    lse = shard.merge_stats([shard.shard_stats(inp, a, b) for a, b in bounds])
+    m = fw.m != 0
+    assert np.allclose(lse[m, 0], fw.lse_z[m], rtol=0, atol=1e-12)
+    assert np.allclose(lse[m, 1], fw.lse_t[m], rtol=0, atol=1e-12)
+    terms = sum(shard.shard_terms(inp, a, b, lse) for a, b in bounds)
+    assert np.allclose(terms[m, 0], fw.l1[m], atol=1e-12)
+    assert np.allclose(terms[m, 1], fw.S[m], atol=1e-12)
+    assert np.allclose(lse[m, 0] - terms[m, 2], fw.ce[m], atol=1e-12)
+    S = terms[:, 1]
+    parts = [shard.shard_grad(inp, hp, a, b, lse, S, grad_scale=0.5) for a, b in bounds]
+    dz = np.concatenate([p[0] for p in parts], axis=1)
+    assert np.allclose(dz, gr.dz, rtol=0, atol=1e-14)
+    dW2 = np.concatenate([p[2] for p in parts], axis=0)
+    assert np.allclose(dW2, gr.dW2, rtol=0, atol=1e-13)
+    # dE summed over shards plus the confidence term once gives dW1
+    dE = sum(p[1] for p in parts)
+    dW1 = np.zeros_like(gr.dW1)
+    Hd = inp.h_d.shape[1]
+    Wc = inp.W_c.reshape(-1)
+    rows = np.nonzero(m)[0]
+    dec = oracle.decay_weights(inp.K, hp.loss_decay_gamma)
+    wr = dec[rows % inp.K]
+    dc = 0.5 * wr * hp.confidence_alpha * (oracle.dspark_oracle.sigmoid(fw.conf_logit[rows]) -
+                                           fw.accept[rows])
+    dE[rows] += dc[:, None] * Wc[None, Hd:]
+    np.add.at(dW1, inp.prev_ids[rows].astype(np.int64), dE[rows])
+    assert np.allclose(dW1, gr.dW1, rtol=0, atol=1e-13)
+
+
+def test_vocab_shard_owner_of_the_target_is_unique():
+    from oracle import shard
+    inp = tiny_inputs(V=64, H=16, r=8, N=2, seed=5)
+    lse = shard.merge_stats([shard.shard_stats(inp, 0, 64)])
+    parts = [shard.shard_terms(inp, a, b, lse) for a, b in ((0, 16), (16, 48), (48, 64))]
+    owned = np.stack([p[:, 2] != 0 for p in parts])
+    m = oracle.effective_mask(inp.eval_mask, inp.block_keep, inp.B, inp.N, inp.K) != 0
+    assert np.all(owned[:, m].sum(axis=0) == 1)
