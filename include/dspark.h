@@ -191,9 +191,10 @@ int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,
  * loss's own kernels and parameter layouts.  All pointers are device memory;
  * rows are [rows, ...] row-major; dtype (DSPARK_F32 / DSPARK_BF16) is the type
  * of every float input; outputs are fp32 and overwritten.  valid_mask [rows]
- * (nonzero = valid slot) may be NULL (every slot valid).  prev_ids [rows] index
- * markov_w1 [target_vocab, markov_rank]; an id outside [0, target_vocab) on a
- * valid slot gives a zero embedding (the loss flags it; these ops do not).
+ * (nonzero = valid slot) may be NULL (every slot valid); both ops return zero
+ * on invalid slots.  prev_ids [rows] index markov_w1 [target_vocab,
+ * markov_rank]; an id outside [0, target_vocab) on a valid slot gives a zero
+ * embedding (the loss flags it; these ops do not).
  * Errors: DSPARK_ERR_NULL, _SHAPE (a size < 0, a vocabulary or rank that is not
  * a multiple of 8, draft_hidden < 1), _DTYPE, _ALIGN (16 bytes),
  * _WORKSPACE, _HIP.  Asynchronous on `stream`. */
@@ -203,22 +204,23 @@ int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,
 size_t dspark_markov_logits_workspace_size(int64_t rows, int64_t draft_vocab,
                                            int64_t markov_rank, int32_t dtype);
 
-/* Markov head: out [rows, draft_vocab] fp32 = z + W2 e with e = W1[prev] on
- * valid slots and e = 0 on the others (the bias is zero there; [HEADS] "Inputs
- * and Outputs"; TorchSpec pull request #132, "Testing": bias == W2(W1[prev])).
- * markov_rank 0: out = z.  z is draft_logits [rows, draft_vocab]. */
+/* Markov head: out [rows, draft_vocab] fp32 = z + W2 W1[prev] on valid slots
+ * and 0 on the others ([HEADS] "Inputs and Outputs": the bias is added on
+ * valid slots and both heads return zero for invalid ones; TorchSpec pull
+ * request #132, "Testing": bias == W2(W1[prev])).  markov_rank 0: out = z on
+ * valid slots.  z is draft_logits [rows, draft_vocab]. */
 int dspark_markov_logits(int64_t rows, int64_t draft_vocab, int64_t target_vocab,
                          int64_t markov_rank, int32_t dtype, const void *draft_logits,
                          const int32_t *prev_ids, const uint8_t *valid_mask,
                          const void *markov_w1, const void *markov_w2, float *out,
                          void *workspace, size_t workspace_bytes, dspark_stream_t stream);
 
-/* Confidence head: out [rows] fp32 = W_c . [h ; e] + b for every row, with
- * h = draft_hidden [rows, draft_hidden] and, when with_markov_conf, e the
- * Markov embedding as above (zero on invalid slots); conf_w is [1, draft_hidden
- * (+ markov_rank)], conf_b [1] ([HEADS] "Checkpoint Contract"; concatenation
- * order [hidden ; embedding]).  The loss computes the same value on valid
- * slots (and uses 0 on invalid ones).  workspace: at least
+/* Confidence head: out [rows] fp32 = W_c . [h ; e] + b on valid slots and 0
+ * on the others, with h = draft_hidden [rows, draft_hidden] and, when
+ * with_markov_conf, e = W1[prev]; conf_w is [1, draft_hidden (+ markov_rank)],
+ * conf_b [1] ([HEADS] "Checkpoint Contract"; concatenation order [hidden ;
+ * embedding]).  With the loss's effective mask as valid_mask this is the
+ * loss's own confidence logit, bit for bit.  workspace: at least
  * dspark_confidence_logits_workspace_size() bytes (0 without Markov features,
  * then it may be NULL). */
 size_t dspark_confidence_logits_workspace_size(int64_t rows, int64_t markov_rank,

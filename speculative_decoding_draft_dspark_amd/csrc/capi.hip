@@ -691,6 +691,8 @@ int dspark_markov_logits(int64_t rows, int64_t draft_vocab, int64_t target_vocab
   ep.stats = reinterpret_cast<float2*>(ws + L.st);
   ep.nstat = (draft_vocab + kStatTile - 1) / kStatTile;
   DSPARK_TRY(launch_logits(dtype, rows, draft_vocab, &A, &B, &ep, 1, s));
+  // the head returns zero on invalid slots
+  if (valid_mask) DSPARK_TRY(launch_zero_masked_rows(rows, draft_vocab, valid_mask, out, s));
   return DSPARK_OK;
 }
 
@@ -737,7 +739,7 @@ int dspark_confidence_logits(int64_t rows, int64_t draft_hidden, int64_t target_
                                    markov_w1, workspace, s));
   }
   DSPARK_TRY(launch_conf_logits(dtype, rows, draft_hidden, wm ? markov_rank : 0, wm ? 1 : 0, hidden,
-                                workspace, conf_w, conf_b, out, s));
+                                workspace, conf_w, conf_b, valid_mask, out, s));
   return DSPARK_OK;
 }
 

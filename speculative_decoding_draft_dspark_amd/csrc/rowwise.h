@@ -37,10 +37,14 @@ hipError_t launch_build_blocks(int64_t B, int64_t L, int64_t N, int K, const int
                                const uint8_t* lm, const int32_t* anchors, int32_t* target,
                                int32_t* prev, uint8_t* evalm, uint8_t* keep, uint8_t* cand,
                                hipStream_t s);
-// c_r = W_c . [h_r ; e_r] + b for every row (E unused unless with_markov_conf).
+// c_r = W_c . [h_r ; e_r] + b on rows with mask[r] != 0 (every row if mask is
+// null), 0 elsewhere (E unused unless with_markov_conf).
 hipError_t launch_conf_logits(int dtype, int64_t R, int64_t Hd, int64_t rank, int with_markov_conf,
                               const void* hd, const void* E, const void* Wc, const void* bc,
-                              float* out, hipStream_t s);
+                              const uint8_t* mask, float* out, hipStream_t s);
+// Zeroes the rows r of out [R, N] (fp32) where mask[r] == 0.
+hipError_t launch_zero_masked_rows(int64_t R, int64_t N, const uint8_t* mask, float* out,
+                                   hipStream_t s);
 hipError_t launch_l1_sweep(int64_t R, int64_t V, const float* Zp, const float* Tt,
                            const float2* sz, const float2* st, int64_t nstat, const uint8_t* mask,
                            const int32_t* tid, int has_teacher, RowState rs, hipStream_t s);

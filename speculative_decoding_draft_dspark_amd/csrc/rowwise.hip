@@ -819,22 +819,6 @@ hipError_t launch_conf_bwd(int dtype, int64_t R, int64_t Hd, int64_t rank, int c
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- head ops
-
-// Standalone confidence head: c_r = W_c . [h_r ; e_r] + b for every row (e
-// is the Markov embedding, zero on invalid slots, when with_markov_conf).
-template <typename T>
-__global__ __launch_bounds__(256) void conf_logits_kernel(int64_t R, int64_t Hd, int64_t rank,
-                                                          int with_markov_conf, const T* hd,
-                                                          const T* E, const T* Wc, const T* bc,
-                                                          float* out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;
-  const float c = conf_logit_wave(r, Hd, rank, with_markov_conf, hd, E, Wc, bc, lane);
-  if (lane == 0) out[r] = c;
-}
-
 // ---------------------------------------------------------------- batch construction
 
 // One thread per (sequence b, anchor n): the block's K rows.  Slot k is
@@ -900,21 +884,59 @@ hipError_t launch_build_blocks(int64_t B, int64_t L, int64_t N, int K, const int
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- head ops
+
+// Standalone confidence head: c_r = W_c . [h_r ; e_r] + b on valid slots (e
+// is the Markov embedding, when with_markov_conf), 0 on the others.
+template <typename T>
+__global__ __launch_bounds__(256) void conf_logits_kernel(int64_t R, int64_t Hd, int64_t rank,
+                                                          int with_markov_conf, const T* hd,
+                                                          const T* E, const T* Wc, const T* bc,
+                                                          const uint8_t* mask, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  if (mask && mask[r] == 0) {
+    if (lane == 0) out[r] = 0.f;
+    return;
+  }
+  const float c = conf_logit_wave(r, Hd, rank, with_markov_conf, hd, E, Wc, bc, lane);
+  if (lane == 0) out[r] = c;
+}
+
 hipError_t launch_conf_logits(int dtype, int64_t R, int64_t Hd, int64_t rank, int with_markov_conf,
                               const void* hd, const void* E, const void* Wc, const void* bc,
-                              float* out, hipStream_t s) {
+                              const uint8_t* mask, float* out, hipStream_t s) {
   if (R <= 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>((R + 3) / 4));
   if (dtype == 1)
     hipLaunchKernelGGL(conf_logits_kernel<bf16_t>, grid, dim3(256), 0, s, R, Hd, rank,
                        with_markov_conf, static_cast<const bf16_t*>(hd),
                        static_cast<const bf16_t*>(E), static_cast<const bf16_t*>(Wc),
-                       static_cast<const bf16_t*>(bc), out);
+                       static_cast<const bf16_t*>(bc), mask, out);
   else
     hipLaunchKernelGGL(conf_logits_kernel<float>, grid, dim3(256), 0, s, R, Hd, rank,
                        with_markov_conf, static_cast<const float*>(hd),
                        static_cast<const float*>(E), static_cast<const float*>(Wc),
-                       static_cast<const float*>(bc), out);
+                       static_cast<const float*>(bc), mask, out);
+  return hipGetLastError();
+}
+
+// Rows r with mask[r] == 0 of an [R, N] fp32 array set to zero (one
+// workgroup per row; valid rows untouched).
+__global__ __launch_bounds__(256) void zero_masked_rows_kernel(int64_t N, const uint8_t* mask,
+                                                               float* out) {
+  const int64_t r = blockIdx.x;
+  if (mask[r] != 0) return;
+  float* row = out + r * N;
+  for (int64_t i = threadIdx.x; i < N; i += blockDim.x) row[i] = 0.f;
+}
+
+hipError_t launch_zero_masked_rows(int64_t R, int64_t N, const uint8_t* mask, float* out,
+                                   hipStream_t s) {
+  if (R <= 0 || N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_masked_rows_kernel, dim3(static_cast<uint32_t>(R)), dim3(256), 0, s, N,
+                     mask, out);
   return hipGetLastError();
 }
 
