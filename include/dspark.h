@@ -255,6 +255,74 @@ int dspark_build_blocks(int64_t batch, int64_t seq_len, int64_t num_blocks, int6
                         uint8_t *eval_mask, uint8_t *block_keep, uint8_t *anchor_ok,
                         dspark_stream_t stream);
 
+/* ---- vocabulary shards (tensor-parallel split of the draft vocabulary) -----
+ * NeMo-RL "DSpark Auxiliary Heads" (Markov head) and the loss section of the
+ * DSpark page: every vocabulary term of the loss is a sum over columns, and a
+ * softmax's log-sum-exp is the log-sum-exp of per-part log-sum-exps, so a
+ * caller holding columns [v0, v0 + draft_vocab) of draft_logits,
+ * aligned_target_logits / lm_head and markov_w2 computes partials that merge
+ * into the unsplit loss exactly (up to rounding).  `shape` describes the
+ * shard: draft_vocab is the shard's width; target_ids are shard-local
+ * (global id - v0), so an id outside [0, draft_vocab) belongs to another
+ * shard (each supervised target must fall in exactly one shard).  Every other
+ * input (masks, prev_ids, markov_w1, confidence head) is the same on every
+ * shard.  The shape must take the bias sweeps: bf16, markov_rank in
+ * {0, 32, 64, 128, 256}, R and draft_vocab multiples of 32 with a Markov head,
+ * options without DSPARK_OPT_STORE_DRAFT_LOGITS; else DSPARK_ERR_SHAPE.  The
+ * workspace is dspark_workspace_size(shape), one per shard, kept from the
+ * first call to the last.  Order per step, with the collectives between:
+ *   shard_fwd_stats -> lse parts [G, R, 2] gathered -> shard_merge_lse ->
+ *   shard_fwd_terms -> terms [R, 3] summed over shards -> shard_fwd_finish ->
+ *   shard_bwd -> d_embed [R, r] summed over shards -> shard_bwd_finish.
+ * Asynchronous on `stream`; errors as dspark_loss_fwd. */
+
+/* Step 1: prep rows, E = W1[prev], the shard's teacher logits and per-tile
+ * statistics, then lse_part [R, 2] fp32 = (log-sum-exp of z' = z + E W2^T,
+ * of T) over the shard's columns; -inf on unsupervised rows and for T without
+ * a teacher.  flags [1] as in dspark_fwd_out (the target-id range is not
+ * checked: shard-local ids leave it legitimately). */
+int dspark_shard_fwd_stats(const dspark_shape *shape, const dspark_hparams *hp,
+                           const dspark_inputs *in, void *workspace, size_t workspace_bytes,
+                           float *lse_part, uint32_t *flags, dspark_stream_t stream);
+
+/* lse [rows, 2] = log-sum-exp over the `shards` parts of lse_parts
+ * [shards, rows, 2] (fp64 inside, -inf when every part is -inf).  Errors:
+ * DSPARK_ERR_SHAPE (shards < 1 or > 65536, rows < 0 or >= 2^31), _NULL, _HIP. */
+int dspark_shard_merge_lse(int64_t shards, int64_t rows, const float *lse_parts, float *lse,
+                           dspark_stream_t stream);
+
+/* Step 2: with the merged lse [R, 2], terms [R, 3] fp64 = this shard's
+ * (sum |p - q|, sum p sign(p - q), z'_y if the shard owns the target else 0)
+ * on supervised rows, zeros elsewhere.  The sum over shards is the row's
+ * (L1, S, z'_y). */
+int dspark_shard_fwd_terms(const dspark_shape *shape, const dspark_hparams *hp,
+                           const dspark_inputs *in, void *workspace, size_t workspace_bytes,
+                           const float *lse, double *terms, dspark_stream_t stream);
+
+/* Step 3: from the shard-summed terms [R, 3], CE = lse_z - z'_y, the
+ * confidence head and the reductions: `out` as dspark_loss_fwd (identical on
+ * every shard). */
+int dspark_shard_fwd_finish(const dspark_shape *shape, const dspark_hparams *hp,
+                            const dspark_inputs *in, void *workspace, size_t workspace_bytes,
+                            const double *terms, dspark_fwd_out *out, dspark_stream_t stream);
+
+/* Step 4: the shard's gradients: d_draft_logits [R, draft_vocab] (grad_dtype),
+ * d_markov_w2 [draft_vocab, r] (the shard's rows of W2's gradient) and
+ * d_embed [R, r] fp32 = the shard's G . W2 term of dloss/dE (0 on unsupervised
+ * rows).  d_markov_w2 and d_embed are required when r > 0. */
+int dspark_shard_bwd(const dspark_shape *shape, const dspark_hparams *hp, const dspark_inputs *in,
+                     void *workspace, size_t workspace_bytes, float grad_scale,
+                     void *d_draft_logits, float *d_markov_w2, float *d_embed,
+                     dspark_stream_t stream);
+
+/* Step 5: from d_embed summed over the shards, the replicated gradients into
+ * out->d_markov_w1, d_conf_w, d_conf_b, d_conf_hidden (as dspark_loss_bwd;
+ * out->d_draft_logits and d_markov_w2 are not touched). */
+int dspark_shard_bwd_finish(const dspark_shape *shape, const dspark_hparams *hp,
+                            const dspark_inputs *in, void *workspace, size_t workspace_bytes,
+                            float grad_scale, const float *d_embed, dspark_bwd_out *out,
+                            dspark_stream_t stream);
+
 const char *dspark_status_string(int status);
 const char *dspark_last_hip_error(void);
 

@@ -5,3 +5,4 @@ from .loss import (DSparkBatch, FwdResult, HParams, REPORT_KEYS, build_blocks, c
                    dspark_accept_report, dspark_loss, dspark_loss_bwd, dspark_loss_fwd,
                    dspark_workspace_size, markov_logits)
 from ._capi import DSparkError
+from .shard import VocabShard, merge_lse, shard_loss

@@ -96,6 +96,20 @@ def lib():
     L.dspark_build_blocks.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int64] + \
         [C.c_void_p] * 9
     L.dspark_build_blocks.restype = C.c_int
+    common = [C.POINTER(Shape), C.POINTER(HParamsC), C.POINTER(InputsC), C.c_void_p,
+              C.c_size_t]
+    L.dspark_shard_fwd_stats.argtypes = common + [C.c_void_p, C.c_void_p, C.c_void_p]
+    L.dspark_shard_merge_lse.argtypes = [C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
+                                         C.c_void_p]
+    L.dspark_shard_fwd_terms.argtypes = common + [C.c_void_p, C.c_void_p, C.c_void_p]
+    L.dspark_shard_fwd_finish.argtypes = common + [C.c_void_p, C.POINTER(FwdOutC), C.c_void_p]
+    L.dspark_shard_bwd.argtypes = common + [C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
+                                            C.c_void_p]
+    L.dspark_shard_bwd_finish.argtypes = common + [C.c_float, C.c_void_p, C.POINTER(BwdOutC),
+                                                   C.c_void_p]
+    for f in ("dspark_shard_fwd_stats", "dspark_shard_merge_lse", "dspark_shard_fwd_terms",
+              "dspark_shard_fwd_finish", "dspark_shard_bwd", "dspark_shard_bwd_finish"):
+        getattr(L, f).restype = C.c_int
     L.dspark_status_string.argtypes = [C.c_int]
     L.dspark_status_string.restype = C.c_char_p
     L.dspark_last_hip_error.argtypes = []

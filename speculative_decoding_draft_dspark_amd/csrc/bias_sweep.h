@@ -53,9 +53,19 @@ hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int64_t rank, int splits,
 // bf16(G) itself and ghi, glo must be null.
 // With a teacher, sign(p - q) comes from the bits launch_bias_l1 wrote (T is
 // not read again).
+// shard: a target id outside [0, V) lives in another vocabulary shard (no
+// target term here) instead of being clamped.
 hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, const bf16_t* z,
                             const bf16_t* E, const bf16_t* W2, const uint2* signs,
                             const int32_t* tid, RowState rs, int has_teacher, float g, float ce_a,
-                            float l1_a, void* dz, bf16_t* ghi, bf16_t* glo, hipStream_t s);
+                            float l1_a, void* dz, bf16_t* ghi, bf16_t* glo, hipStream_t s,
+                            int shard = 0);
+
+// Vocabulary shard: part [R, 3] (fp64) = this shard's L1, S and, on the shard
+// that owns the target, z'_y (0 on the others and on unsupervised rows).
+hipError_t launch_bias_l1_shard(int64_t R, int64_t V, int64_t rank, int splits, int has_teacher,
+                                const double* part_l1, const double* part_s, const bf16_t* z,
+                                const bf16_t* E, const bf16_t* W2, const int32_t* tid,
+                                RowState rs, double* part, hipStream_t s);
 
 }  // namespace dspark

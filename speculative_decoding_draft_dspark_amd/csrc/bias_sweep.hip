@@ -206,6 +206,7 @@ struct SweepParams {
   bf16_t* ghi;
   bf16_t* glo;
   float g, ce_a, l1_a;
+  int shard;  // vocabulary shard: a target id outside [0, V) lives in another shard
 };
 
 // State of one sweep over a workgroup's 256 rows and vocabulary range.
@@ -284,7 +285,8 @@ struct Sweep {
           c0[rb] = cc[rb] - cl1[rb] * Sr[rb];
         }
         const int64_t t = P.tid[row];
-        y = t < 0 ? 0 : (t >= P.V ? P.V - 1 : t);
+        if (P.shard) y = (t >= 0 && t < P.V) ? t : -1;  // another shard owns the target
+        else y = t < 0 ? 0 : (t >= P.V ? P.V - 1 : t);
       }
       yl[rb] = (y >= vb && y < ve) ? static_cast<int>(y - vb) : -1;
       ebase[rb] = static_cast<uint32_t>((16 * rb + cl) * P.V + vb);
@@ -564,6 +566,20 @@ __global__ __launch_bounds__(kNT, 1) void bias_sweep_kernel(SweepParams P) {
 // Per supervised row: L1 and S from the split partials (0 without a
 // teacher) and CE = lse_z - z'_y, with z'_y = z_y + E_row . W2_y (fp32, k in
 // order: the same value as the sweeps' MFMA bias up to rounding).
+// z'_y = z_y + E_row . W2_y (fp32, k in order: the same value as the sweeps'
+// MFMA bias up to rounding).
+__device__ __forceinline__ float zprime_at(int64_t r, int64_t y, int64_t V, int64_t rank,
+                                           const bf16_t* z, const bf16_t* E, const bf16_t* W2) {
+  float zy = bf16_to_f32(z[r * V + y]);
+  if (rank > 0) {
+    float bias = 0.f;
+    for (int64_t k = 0; k < rank; ++k)
+      bias = fmaf(bf16_to_f32(E[r * rank + k]), bf16_to_f32(W2[y * rank + k]), bias);
+    zy += bias;
+  }
+  return zy;
+}
+
 __global__ void l1_finish_kernel(int64_t R, int64_t V, int64_t rank, int splits, int has_teacher,
                                  const double* pl1, const double* ps, const bf16_t* z,
                                  const bf16_t* E, const bf16_t* W2, const int32_t* tid,
@@ -582,16 +598,34 @@ __global__ void l1_finish_kernel(int64_t R, int64_t V, int64_t rank, int splits,
     }
   const int64_t t = tid[r];
   const int64_t y = t < 0 ? 0 : (t >= V ? V - 1 : t);
-  float zy = bf16_to_f32(z[r * V + y]);
-  if (rank > 0) {
-    float bias = 0.f;
-    for (int64_t k = 0; k < rank; ++k)
-      bias = fmaf(bf16_to_f32(E[r * rank + k]), bf16_to_f32(W2[y * rank + k]), bias);
-    zy += bias;
-  }
+  const float zy = zprime_at(r, y, V, rank, z, E, W2);
   rs.l1[r] = static_cast<float>(a);
   rs.S[r] = static_cast<float>(b);
   rs.ce[r] = rs.lse_z[r] - zy;
+}
+
+// Vocabulary shard: per supervised row, this shard's L1 and S (its split
+// partials summed) and z'_y when the shard owns the target (else 0), for the
+// caller to sum over the shards; unsupervised rows: zeros.
+__global__ void l1_shard_kernel(int64_t R, int64_t V, int64_t rank, int splits, int has_teacher,
+                                const double* pl1, const double* ps, const bf16_t* z,
+                                const bf16_t* E, const bf16_t* W2, const int32_t* tid,
+                                RowState rs, double* part) {
+  const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (r >= R) return;
+  double a = 0.0, b = 0.0, zy = 0.0;
+  if (rs.mask[r]) {
+    if (has_teacher)
+      for (int k = 0; k < splits; ++k) {
+        a += pl1[k * R + r];
+        b += ps[k * R + r];
+      }
+    const int64_t t = tid[r];
+    if (t >= 0 && t < V) zy = zprime_at(r, t, V, rank, z, E, W2);
+  }
+  part[3 * r] = a;
+  part[3 * r + 1] = b;
+  part[3 * r + 2] = zy;
 }
 
 template <int MODE, bool TEACHER, typename GT>
@@ -674,12 +708,24 @@ hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int64_t rank, int splits,
   return hipGetLastError();
 }
 
+hipError_t launch_bias_l1_shard(int64_t R, int64_t V, int64_t rank, int splits, int has_teacher,
+                                const double* part_l1, const double* part_s, const bf16_t* z,
+                                const bf16_t* E, const bf16_t* W2, const int32_t* tid,
+                                RowState rs, double* part, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(l1_shard_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)), dim3(256), 0,
+                     s, R, V, rank, splits, has_teacher, part_l1, part_s, z, E, W2, tid, rs, part);
+  return hipGetLastError();
+}
+
 hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, const bf16_t* z,
                             const bf16_t* E, const bf16_t* W2, const uint2* signs,
                             const int32_t* tid, RowState rs, int has_teacher, float g, float ce_a,
-                            float l1_a, void* dz, bf16_t* ghi, bf16_t* glo, hipStream_t s) {
+                            float l1_a, void* dz, bf16_t* ghi, bf16_t* glo, hipStream_t s,
+                            int shard) {
   if (R <= 0) return hipSuccess;
   SweepParams P = base_params(R, V, z, E, W2);
+  P.shard = shard;
   P.tid = tid; P.rs = rs; P.dz = dz; P.ghi = ghi; P.glo = glo;
   P.signs = reinterpret_cast<u32x2*>(const_cast<uint2*>(signs));
   P.nstat = (V + kSliceV - 1) / kSliceV;

@@ -287,6 +287,49 @@ int check_inputs(const Dims& d, const dspark_hparams* hp, const dspark_inputs* i
   return DSPARK_OK;
 }
 
+// In-place bf16 backward products (R and Vd multiples of 32).  dE partials =
+// [G hi | G lo] . [W2 | W2] (or G . W2) over vocabulary splits.
+hipError_t de_parts_direct(const Dims& d, const void* gA, const void* glo, const void* W2,
+                           float* dEpart, hipStream_t s) {
+  Operand A{}, B{};
+  const int gseg = glo ? 2 : 1;
+  A.seg[0] = gA; A.seg[1] = glo ? glo : gA;
+  A.kseg = d.Vd; A.kpad = d.Vd;
+  A.ld = d.Vd; A.layout = LAYOUT_KC; A.nseg = gseg;
+  B.seg[0] = B.seg[1] = W2; B.kseg = d.Vd; B.kpad = d.Vd; B.ld = d.r;
+  B.layout = LAYOUT_MK; B.nseg = gseg;
+  return launch_gemm_w4p(2, d.R, d.r, A, B, static_cast<int>(d.splits), dEpart, d.r, s);
+}
+
+// dW2 = [G hi ; G lo]^T . [E ; E] (or G^T . E) over row splits into `part`.
+hipError_t dw2_parts_direct(const Dims& d, const void* gA, const void* glo, const void* E,
+                            float* part, hipStream_t s) {
+  Operand A{}, B{};
+  const int gseg = glo ? 2 : 1;
+  A.seg[0] = gA; A.seg[1] = glo ? glo : gA;
+  A.kseg = d.R; A.kpad = d.R;
+  A.ld = d.Vd; A.layout = LAYOUT_MK; A.nseg = gseg;
+  B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = d.R; B.ld = d.r;
+  B.layout = LAYOUT_MK; B.nseg = gseg;
+  return launch_gemm_w4p(3, d.Vd, d.r, A, B, static_cast<int>(d.dw2_splits), part, d.r, s);
+}
+
+// Common checks of the vocabulary-shard entry points: the shape must take the
+// bias sweeps (bf16, rank in {0, 32, 64, 128, 256}, R and the shard width
+// multiples of 32 with a Markov head) and not ask for stored logits.
+int shard_setup(const dspark_shape* shape, const dspark_hparams* hp, const dspark_inputs* in,
+                void* ws, size_t wsb, Dims* d, Layout* L, Teacher* t) {
+  int st = make_dims(shape, d);
+  if (st) return st;
+  if (!d->bias_path) return DSPARK_ERR_SHAPE;
+  st = check_inputs(*d, hp, in, t);
+  if (st) return st;
+  if (misaligned(ws)) return DSPARK_ERR_ALIGN;
+  *L = make_layout(*d);
+  if (!ws || wsb < L->total) return DSPARK_ERR_WORKSPACE;
+  return DSPARK_OK;
+}
+
 }  // namespace
 }  // namespace dspark
 
@@ -455,7 +498,6 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
     // dW2 = G^T . E (contraction over rows).
     bf16_t* ghi = d.gdtype == DSPARK_BF16 ? nullptr : reinterpret_cast<bf16_t*>(ws + L.ghi);
     bf16_t* glo = d.g_lo ? reinterpret_cast<bf16_t*>(ws + L.glo) : nullptr;
-    const int gseg = d.g_lo ? 2 : 1;  // K segments of the products: G hi (, G lo)
     const void* gA = ghi ? static_cast<const void*>(ghi) : out->d_draft_logits;
     bf16_t* bhi = reinterpret_cast<bf16_t*>(ws + L.blkhi);
     bf16_t* blo = reinterpret_cast<bf16_t*>(ws + L.blklo);
@@ -478,33 +520,18 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
         DSPARK_STAGE(kGradSweep, launch_grad_sweep(d.gdtype, d.R, d.Vd, Zp, T, in->target_ids, rs,
                                                    teacher != kNone, g, hp->ce_alpha, hp->l1_alpha,
                                                    out->d_draft_logits, ghi, glo, nullptr, s));
-      {  // dE partials = [G hi | G lo] . [W2 | W2] (or G . W2) over vocabulary splits
-        Operand A{}, B{};
-        A.seg[0] = gA; A.seg[1] = glo ? static_cast<const void*>(glo) : gA;
-        A.kseg = d.Vd; A.kpad = d.Vd;
-        A.ld = d.Vd; A.layout = LAYOUT_KC; A.nseg = gseg;
-        B.seg[0] = B.seg[1] = in->markov_w2; B.kseg = d.Vd; B.kpad = d.Vd; B.ld = d.r;
-        B.layout = LAYOUT_MK; B.nseg = gseg;
-        DSPARK_STAGE(kDeGemm, launch_gemm_w4p(2, d.R, d.r, A, B, static_cast<int>(d.splits),
-                                              dEpart, d.r, s));
-      }
+      DSPARK_STAGE(kDeGemm, de_parts_direct(d, gA, glo, in->markov_w2, dEpart, s));
       DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
                                                dEpart, rs, d.conf_markov, in->conf_w, d.Hd, g,
                                                c_a, dE, s));
       DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
       DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
                                             out->d_markov_w1, s));
-      {  // dW2 = [G hi ; G lo]^T . [E ; E] (or G^T . E) over row splits, then summed
+      {  // dW2 over row splits, then summed
         float* part = reinterpret_cast<float*>(ws + L.dw2part);
-        Operand A{}, B{};
-        A.seg[0] = gA; A.seg[1] = glo ? static_cast<const void*>(glo) : gA;
-        A.kseg = d.R; A.kpad = d.R;
-        A.ld = d.Vd; A.layout = LAYOUT_MK; A.nseg = gseg;
-        B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = d.R; B.ld = d.r;
-        B.layout = LAYOUT_MK; B.nseg = gseg;
-        const int sp = static_cast<int>(d.dw2_splits);
-        DSPARK_STAGE(kDw2Gemm, launch_gemm_w4p(3, d.Vd, d.r, A, B, sp, part, d.r, s));
-        DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, sp, part, out->d_markov_w2, s));
+        DSPARK_STAGE(kDw2Gemm, dw2_parts_direct(d, gA, glo, E, part, s));
+        DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, static_cast<int>(d.dw2_splits), part,
+                                                out->d_markov_w2, s));
       }
     } else if (d.markov) {
       DSPARK_STAGE(kGradSweep, launch_grad_sweep8(d.gdtype, d.R, rgroups, d.Vd, Zp, T,
@@ -772,6 +799,208 @@ int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,
   return hip_status(launch_accept_report(batch * num_blocks, static_cast<int>(block_size),
                                          accept_rate, eval_mask, block_keep_mask, out4,
                                          static_cast<hipStream_t>(stream)));
+}
+
+// ---- vocabulary shards: each caller holds draft_vocab columns of the draft
+// logits, teacher and W2; the (lse, L1, S, z'_y) row partials merge exactly.
+
+int dspark_shard_fwd_stats(const dspark_shape* shape, const dspark_hparams* hp,
+                           const dspark_inputs* in, void* workspace, size_t workspace_bytes,
+                           float* lse_part, uint32_t* flags, dspark_stream_t stream) {
+  Dims d;
+  Layout L;
+  Teacher teacher;
+  int st = shard_setup(shape, hp, in, workspace, workspace_bytes, &d, &L, &teacher);
+  if (st) return st;
+  if (!lse_part || !flags) return DSPARK_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const RowState rs = row_state(ws, L, d);
+  float* T = reinterpret_cast<float*>(ws + L.T);
+  float2* sz = reinterpret_cast<float2*>(ws + L.sz);
+  float2* stt = reinterpret_cast<float2*>(ws + L.st);
+  void* E = ws + L.E;
+  // target ids are shard-local: out of [0, Vd) means another shard owns them
+  DSPARK_STAGE(kPrep, launch_prep_rows(d.R, static_cast<int>(d.K), in->eval_mask,
+                                       in->block_keep_mask, in->target_ids, in->prev_ids, d.Vd,
+                                       d.Vt, d.markov, hp->loss_decay_gamma,
+                                       teacher == kNone ? DSPARK_FLAG_NO_TEACHER : 0u, rs.mask,
+                                       rs.w, flags, s, 0));
+  if (d.markov)
+    DSPARK_STAGE(kGather, launch_gather_embed(d.dtype, d.R, d.r, d.Vt, in->prev_ids, rs.mask,
+                                              in->markov_w1, E, s));
+  if (teacher != kNone) {
+    Operand A{}, B{};
+    EpiParams ep{};
+    A.nseg = B.nseg = 1;
+    A.layout = B.layout = LAYOUT_KC;
+    ep.C = T; ep.ldc = d.Vd; ep.stats = stt; ep.nstat = d.nstat;
+    if (teacher == kHidden) {
+      A.seg[0] = A.seg[1] = in->target_hidden; A.kseg = d.H; A.kpad = gemm_kpad(d.H, d.esize);
+      A.ld = d.H;
+      B.seg[0] = B.seg[1] = in->lm_head; B.kseg = d.H; B.kpad = A.kpad; B.ld = d.H;
+    } else {
+      ep.X = in->aligned_target_logits; ep.ldx = d.Vd;
+    }
+    DSPARK_STAGE(kLogitsGemm, launch_gemm(d.dtype, EPI_STATS, 1, d.R, d.Vd, A, B, 1, ep, s));
+  }
+  const bf16_t* z = static_cast<const bf16_t*>(in->draft_logits);
+  DSPARK_STAGE(kBiasStats, launch_bias_stats(d.R, d.Vd, d.r, z,
+                                             d.markov ? static_cast<const bf16_t*>(E) : nullptr,
+                                             d.markov ? static_cast<const bf16_t*>(in->markov_w2)
+                                                      : nullptr,
+                                             sz, d.nstat, s));
+  DSPARK_STAGE(kL1Sweep, launch_lse_rows(d.R, sz, stt, d.nstat, rs.mask, teacher != kNone, rs, s));
+  DSPARK_STAGE(kL1Sweep, launch_shard_lse_out(d.R, teacher != kNone, rs,
+                                              reinterpret_cast<float2*>(lse_part), s));
+  return DSPARK_OK;
+}
+
+int dspark_shard_merge_lse(int64_t shards, int64_t rows, const float* lse_parts, float* lse,
+                           dspark_stream_t stream) {
+  if (shards < 1 || rows < 0 || rows > (int64_t{1} << 31) - 1 || shards > (int64_t{1} << 16))
+    return DSPARK_ERR_SHAPE;
+  if (rows == 0) return DSPARK_OK;
+  if (!lse_parts || !lse) return DSPARK_ERR_NULL;
+  return hip_status(launch_shard_merge_lse(shards, rows, lse_parts, lse,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int dspark_shard_fwd_terms(const dspark_shape* shape, const dspark_hparams* hp,
+                           const dspark_inputs* in, void* workspace, size_t workspace_bytes,
+                           const float* lse, double* terms, dspark_stream_t stream) {
+  Dims d;
+  Layout L;
+  Teacher teacher;
+  int st = shard_setup(shape, hp, in, workspace, workspace_bytes, &d, &L, &teacher);
+  if (st) return st;
+  if (!lse || !terms) return DSPARK_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const RowState rs = row_state(ws, L, d);
+  const bf16_t* z = static_cast<const bf16_t*>(in->draft_logits);
+  const bf16_t* Eb = d.markov ? reinterpret_cast<const bf16_t*>(ws + L.E) : nullptr;
+  const bf16_t* W2 = d.markov ? static_cast<const bf16_t*>(in->markov_w2) : nullptr;
+  double* pl1 = reinterpret_cast<double*>(ws + L.pl1);
+  double* ps = reinterpret_cast<double*>(ws + L.ps);
+  DSPARK_STAGE(kL1Sweep, launch_shard_set_lse(d.R, teacher != kNone,
+                                              reinterpret_cast<const float2*>(lse), rs, s));
+  DSPARK_STAGE(kL1Sweep, launch_bias_l1(d.R, d.Vd, d.r, z, Eb, W2,
+                                        teacher != kNone ? reinterpret_cast<const float*>(ws + L.T)
+                                                         : nullptr,
+                                        in->target_ids, rs, pl1, ps,
+                                        reinterpret_cast<uint2*>(ws + L.sg), s));
+  DSPARK_STAGE(kL1Sweep, launch_bias_l1_shard(d.R, d.Vd, d.r, static_cast<int>(d.bsplits),
+                                              teacher != kNone, pl1, ps, z, Eb, W2,
+                                              in->target_ids, rs, terms, s));
+  return DSPARK_OK;
+}
+
+int dspark_shard_fwd_finish(const dspark_shape* shape, const dspark_hparams* hp,
+                            const dspark_inputs* in, void* workspace, size_t workspace_bytes,
+                            const double* terms, dspark_fwd_out* out, dspark_stream_t stream) {
+  Dims d;
+  Layout L;
+  Teacher teacher;
+  int st = shard_setup(shape, hp, in, workspace, workspace_bytes, &d, &L, &teacher);
+  if (st) return st;
+  if (!terms) return DSPARK_ERR_NULL;
+  if (!out || !out->loss || !out->num_tokens || !out->pairs || !out->flags) return DSPARK_ERR_NULL;
+  if (misaligned(out->accept_rate) || misaligned(out->row_terms)) return DSPARK_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const RowState rs = row_state(ws, L, d);
+  DSPARK_STAGE(kFinalize, launch_shard_set_terms(d.R, terms, rs, s));
+  DSPARK_STAGE(kFinalize, launch_finalize_rows(d.dtype, d.R, d.Hd, d.r, d.conf_markov, d.conf,
+                                               in->conf_hidden, ws + L.E, in->conf_w, in->conf_b,
+                                               rs, out->accept_rate, out->row_terms, out->flags,
+                                               hp->ce_alpha, hp->l1_alpha, hp->confidence_alpha,
+                                               s));
+  DSPARK_STAGE(kReduce, launch_reduce_fwd(d.R, d.B * d.N, static_cast<int>(d.K), rs,
+                                          in->eval_mask, in->block_keep_mask, hp->ce_alpha,
+                                          hp->l1_alpha, d.conf ? hp->confidence_alpha : 0.f,
+                                          out->loss, out->num_tokens, out->pairs, s));
+  return DSPARK_OK;
+}
+
+int dspark_shard_bwd(const dspark_shape* shape, const dspark_hparams* hp, const dspark_inputs* in,
+                     void* workspace, size_t workspace_bytes, float grad_scale,
+                     void* d_draft_logits, float* d_markov_w2, float* d_embed,
+                     dspark_stream_t stream) {
+  Dims d;
+  Layout L;
+  Teacher teacher;
+  int st = shard_setup(shape, hp, in, workspace, workspace_bytes, &d, &L, &teacher);
+  if (st) return st;
+  if (!d_draft_logits) return DSPARK_ERR_NULL;
+  if (d.markov && (!d_markov_w2 || !d_embed)) return DSPARK_ERR_NULL;
+  if (misaligned(d_draft_logits) || misaligned(d_markov_w2) || misaligned(d_embed))
+    return DSPARK_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const RowState rs = row_state(ws, L, d);
+  void* E = ws + L.E;
+  bf16_t* ghi = d.gdtype == DSPARK_BF16 ? nullptr : reinterpret_cast<bf16_t*>(ws + L.ghi);
+  bf16_t* glo = d.g_lo ? reinterpret_cast<bf16_t*>(ws + L.glo) : nullptr;
+  const void* gA = ghi ? static_cast<const void*>(ghi) : d_draft_logits;
+  DSPARK_STAGE(kGradSweep,
+               launch_bias_grad(d.gdtype, d.R, d.Vd, d.r,
+                                static_cast<const bf16_t*>(in->draft_logits),
+                                d.markov ? static_cast<const bf16_t*>(E) : nullptr,
+                                d.markov ? static_cast<const bf16_t*>(in->markov_w2) : nullptr,
+                                reinterpret_cast<const uint2*>(ws + L.sg), in->target_ids, rs,
+                                teacher != kNone, grad_scale, hp->ce_alpha, hp->l1_alpha,
+                                d_draft_logits, ghi, glo, s, 1));
+  if (d.markov) {
+    float* dEpart = reinterpret_cast<float*>(ws + L.dEpart);
+    DSPARK_STAGE(kDeGemm, de_parts_direct(d, gA, glo, in->markov_w2, dEpart, s));
+    DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
+                                             dEpart, rs, 0, nullptr, d.Hd, grad_scale, 0.f,
+                                             d_embed, s));
+    float* part = reinterpret_cast<float*>(ws + L.dw2part);
+    DSPARK_STAGE(kDw2Gemm, dw2_parts_direct(d, gA, glo, E, part, s));
+    DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, static_cast<int>(d.dw2_splits), part,
+                                            d_markov_w2, s));
+  }
+  return DSPARK_OK;
+}
+
+int dspark_shard_bwd_finish(const dspark_shape* shape, const dspark_hparams* hp,
+                            const dspark_inputs* in, void* workspace, size_t workspace_bytes,
+                            float grad_scale, const float* d_embed, dspark_bwd_out* out,
+                            dspark_stream_t stream) {
+  Dims d;
+  Layout L;
+  Teacher teacher;
+  int st = shard_setup(shape, hp, in, workspace, workspace_bytes, &d, &L, &teacher);
+  if (st) return st;
+  if (!out) return DSPARK_ERR_NULL;
+  if (d.markov && (!d_embed || !out->d_markov_w1)) return DSPARK_ERR_NULL;
+  if (d.conf && (!out->d_conf_w || !out->d_conf_b)) return DSPARK_ERR_NULL;
+  if (misaligned(d_embed) || misaligned(out->d_markov_w1) || misaligned(out->d_conf_hidden))
+    return DSPARK_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const RowState rs = row_state(ws, L, d);
+  void* E = ws + L.E;
+  const float c_a = d.conf ? hp->confidence_alpha : 0.f;
+  if (d.markov) {
+    float* dE = reinterpret_cast<float*>(ws + L.dE);
+    // the confidence term of dE once, on the shard-summed vocabulary term
+    DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, 1, d_embed, rs, d.conf_markov,
+                                             in->conf_w, d.Hd, grad_scale, c_a, dE, s));
+    DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
+    DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
+                                          out->d_markov_w1, s));
+  }
+  if (d.conf) {
+    float* part = reinterpret_cast<float*>(ws + L.confpart);
+    DSPARK_STAGE(kConfBwd, launch_conf_bwd(d.dtype, d.R, d.Hd, d.r, d.conf_markov,
+                                           in->conf_hidden, E, in->conf_w, rs, grad_scale, c_a,
+                                           part, d.conf_chunks, out->d_conf_w, out->d_conf_b,
+                                           out->d_conf_hidden, s));
+  }
+  return DSPARK_OK;
 }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_prep_rows(int64_t R, int K, const uint8_t* eval, const uint8_t* keep,
                             const int32_t* tid, const int32_t* prev, int64_t Vd, int64_t Vt,
                             int has_markov, float gamma, uint32_t set_bits, uint8_t* mask, float* w,
-                            uint32_t* flags, hipStream_t s);
+                            uint32_t* flags, hipStream_t s, int check_target = 1);
 hipError_t launch_gather_embed(int dtype, int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
                                const uint8_t* mask, const void* W1, void* E, hipStream_t s);
 // Loss rows of sampled anchors [B, N] over sequences [B, L] (labels, previous
@@ -86,5 +86,18 @@ hipError_t launch_conf_bwd(int dtype, int64_t R, int64_t Hd, int64_t rank, int c
                            const void* hd, const void* E, const void* Wc, RowState rs, float g,
                            float c_a, float* part, int chunks, float* dWc, float* db, float* dh,
                            hipStream_t s);
+
+// Vocabulary shards.  Per row, the shard's (lse_z, lse_t), -inf on unsupervised
+// rows and for lse_t without a teacher.
+hipError_t launch_shard_lse_out(int64_t R, int has_teacher, RowState rs, float2* out,
+                                hipStream_t s);
+// out [R, 2] = log-sum-exp over the G shards of parts [G, R, 2].
+hipError_t launch_shard_merge_lse(int64_t G, int64_t R, const float* parts, float* out,
+                                  hipStream_t s);
+// rs.lse_z, rs.lse_t from merged log-sum-exps [R, 2] (0 on unsupervised rows).
+hipError_t launch_shard_set_lse(int64_t R, int has_teacher, const float2* lse, RowState rs,
+                                hipStream_t s);
+// rs.l1, rs.S, rs.ce from the shard-summed (L1, S, z'_y) [R, 3] (fp64).
+hipError_t launch_shard_set_terms(int64_t R, const double* terms, RowState rs, hipStream_t s);
 
 }  // namespace dspark

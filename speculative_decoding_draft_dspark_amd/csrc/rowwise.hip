@@ -49,8 +49,8 @@ __device__ __forceinline__ bool slot_supervised(const uint8_t* eval, const uint8
 
 __global__ void prep_rows_kernel(int64_t R, int K, const uint8_t* eval, const uint8_t* keep,
                                  const int32_t* tid, const int32_t* prev, int64_t Vd, int64_t Vt,
-                                 int has_markov, float gamma, uint32_t set_bits, uint8_t* mask,
-                                 float* w, uint32_t* flags) {
+                                 int has_markov, float gamma, uint32_t set_bits, int check_target,
+                                 uint8_t* mask, float* w, uint32_t* flags) {
   const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (r >= R) return;
   if (r == 0 && set_bits) atomicOr(flags, set_bits);
@@ -61,7 +61,7 @@ __global__ void prep_rows_kernel(int64_t R, int K, const uint8_t* eval, const ui
   if (m) {
     uint32_t f = 0;
     const int32_t y = tid[r];
-    if (y < 0 || y >= Vd) f |= 1u;
+    if (check_target && (y < 0 || y >= Vd)) f |= 1u;
     if (has_markov) {
       const int32_t pv = prev[r];
       if (pv < 0 || pv >= Vt) f |= 2u;
@@ -73,9 +73,10 @@ __global__ void prep_rows_kernel(int64_t R, int K, const uint8_t* eval, const ui
 hipError_t launch_prep_rows(int64_t R, int K, const uint8_t* eval, const uint8_t* keep,
                             const int32_t* tid, const int32_t* prev, int64_t Vd, int64_t Vt,
                             int has_markov, float gamma, uint32_t set_bits, uint8_t* mask, float* w,
-                            uint32_t* flags, hipStream_t s) {
+                            uint32_t* flags, hipStream_t s, int check_target) {
   hipLaunchKernelGGL(prep_rows_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)), dim3(256), 0,
-                     s, R, K, eval, keep, tid, prev, Vd, Vt, has_markov, gamma, set_bits, mask, w, flags);
+                     s, R, K, eval, keep, tid, prev, Vd, Vt, has_markov, gamma, set_bits,
+                     check_target, mask, w, flags);
   return hipGetLastError();
 }
 
@@ -937,6 +938,87 @@ hipError_t launch_zero_masked_rows(int64_t R, int64_t N, const uint8_t* mask, fl
   if (R <= 0 || N <= 0) return hipSuccess;
   hipLaunchKernelGGL(zero_masked_rows_kernel, dim3(static_cast<uint32_t>(R)), dim3(256), 0, s, N,
                      mask, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- vocabulary shards
+
+// A shard's log-sum-exp of z' and T per row: -inf on unsupervised rows (and for
+// T without a teacher), the identity of the merge below.
+__global__ void shard_lse_out_kernel(int64_t R, int has_teacher, RowState rs, float2* out) {
+  const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (r >= R) return;
+  const float ninf = -INFINITY;
+  const bool m = rs.mask[r] != 0;
+  out[r] = make_float2(m ? rs.lse_z[r] : ninf, m && has_teacher ? rs.lse_t[r] : ninf);
+}
+
+hipError_t launch_shard_lse_out(int64_t R, int has_teacher, RowState rs, float2* out,
+                                hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shard_lse_out_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)), dim3(256),
+                     0, s, R, has_teacher, rs, out);
+  return hipGetLastError();
+}
+
+// lse = M + log sum_g exp(lse_g - M), M = max_g lse_g, in fp64 over the shards
+// in order; -inf when every shard gives -inf.
+__global__ void shard_merge_lse_kernel(int64_t G, int64_t R, const float* parts, float* out) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= 2 * R) return;
+  double M = -INFINITY;
+  for (int64_t g = 0; g < G; ++g) M = fmax(M, static_cast<double>(parts[g * 2 * R + i]));
+  double v = M;
+  if (M > -INFINITY) {
+    double l = 0.0;
+    for (int64_t g = 0; g < G; ++g) l += exp(static_cast<double>(parts[g * 2 * R + i]) - M);
+    v = M + log(l);
+  }
+  out[i] = static_cast<float>(v);
+}
+
+hipError_t launch_shard_merge_lse(int64_t G, int64_t R, const float* parts, float* out,
+                                  hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shard_merge_lse_kernel, dim3(static_cast<uint32_t>((2 * R + 255) / 256)),
+                     dim3(256), 0, s, G, R, parts, out);
+  return hipGetLastError();
+}
+
+// Row state from the merged log-sum-exps (0 on unsupervised rows, lse_t 0
+// without a teacher, as the unsplit forward leaves them).
+__global__ void shard_set_lse_kernel(int64_t R, int has_teacher, const float2* lse, RowState rs) {
+  const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (r >= R) return;
+  const bool m = rs.mask[r] != 0;
+  const float2 v = lse[r];
+  rs.lse_z[r] = m ? v.x : 0.f;
+  rs.lse_t[r] = m && has_teacher ? v.y : 0.f;
+}
+
+hipError_t launch_shard_set_lse(int64_t R, int has_teacher, const float2* lse, RowState rs,
+                                hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shard_set_lse_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)), dim3(256),
+                     0, s, R, has_teacher, lse, rs);
+  return hipGetLastError();
+}
+
+// Row state from the shard-summed terms [R, 3] (L1, S, z'_y): CE = lse_z - z'_y
+// on supervised rows, every term 0 on the others.
+__global__ void shard_set_terms_kernel(int64_t R, const double* terms, RowState rs) {
+  const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (r >= R) return;
+  const bool m = rs.mask[r] != 0;
+  rs.l1[r] = m ? static_cast<float>(terms[3 * r]) : 0.f;
+  rs.S[r] = m ? static_cast<float>(terms[3 * r + 1]) : 0.f;
+  rs.ce[r] = m ? rs.lse_z[r] - static_cast<float>(terms[3 * r + 2]) : 0.f;
+}
+
+hipError_t launch_shard_set_terms(int64_t R, const double* terms, RowState rs, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shard_set_terms_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)),
+                     dim3(256), 0, s, R, terms, rs);
   return hipGetLastError();
 }
 

@@ -183,3 +183,40 @@ def test_build_blocks_validation_codes(L):
     assert L.dspark_build_blocks(2, 64, 4, 0, *args, None, None) == E["ERR_SHAPE"]
     assert L.dspark_build_blocks(0, 64, 4, 7, *args, None, None) == E["ERR_SHAPE"]
     assert L.dspark_build_blocks(2, 64, 1 << 40, 7, *args, None, None) == E["ERR_SHAPE"]
+
+
+def test_vocab_shard_validation_codes(L):
+    """The vocabulary-shard entry points take only shapes of the bias sweeps and
+    reject bad arguments on the host (no HIP call)."""
+    E = {v: k for k, v in capi.STATUS.items()}
+    hp = capi.HParamsC(0.1, 0.9, 1.0, 4.0)
+    inp = _inputs()
+    good = _shape(num_blocks=16, markov_rank=64)          # R = 224, bf16, rank 64
+    ws = L.dspark_workspace_size(C.byref(good))
+
+    def stats(shape, lse=FAKE, flags=FAKE, wsbytes=ws):
+        return L.dspark_shard_fwd_stats(C.byref(shape), C.byref(hp), C.byref(inp), FAKE,
+                                        wsbytes, lse, flags, None)
+    assert stats(good, lse=None) == E["ERR_NULL"]
+    assert stats(good, flags=None) == E["ERR_NULL"]
+    assert stats(good, wsbytes=ws - 1) == E["ERR_WORKSPACE"]
+    assert stats(_shape(num_blocks=16, markov_rank=16)) == E["ERR_SHAPE"]       # rank 16
+    assert stats(_shape(num_blocks=16, markov_rank=64, dtype=0, grad_dtype=0)) == E["ERR_SHAPE"]
+    assert stats(_shape(num_blocks=16, markov_rank=64,
+                        options=capi.OPT_STORE_DRAFT_LOGITS)) == E["ERR_SHAPE"]
+    assert stats(_shape(num_blocks=3, markov_rank=64)) == E["ERR_SHAPE"]       # R = 42
+    assert L.dspark_shard_fwd_terms(C.byref(good), C.byref(hp), C.byref(inp), FAKE, ws, None,
+                                    FAKE, None) == E["ERR_NULL"]
+    assert L.dspark_shard_fwd_finish(C.byref(good), C.byref(hp), C.byref(inp), FAKE, ws, FAKE,
+                                     None, None) == E["ERR_NULL"]
+    assert L.dspark_shard_bwd(C.byref(good), C.byref(hp), C.byref(inp), FAKE, ws, 1.0, FAKE,
+                              None, FAKE, None) == E["ERR_NULL"]
+    assert L.dspark_shard_bwd(C.byref(good), C.byref(hp), C.byref(inp), FAKE, ws, 1.0, FAKE + 2,
+                              FAKE, FAKE, None) == E["ERR_ALIGN"]
+    o = capi.BwdOutC(None, None, None, FAKE, FAKE, None)
+    assert L.dspark_shard_bwd_finish(C.byref(good), C.byref(hp), C.byref(inp), FAKE, ws, 1.0,
+                                     FAKE, C.byref(o), None) == E["ERR_NULL"]   # d_markov_w1
+    assert L.dspark_shard_merge_lse(0, 10, FAKE, FAKE, None) == E["ERR_SHAPE"]
+    assert L.dspark_shard_merge_lse(2, -1, FAKE, FAKE, None) == E["ERR_SHAPE"]
+    assert L.dspark_shard_merge_lse(2, 10, None, FAKE, None) == E["ERR_NULL"]
+    assert L.dspark_shard_merge_lse(2, 0, None, None, None) == E["OK"]
