@@ -563,45 +563,60 @@ __global__ __launch_bounds__(kNT, 1) void bias_sweep_kernel(SweepParams P) {
   sw.finish();
 }
 
-// Per supervised row: L1 and S from the split partials (0 without a
-// teacher) and CE = lse_z - z'_y, with z'_y = z_y + E_row . W2_y (fp32, k in
-// order: the same value as the sweeps' MFMA bias up to rounding).
-// z'_y = z_y + E_row . W2_y (fp32, k in order: the same value as the sweeps'
-// MFMA bias up to rounding).
-__device__ __forceinline__ float zprime_at(int64_t r, int64_t y, int64_t V, int64_t rank,
-                                           const bf16_t* z, const bf16_t* E, const bf16_t* W2) {
-  float zy = bf16_to_f32(z[r * V + y]);
-  if (rank > 0) {
-    float bias = 0.f;
-    for (int64_t k = 0; k < rank; ++k)
+// Finishing kernels: one wave per row (rows are few, each needs a short
+// dot product and a sum over the vocabulary splits).
+constexpr int kFinishWaves = 4;
+
+// Per row, over the wave: (sum of the split partials of L1, of S) in fp64
+// and, if y >= 0, z'_y = z_y + E_row . W2_y (fp32; lane k takes k, k + 64, ...).
+struct RowFinish {
+  double l1, S;
+  float zy;
+};
+__device__ __forceinline__ RowFinish row_finish(int64_t r, int64_t R, int64_t y, int64_t V,
+                                                int64_t rank, int splits, int has_teacher,
+                                                const double* pl1, const double* ps,
+                                                const bf16_t* z, const bf16_t* E,
+                                                const bf16_t* W2, int lane) {
+  double a = 0.0, b = 0.0;
+  if (has_teacher)
+    for (int k = lane; k < splits; k += kWave) {
+      a += pl1[k * R + r];
+      b += ps[k * R + r];
+    }
+  float bias = 0.f;
+  if (y >= 0)
+    for (int64_t k = lane; k < rank; k += kWave)
       bias = fmaf(bf16_to_f32(E[r * rank + k]), bf16_to_f32(W2[y * rank + k]), bias);
-    zy += bias;
-  }
-  return zy;
+  RowFinish f;
+  f.l1 = wave_sum(a);
+  f.S = wave_sum(b);
+  f.zy = y >= 0 ? bf16_to_f32(z[r * V + y]) + wave_sumf(bias) : 0.f;
+  return f;
 }
 
+// Per supervised row: L1 and S from the split partials (0 without a
+// teacher) and CE = lse_z - z'_y (target id clamped to the vocabulary);
+// unsupervised rows: zeros.
 __global__ void l1_finish_kernel(int64_t R, int64_t V, int64_t rank, int splits, int has_teacher,
                                  const double* pl1, const double* ps, const bf16_t* z,
                                  const bf16_t* E, const bf16_t* W2, const int32_t* tid,
                                  RowState rs) {
-  const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int64_t r = blockIdx.x * static_cast<int64_t>(kFinishWaves) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (r >= R) return;
   if (!rs.mask[r]) {
-    rs.l1[r] = 0.f; rs.S[r] = 0.f; rs.ce[r] = 0.f;
+    if (lane == 0) { rs.l1[r] = 0.f; rs.S[r] = 0.f; rs.ce[r] = 0.f; }
     return;
   }
-  double a = 0.0, b = 0.0;
-  if (has_teacher)
-    for (int k = 0; k < splits; ++k) {
-      a += pl1[k * R + r];
-      b += ps[k * R + r];
-    }
   const int64_t t = tid[r];
   const int64_t y = t < 0 ? 0 : (t >= V ? V - 1 : t);
-  const float zy = zprime_at(r, y, V, rank, z, E, W2);
-  rs.l1[r] = static_cast<float>(a);
-  rs.S[r] = static_cast<float>(b);
-  rs.ce[r] = rs.lse_z[r] - zy;
+  const RowFinish f = row_finish(r, R, y, V, rank, splits, has_teacher, pl1, ps, z, E, W2, lane);
+  if (lane == 0) {
+    rs.l1[r] = static_cast<float>(f.l1);
+    rs.S[r] = static_cast<float>(f.S);
+    rs.ce[r] = rs.lse_z[r] - f.zy;
+  }
 }
 
 // Vocabulary shard: per supervised row, this shard's L1 and S (its split
@@ -611,21 +626,20 @@ __global__ void l1_shard_kernel(int64_t R, int64_t V, int64_t rank, int splits, 
                                 const double* pl1, const double* ps, const bf16_t* z,
                                 const bf16_t* E, const bf16_t* W2, const int32_t* tid,
                                 RowState rs, double* part) {
-  const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int64_t r = blockIdx.x * static_cast<int64_t>(kFinishWaves) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (r >= R) return;
-  double a = 0.0, b = 0.0, zy = 0.0;
+  RowFinish f{0.0, 0.0, 0.f};
   if (rs.mask[r]) {
-    if (has_teacher)
-      for (int k = 0; k < splits; ++k) {
-        a += pl1[k * R + r];
-        b += ps[k * R + r];
-      }
     const int64_t t = tid[r];
-    if (t >= 0 && t < V) zy = zprime_at(r, t, V, rank, z, E, W2);
+    f = row_finish(r, R, (t >= 0 && t < V) ? t : -1, V, rank, splits, has_teacher, pl1, ps, z,
+                   E, W2, lane);
   }
-  part[3 * r] = a;
-  part[3 * r + 1] = b;
-  part[3 * r + 2] = zy;
+  if (lane == 0) {
+    part[3 * r] = f.l1;
+    part[3 * r + 1] = f.S;
+    part[3 * r + 2] = f.zy;
+  }
 }
 
 template <int MODE, bool TEACHER, typename GT>
@@ -703,7 +717,9 @@ hipError_t launch_bias_l1_finish(int64_t R, int64_t V, int64_t rank, int splits,
                                  const bf16_t* E, const bf16_t* W2, const int32_t* tid,
                                  RowState rs, hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(l1_finish_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(l1_finish_kernel,
+                     dim3(static_cast<uint32_t>((R + kFinishWaves - 1) / kFinishWaves)),
+                     dim3(kFinishWaves * kWave), 0,
                      s, R, V, rank, splits, has_teacher, part_l1, part_s, z, E, W2, tid, rs);
   return hipGetLastError();
 }
@@ -713,7 +729,9 @@ hipError_t launch_bias_l1_shard(int64_t R, int64_t V, int64_t rank, int splits, 
                                 const bf16_t* E, const bf16_t* W2, const int32_t* tid,
                                 RowState rs, double* part, hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(l1_shard_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(l1_shard_kernel,
+                     dim3(static_cast<uint32_t>((R + kFinishWaves - 1) / kFinishWaves)),
+                     dim3(kFinishWaves * kWave), 0,
                      s, R, V, rank, splits, has_teacher, part_l1, part_s, z, E, W2, tid, rs, part);
   return hipGetLastError();
 }

@@ -770,11 +770,54 @@ __global__ void conf_bwd_partial_kernel(int64_t R, int64_t Hd, int64_t rank, int
   part[blockIdx.y * (F + 1) + f] = acc;
 }
 
+// bf16 inputs with Hd % 8 == 0: one thread per 8 consecutive features (one
+// 16-byte load per row; a group never straddles h and e), plus one thread for
+// the bias column.  Same per-feature sums, in the same row order.
+__global__ void conf_bwd_partial8_kernel(int64_t R, int64_t Hd, int64_t rank, int64_t F,
+                                         int64_t rows_per, const bf16_t* hd, const bf16_t* E,
+                                         RowState rs, float g, float c_a, float* part) {
+  const int64_t f0 = (blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x) * 8;
+  const int64_t r0 = blockIdx.y * rows_per;
+  const int64_t r1 = (r0 + rows_per) < R ? (r0 + rows_per) : R;
+  if (f0 > F) return;
+  float* out = part + blockIdx.y * (F + 1);
+  if (f0 == F) {  // bias column: x = 1
+    float acc = 0.f;
+#pragma unroll 8
+    for (int64_t r = r0; r < r1; ++r) {
+      const float t = g * rs.w[r] * c_a * rs.dcoef[r];
+      acc += rs.mask[r] ? t : 0.f;
+    }
+    out[F] = acc;
+    return;
+  }
+  const bf16_t* src = f0 < Hd ? hd + f0 : E + (f0 - Hd);
+  const int64_t ld = f0 < Hd ? Hd : rank;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int64_t r = r0; r < r1; ++r) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + r * ld);
+    const float c = g * rs.w[r] * c_a * rs.dcoef[r];
+    const bool m = rs.mask[r] != 0;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float t0 = c * __uint_as_float(w[i] << 16);
+      const float t1 = c * __uint_as_float(w[i] & 0xffff0000u);
+      acc[2 * i] += m ? t0 : 0.f;
+      acc[2 * i + 1] += m ? t1 : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[f0 + i] = acc[i];
+}
+
 __global__ void conf_bwd_final_kernel(int64_t F, int chunks, const float* part, float* dWc,
                                       float* db) {
   const int64_t f = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (f > F) return;
   double acc = 0.0;
+#pragma unroll 8
   for (int c = 0; c < chunks; ++c) acc += part[c * (F + 1) + f];
   if (f < F) dWc[f] = static_cast<float>(acc);
   else *db = static_cast<float>(acc);
@@ -796,7 +839,12 @@ hipError_t launch_conf_bwd(int dtype, int64_t R, int64_t Hd, int64_t rank, int c
   const int64_t F = Hd + (conf_markov ? rank : 0);
   const int64_t rows_per = (R + chunks - 1) / chunks;
   dim3 grid(static_cast<uint32_t>((F + 1 + 255) / 256), static_cast<uint32_t>(chunks));
-  if (dtype == 1)
+  if (dtype == 1 && Hd % 8 == 0) {
+    dim3 grid8(static_cast<uint32_t>((F / 8 + 1 + 255) / 256), static_cast<uint32_t>(chunks));
+    hipLaunchKernelGGL(conf_bwd_partial8_kernel, grid8, dim3(256), 0, s, R, Hd, rank, F, rows_per,
+                       static_cast<const bf16_t*>(hd), static_cast<const bf16_t*>(E), rs, g, c_a,
+                       part);
+  } else if (dtype == 1)
     hipLaunchKernelGGL(conf_bwd_partial_kernel<bf16_t>, grid, dim3(256), 0, s, R, Hd, rank, F,
                        rows_per, static_cast<const bf16_t*>(hd), static_cast<const bf16_t*>(E), rs,
                        g, c_a, part);
