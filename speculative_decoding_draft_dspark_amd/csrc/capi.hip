@@ -745,7 +745,7 @@ int dspark_confidence_logits(int64_t rows, int64_t draft_hidden, int64_t target_
   if (!hidden || !conf_w || !conf_b || !out) return DSPARK_ERR_NULL;
   if (wm && (!prev_ids || !markov_w1 || !workspace)) return DSPARK_ERR_NULL;
   if (misaligned(hidden) || misaligned(out) || misaligned(prev_ids) || misaligned(markov_w1) ||
-      misaligned(workspace))
+      misaligned(conf_w) || misaligned(workspace))
     return DSPARK_ERR_ALIGN;
   const size_t esize = dtype == DSPARK_BF16 ? 2 : 4;
   const size_t eb = up(static_cast<size_t>(rows) * markov_rank * esize);

@@ -182,29 +182,81 @@ __global__ __launch_bounds__(kSweepThreads) void l1_sweep_kernel(
   }
 }
 
-// Per supervised row: log-sum-exp of the corrected draft logits and of the
-// teacher logits from their tile statistics (the same merge as l1_sweep_kernel).
-__global__ __launch_bounds__(kSweepThreads) void lse_rows_kernel(const float2* sz, const float2* st,
-                                                                 int64_t nstat, const uint8_t* mask,
-                                                                 int has_teacher, float* lse_z,
-                                                                 float* lse_t) {
-  __shared__ float fscr[kSweepThreads / kWave];
-  __shared__ double dscr[kSweepThreads / kWave];
-  const int64_t r = blockIdx.x;
+// The bias path's merge: one wave per row, both rows' tiles in one pass.
+// Each lane folds its tiles (lane, lane + 64, ...) into a running (max m,
+// fp64 sum l of 2^(tile sum) scaled to m); the lanes merge by an xor
+// butterfly, whose pairwise merge is symmetric, so every lane ends with the
+// same value.  The draft and the teacher row go through the same code, so
+// equal statistics still give bitwise-equal log-sum-exps.
+struct RunLse {
+  float m;
+  double l;
+};
+__device__ __forceinline__ void lse_fold(RunLse& a, float2 t) {
+  if (t.x == -INFINITY) return;  // an empty tile
+  const float mn = fmaxf(a.m, t.x);
+  const double keep = a.m == -INFINITY ? 0.0 : a.l * static_cast<double>(dexp(a.m - mn));
+  a.l = keep + static_cast<double>(t.y) * static_cast<double>(dexp(t.x - mn));
+  a.m = mn;
+}
+__device__ __forceinline__ RunLse lse_wave_merge(RunLse a) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(a.m, o, kWave);
+    const double l2 = __shfl_xor(a.l, o, kWave);
+    const float mn = fmaxf(a.m, m2);
+    const double x = a.m == -INFINITY ? 0.0 : a.l * static_cast<double>(dexp(a.m - mn));
+    const double y = m2 == -INFINITY ? 0.0 : l2 * static_cast<double>(dexp(m2 - mn));
+    a.l = x + y;
+    a.m = mn;
+  }
+  return a;
+}
+
+constexpr int kLseWaves = 4;
+__global__ __launch_bounds__(kLseWaves * kWave) void lse_rows_wave_kernel(
+    int64_t R, const float2* sz, const float2* st, int64_t nstat, const uint8_t* mask,
+    int has_teacher, float* lse_z, float* lse_t) {
+  const int64_t r = blockIdx.x * static_cast<int64_t>(kLseWaves) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= R) return;
   if (!mask[r]) {
-    if (threadIdx.x == 0) { lse_z[r] = 0.f; lse_t[r] = 0.f; }
+    if (lane == 0) { lse_z[r] = 0.f; lse_t[r] = 0.f; }
     return;
   }
-  const float lz = merge_lse(sz + r * nstat, nstat, fscr, dscr);
-  const float lt = has_teacher ? merge_lse(st + r * nstat, nstat, fscr, dscr) : 0.f;
-  if (threadIdx.x == 0) { lse_z[r] = lz; lse_t[r] = lt; }
+  const float2* a = sz + r * nstat;
+  const float2* b = st + r * nstat;
+  RunLse za{-INFINITY, 0.0}, ta{-INFINITY, 0.0};
+  constexpr int U = 4;
+  for (int64_t i0 = lane; i0 < nstat; i0 += kWave * U) {
+    float2 va[U], vb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * kWave;
+      va[u] = i < nstat ? a[i] : make_float2(-INFINITY, 0.f);
+      vb[u] = (has_teacher && i < nstat) ? b[i] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      lse_fold(za, va[u]);
+      lse_fold(ta, vb[u]);
+    }
+  }
+  za = lse_wave_merge(za);
+  ta = lse_wave_merge(ta);
+  if (lane == 0) {
+    lse_z[r] = za.m + static_cast<float>(log(za.l));
+    lse_t[r] = has_teacher ? ta.m + static_cast<float>(log(ta.l)) : 0.f;
+  }
 }
 
 hipError_t launch_lse_rows(int64_t R, const float2* sz, const float2* st, int64_t nstat,
                            const uint8_t* mask, int has_teacher, RowState rs, hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lse_rows_kernel, dim3(static_cast<uint32_t>(R)), dim3(kSweepThreads), 0, s, sz,
-                     st, nstat, mask, has_teacher, rs.lse_z, rs.lse_t);
+  hipLaunchKernelGGL(lse_rows_wave_kernel,
+                     dim3(static_cast<uint32_t>((R + kLseWaves - 1) / kLseWaves)),
+                     dim3(kLseWaves * kWave), 0, s, R, sz, st, nstat, mask, has_teacher, rs.lse_z,
+                     rs.lse_t);
   return hipGetLastError();
 }
 
@@ -223,12 +275,41 @@ hipError_t launch_l1_sweep(int64_t R, int64_t V, const float* Zp, const float* T
 // Confidence logit of row r, W_c . [h ; e] + b, by one wave (lane strides,
 // then a fixed butterfly): the loss and the standalone head op share it, so
 // both give the same value for a row.
+// acc + sum over this lane's 8-element groups (lane, lane + 64, ...) of
+// a . b, bf16 pairs widened to fp32, elements in order (n % 8 == 0, a and b
+// 16-byte aligned).
+__device__ __forceinline__ float dot8_lane(const bf16_t* a, const bf16_t* b, int64_t n, int lane,
+                                           float acc) {
+#pragma unroll 4
+  for (int64_t i = static_cast<int64_t>(lane) * 8; i < n; i += 64 * 8) {
+    const uint4 x = *reinterpret_cast<const uint4*>(a + i);
+    const uint4 y = *reinterpret_cast<const uint4*>(b + i);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc += __uint_as_float(xs[k] << 16) * __uint_as_float(ys[k] << 16);
+      acc += __uint_as_float(xs[k] & 0xffff0000u) * __uint_as_float(ys[k] & 0xffff0000u);
+    }
+  }
+  return acc;
+}
+
 template <typename T>
 __device__ __forceinline__ float conf_logit_wave(int64_t r, int64_t Hd, int64_t rank,
                                                  int with_markov_conf, const T* hd, const T* E,
                                                  const T* Wc, const T* bc, int lane) {
   float acc = 0.f;
   const T* h = hd + r * Hd;
+  if (sizeof(T) == 2 && Hd % 8 == 0) {
+    // bf16: 8 consecutive elements per lane and load (16-byte aligned: the
+    // rows and Wc start 16-byte aligned and Hd, rank are multiples of 8)
+    acc = dot8_lane(reinterpret_cast<const bf16_t*>(h), reinterpret_cast<const bf16_t*>(Wc), Hd,
+                    lane, acc);
+    if (with_markov_conf)
+      acc = dot8_lane(reinterpret_cast<const bf16_t*>(E + r * rank),
+                      reinterpret_cast<const bf16_t*>(Wc + Hd), rank, lane, acc);
+    return wave_sumf(acc) + Elem<T>::to_f32(bc[0]);
+  }
   for (int64_t i = lane; i < Hd; i += 64) acc += Elem<T>::to_f32(h[i]) * Elem<T>::to_f32(Wc[i]);
   if (with_markov_conf) {
     const T* e = E + r * rank;
