@@ -52,17 +52,17 @@ def _shard_batch(b: DSparkBatch, v0: int, v1: int) -> DSparkBatch:
         aligned_target_logits=cols(b.aligned_target_logits))
 
 
-def _run_shards(d, hp, spans, conf=True):
-    b = DSparkBatch.from_workload(d, conf=conf)
-    shards = [VocabShard(_shard_batch(b, v0, v1), hp) for v0, v1 in spans]
+def _run_shards(d, hp, spans, conf=True, teacher="hidden", grad_dtype=None):
+    b = DSparkBatch.from_workload(d, teacher=teacher, conf=conf)
+    shards = [VocabShard(_shard_batch(b, v0, v1), hp, grad_dtype) for v0, v1 in spans]
     fwd, per, rep = shard_loss(shards, GS, conf_hidden_grad=conf)
     torch.cuda.synchronize()
     return b, shards, fwd, per, rep
 
 
-def _check(d, hp, spans, conf=True):
-    b, shards, fwd, per, rep = _run_shards(d, hp, spans, conf)
-    inp = oracle_inputs(d, conf=conf)
+def _check(d, hp, spans, conf=True, teacher="hidden", grad_dtype=None):
+    b, shards, fwd, per, rep = _run_shards(d, hp, spans, conf, teacher, grad_dtype)
+    inp = oracle_inputs(d, teacher=teacher, conf=conf)
     tol = TOL["bf16"]
     # (a) the oracle's per-shard protocol
     stats = [oshard.shard_stats(inp, v0, v1) for v0, v1 in spans]
@@ -108,7 +108,7 @@ def _check(d, hp, spans, conf=True):
         assert_scalar("db_c", rep["d_conf_b"].item(), gr.db_c[0], tol)
         assert_norm("dh_d", to_np(rep["d_conf_hidden"]), gr.dh_d, tol)
     # (c) the unsplit GPU path
-    _, f1, g1 = run_gpu(d, hp, GS, conf=conf)
+    _, f1, g1 = run_gpu(d, hp, GS, conf=conf, teacher=teacher, grad_dtype=grad_dtype)
     assert int(f1.num_tokens.item()) == int(fwd.num_tokens.item())
     assert int(fwd.flags.item()) == int(f1.flags.item()) == 0
     assert_scalar("loss vs unsplit", fwd.loss.item(), f1.loss.item(), 1e-5)
@@ -142,3 +142,17 @@ def test_vocab_shards_no_markov_head():
     d["eval_mask"][7 * 3 + 2:7 * 4] = 0   # one truncated block
     d["block_keep"][5] = 0                # one dropped block
     _check(d, HParams(), _cuts(wl.Vd, (1024, 512, 512)))
+
+
+@pytest.mark.parametrize("teacher,grad_dtype", [("aligned", None), ("hidden", torch.float32)],
+                         ids=["aligned-teacher", "fp32-grads"])
+def test_vocab_shards_teacher_and_grad_variants(teacher, grad_dtype):
+    """Teacher logits given directly (sliced per shard), and fp32 dz (the Markov
+    products then take G as bf16 hi + lo parts)."""
+    wl = get_workload(1)
+    say(f"[shard] {wl.name} teacher={teacher} grad_dtype={grad_dtype}")
+    d = make_inputs(wl, DEV)
+    if teacher == "aligned":
+        d["aligned"] = (d["H_t"].float() @ d["LM"].float().T).to(torch.bfloat16).contiguous()
+    _check(d, HParams(ce_alpha=0.2, l1_alpha=0.8, confidence_alpha=0.7), _cuts(wl.Vd, (16000, 16000)),
+           teacher=teacher, grad_dtype=grad_dtype)
