@@ -134,15 +134,22 @@ def _cpu_leg(wl, blocks: int):
 
 
 def _copy_probe(nbytes: int, reps: int = 3):
-    """A plain device-to-device copy of a known size (counter calibration)."""
+    """A plain device-to-device copy of a known size (counter calibration and
+    the measured HBM reference: read + write bytes over the best copy time)."""
     import torch
     n = nbytes // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
+    best = float("inf")
     for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes": n * 4, "reps": reps}), flush=True)
+        b.record()
+        b.synchronize()
+        best = min(best, a.elapsed_time(b))
+    print(json.dumps({"copy_probe_bytes": n * 4, "reps": reps, "best_ms": round(best, 4),
+                      "read_plus_write_GB/s": round(2 * n * 4 / best / 1e6, 1)}), flush=True)
 
 
 def _side_ops(args, reps: int = 20):

@@ -252,7 +252,7 @@ def _row_terms(inp: Inputs, rows: np.ndarray):
         S = np.zeros(len(rows))
         lse_t = np.zeros(len(rows))
     lse_z = (zp - lz)[:, 0]
-    return dict(e=e, p=p, s=s, S=S, ce=ce, l1=l1, y=y, lse_z=lse_z, lse_t=lse_t)
+    return dict(e=e, p=p, q=q, s=s, S=S, ce=ce, l1=l1, y=y, lse_z=lse_z, lse_t=lse_t)
 
 
 def forward(inp: Inputs, hp: HParams, row_chunk: int = 64) -> Forward:
