@@ -272,7 +272,7 @@ int dspark_build_blocks(int64_t batch, int64_t seq_len, int64_t num_blocks, int6
  * workspace is dspark_workspace_size(shape), one per shard, kept from the
  * first call to the last.  Order per step, with the collectives between:
  *   shard_fwd_stats -> lse parts [G, R, 2] gathered -> shard_merge_lse ->
- *   shard_fwd_terms -> terms [R, 3] summed over shards -> shard_fwd_finish ->
+ *   shard_fwd_terms -> terms [R, 4] summed over shards -> shard_fwd_finish ->
  *   shard_bwd -> d_embed [R, r] summed over shards -> shard_bwd_finish.
  * Asynchronous on `stream`; errors as dspark_loss_fwd. */
 
@@ -291,17 +291,18 @@ int dspark_shard_fwd_stats(const dspark_shape *shape, const dspark_hparams *hp,
 int dspark_shard_merge_lse(int64_t shards, int64_t rows, const float *lse_parts, float *lse,
                            dspark_stream_t stream);
 
-/* Step 2: with the merged lse [R, 2], terms [R, 3] fp64 = this shard's
- * (sum |p - q|, sum p sign(p - q), z'_y if the shard owns the target else 0)
- * on supervised rows, zeros elsewhere.  The sum over shards is the row's
- * (L1, S, z'_y). */
+/* Step 2: with the merged lse [R, 2], terms [R, 4] fp64 = this shard's
+ * (sum |p - q|, sum p sign(p - q), z'_y if the shard owns the target else 0,
+ * 1 if it owns the target else 0) on supervised rows, zeros elsewhere.  The
+ * sum over shards is the row's (L1, S, z'_y, number of owners). */
 int dspark_shard_fwd_terms(const dspark_shape *shape, const dspark_hparams *hp,
                            const dspark_inputs *in, void *workspace, size_t workspace_bytes,
                            const float *lse, double *terms, dspark_stream_t stream);
 
-/* Step 3: from the shard-summed terms [R, 3], CE = lse_z - z'_y, the
+/* Step 3: from the shard-summed terms [R, 4], CE = lse_z - z'_y, the
  * confidence head and the reductions: `out` as dspark_loss_fwd (identical on
- * every shard). */
+ * every shard); DSPARK_FLAG_TARGET_ID_RANGE where a supervised row's target
+ * has not exactly one owner (a global id outside the vocabulary). */
 int dspark_shard_fwd_finish(const dspark_shape *shape, const dspark_hparams *hp,
                             const dspark_inputs *in, void *workspace, size_t workspace_bytes,
                             const double *terms, dspark_fwd_out *out, dspark_stream_t stream);

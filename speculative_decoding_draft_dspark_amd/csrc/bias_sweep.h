@@ -61,8 +61,9 @@ hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, 
                             float l1_a, void* dz, bf16_t* ghi, bf16_t* glo, hipStream_t s,
                             int shard = 0);
 
-// Vocabulary shard: part [R, 3] (fp64) = this shard's L1, S and, on the shard
-// that owns the target, z'_y (0 on the others and on unsupervised rows).
+// Vocabulary shard: part [R, 4] (fp64) = this shard's L1, S and, on the shard
+// that owns the target, z'_y and 1 (0 and 0 on the others and on unsupervised
+// rows).
 hipError_t launch_bias_l1_shard(int64_t R, int64_t V, int64_t rank, int splits, int has_teacher,
                                 const double* part_l1, const double* part_s, const bf16_t* z,
                                 const bf16_t* E, const bf16_t* W2, const int32_t* tid,

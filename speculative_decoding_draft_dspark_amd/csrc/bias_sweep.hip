@@ -620,8 +620,9 @@ __global__ void l1_finish_kernel(int64_t R, int64_t V, int64_t rank, int splits,
 }
 
 // Vocabulary shard: per supervised row, this shard's L1 and S (its split
-// partials summed) and z'_y when the shard owns the target (else 0), for the
-// caller to sum over the shards; unsupervised rows: zeros.
+// partials summed), z'_y when the shard owns the target (else 0) and 1 when
+// it owns it (else 0), for the caller to sum over the shards; unsupervised
+// rows: zeros.
 __global__ void l1_shard_kernel(int64_t R, int64_t V, int64_t rank, int splits, int has_teacher,
                                 const double* pl1, const double* ps, const bf16_t* z,
                                 const bf16_t* E, const bf16_t* W2, const int32_t* tid,
@@ -630,15 +631,17 @@ __global__ void l1_shard_kernel(int64_t R, int64_t V, int64_t rank, int splits, 
   const int lane = threadIdx.x & 63;
   if (r >= R) return;
   RowFinish f{0.0, 0.0, 0.f};
+  bool own = false;
   if (rs.mask[r]) {
     const int64_t t = tid[r];
-    f = row_finish(r, R, (t >= 0 && t < V) ? t : -1, V, rank, splits, has_teacher, pl1, ps, z,
-                   E, W2, lane);
+    own = t >= 0 && t < V;
+    f = row_finish(r, R, own ? t : -1, V, rank, splits, has_teacher, pl1, ps, z, E, W2, lane);
   }
   if (lane == 0) {
-    part[3 * r] = f.l1;
-    part[3 * r + 1] = f.S;
-    part[3 * r + 2] = f.zy;
+    part[4 * r] = f.l1;
+    part[4 * r + 1] = f.S;
+    part[4 * r + 2] = f.zy;
+    part[4 * r + 3] = own ? 1.0 : 0.0;
   }
 }
 

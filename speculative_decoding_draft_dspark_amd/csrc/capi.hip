@@ -910,7 +910,7 @@ int dspark_shard_fwd_finish(const dspark_shape* shape, const dspark_hparams* hp,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const RowState rs = row_state(ws, L, d);
-  DSPARK_STAGE(kFinalize, launch_shard_set_terms(d.R, terms, rs, s));
+  DSPARK_STAGE(kFinalize, launch_shard_set_terms(d.R, terms, rs, out->flags, s));
   DSPARK_STAGE(kFinalize, launch_finalize_rows(d.dtype, d.R, d.Hd, d.r, d.conf_markov, d.conf,
                                                in->conf_hidden, ws + L.E, in->conf_w, in->conf_b,
                                                rs, out->accept_rate, out->row_terms, out->flags,

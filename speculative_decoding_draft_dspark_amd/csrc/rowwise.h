@@ -97,7 +97,9 @@ hipError_t launch_shard_merge_lse(int64_t G, int64_t R, const float* parts, floa
 // rs.lse_z, rs.lse_t from merged log-sum-exps [R, 2] (0 on unsupervised rows).
 hipError_t launch_shard_set_lse(int64_t R, int has_teacher, const float2* lse, RowState rs,
                                 hipStream_t s);
-// rs.l1, rs.S, rs.ce from the shard-summed (L1, S, z'_y) [R, 3] (fp64).
-hipError_t launch_shard_set_terms(int64_t R, const double* terms, RowState rs, hipStream_t s);
+// rs.l1, rs.S, rs.ce from the shard-summed (L1, S, z'_y, owners) [R, 4]
+// (fp64); flag bit 1 where a supervised row's owner count is not 1.
+hipError_t launch_shard_set_terms(int64_t R, const double* terms, RowState rs, uint32_t* flags,
+                                  hipStream_t s);
 
 }  // namespace dspark

@@ -1133,21 +1133,25 @@ hipError_t launch_shard_set_lse(int64_t R, int has_teacher, const float2* lse, R
   return hipGetLastError();
 }
 
-// Row state from the shard-summed terms [R, 3] (L1, S, z'_y): CE = lse_z - z'_y
-// on supervised rows, every term 0 on the others.
-__global__ void shard_set_terms_kernel(int64_t R, const double* terms, RowState rs) {
+// Row state from the shard-summed terms [R, 4] (L1, S, z'_y, owners): CE =
+// lse_z - z'_y on supervised rows, every term 0 on the others; a supervised
+// row whose target no shard or several shards own sets flag bit 1.
+__global__ void shard_set_terms_kernel(int64_t R, const double* terms, RowState rs,
+                                       uint32_t* flags) {
   const int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (r >= R) return;
   const bool m = rs.mask[r] != 0;
-  rs.l1[r] = m ? static_cast<float>(terms[3 * r]) : 0.f;
-  rs.S[r] = m ? static_cast<float>(terms[3 * r + 1]) : 0.f;
-  rs.ce[r] = m ? rs.lse_z[r] - static_cast<float>(terms[3 * r + 2]) : 0.f;
+  rs.l1[r] = m ? static_cast<float>(terms[4 * r]) : 0.f;
+  rs.S[r] = m ? static_cast<float>(terms[4 * r + 1]) : 0.f;
+  rs.ce[r] = m ? rs.lse_z[r] - static_cast<float>(terms[4 * r + 2]) : 0.f;
+  if (m && terms[4 * r + 3] != 1.0) atomicOr(flags, 1u);
 }
 
-hipError_t launch_shard_set_terms(int64_t R, const double* terms, RowState rs, hipStream_t s) {
+hipError_t launch_shard_set_terms(int64_t R, const double* terms, RowState rs, uint32_t* flags,
+                                  hipStream_t s) {
   if (R <= 0) return hipSuccess;
   hipLaunchKernelGGL(shard_set_terms_kernel, dim3(static_cast<uint32_t>((R + 255) / 256)),
-                     dim3(256), 0, s, R, terms, rs);
+                     dim3(256), 0, s, R, terms, rs, flags);
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@ and shard-local target ids; the row partials it returns merge exactly into
 the unsplit loss (the log-sum-exp of a softmax is the log-sum-exp of its
 parts' log-sum-exps, and L1, S and z'_y are sums over columns).  Between the
 steps the caller runs the collectives of its tensor-parallel group: gather the
-[R, 2] log-sum-exp parts, sum the [R, 3] terms, sum the [R, r] embedding
+[R, 2] log-sum-exp parts, sum the [R, 4] terms, sum the [R, r] embedding
 gradients.  ``shard_loss`` runs every shard of a group in one process with
 those collectives done by stacking and summing tensors.
 """
@@ -50,8 +50,8 @@ class VocabShard:
         return out
 
     def fwd_terms(self, lse: torch.Tensor, stream=None) -> torch.Tensor:
-        """[R, 3] fp64 (L1, S, z'_y if owned) of this shard, given the merged lse."""
-        out = torch.empty(self.b.R, 3, dtype=torch.float64, device=self.dev)
+        """[R, 4] fp64 (L1, S, z'_y if owned, 1 if owned) of this shard, given the merged lse."""
+        out = torch.empty(self.b.R, 4, dtype=torch.float64, device=self.dev)
         st = capi.lib().dspark_shard_fwd_terms(*self._common(), _ptr(lse), _ptr(out),
                                                _stream(stream))
         capi.check(st, "dspark_shard_fwd_terms")

@@ -83,6 +83,9 @@ def _check(d, hp, spans, conf=True, teacher="hidden", grad_dtype=None):
         ref = terms_ref[g]
         got = to_np(shards[g].fwd_terms(lse))
         assert not np.any(got[~valid])
+        y = inp.target_ids.astype(np.int64)
+        owned = valid & (y >= v0) & (y < v1)
+        assert np.array_equal(got[:, 3], owned.astype(np.float64)), "owner column"
         for j, k in enumerate(("L1_g", "S_g", "z'_y")):
             if np.any(ref[:, j]):
                 assert_norm(f"shard {g} {k}", got[:, j], ref[:, j], tol)
@@ -156,3 +159,22 @@ def test_vocab_shards_teacher_and_grad_variants(teacher, grad_dtype):
         d["aligned"] = (d["H_t"].float() @ d["LM"].float().T).to(torch.bfloat16).contiguous()
     _check(d, HParams(ce_alpha=0.2, l1_alpha=0.8, confidence_alpha=0.7), _cuts(wl.Vd, (16000, 16000)),
            teacher=teacher, grad_dtype=grad_dtype)
+
+
+def test_vocab_shards_flag_a_target_no_shard_owns():
+    """A supervised row whose global target id lies outside the vocabulary has
+    no owner: the finish sets DSPARK_FLAG_TARGET_ID_RANGE, as the unsplit loss
+    does for an out-of-range id."""
+    wl = get_workload(1)
+    say(f"[shard] {wl.name} unowned target")
+    d = make_inputs(wl, DEV)
+    spans = _cuts(wl.Vd, (16000, 16000))
+    hp = HParams()
+    _, _, fwd, _, _ = _run_shards(d, hp, spans)
+    assert int(fwd.flags.item()) == 0
+    m = oracle.effective_mask(d["eval_mask"].cpu().numpy(), d["block_keep"].cpu().numpy(),
+                              wl.B, wl.N, wl.K)
+    r = int(np.nonzero(m)[0][3])
+    d["target_ids"][r] = wl.Vd + 5
+    _, _, fwd, _, _ = _run_shards(d, hp, spans)
+    assert int(fwd.flags.item()) & 1
