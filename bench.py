@@ -152,6 +152,54 @@ def _copy_probe(nbytes: int, reps: int = 3):
                       "read_plus_write_GB/s": round(2 * n * 4 / best / 1e6, 1)}), flush=True)
 
 
+def _vocab_shard(args, reps: int = 10):
+    """One tensor-parallel rank's share of the loss: the large-batch rows over
+    the first of G vocabulary shards (widths multiples of 32, the last shard
+    takes the remainder), every shard step timed on this GPU with the
+    exchanges left out (a single shard merges with itself).  Prints one JSON
+    line; not the benchmark line."""
+    import dataclasses
+
+    import torch
+
+    from speculative_decoding_draft_dspark_amd import DSparkBatch, HParams, _capi
+    from speculative_decoding_draft_dspark_amd.shard import VocabShard, merge_lse
+    from workloads import get_workload, make_inputs
+
+    _capi.lib()
+    wl = get_workload(args.workload)
+    G = args.vocab_shards
+    Vs = wl.Vd // G // 32 * 32
+    d = make_inputs(wl, "cuda:0")
+    b = DSparkBatch.from_workload(d)
+    sb = dataclasses.replace(
+        b, draft_logits=b.draft_logits[:, :Vs].contiguous(), markov_w2=b.markov_w2[:Vs].contiguous(),
+        lm_head=b.lm_head[:Vs].contiguous())
+    del d, b
+    sh = VocabShard(sb, HParams())
+
+    def step():
+        lse = merge_lse(sh.fwd_stats()[None])
+        sh.fwd_finish(sh.fwd_terms(lse), row_outputs=False)
+        g = sh.bwd(1.0 / wl.R)
+        sh.bwd_finish(g.get("d_embed"), 1.0 / wl.R)
+
+    step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(e) / reps
+    print(json.dumps({"mode": "vocab-shard", "workload": wl.name, "shards": G, "shard_vocab": Vs,
+                      "rows": wl.R, "ms_per_step_one_shard": round(ms, 4),
+                      "rows_per_s_if_exchanges_free": round(wl.R / (ms * 1e-3), 1),
+                      "reps": reps}), flush=True)
+
+
 def _side_ops(args, reps: int = 20):
     """Times the standalone ops beside the loss (head ops at the large-batch
     shapes, batch construction for its rows) and prints one JSON line; not the
@@ -216,6 +264,9 @@ def main():
                          "logits instead of recomputing the Markov bias in each sweep")
     ap.add_argument("--side-ops", action="store_true",
                     help="only time the standalone head ops and batch construction")
+    ap.add_argument("--vocab-shards", type=int, default=0, metavar="G",
+                    help="only time one of G draft-vocabulary shards of the workload (one "
+                         "tensor-parallel rank's share, exchanges excluded)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (rocprofv3 byte-counter calibration)")
     args = ap.parse_args()
@@ -230,6 +281,9 @@ def main():
         return
     if args.side_ops:
         _side_ops(args)
+        return
+    if args.vocab_shards:
+        _vocab_shard(args)
         return
     wl, elapsed, stages = _gpu_leg(args)
     R, V, H, r = wl.R, wl.Vd, wl.H, wl.r
