@@ -128,7 +128,14 @@ def _cpu_leg(wl, blocks: int):
     oracle.backward(inp, hp, grad_scale=1.0 / wl.R)
     dt = time.perf_counter() - t0
     rows = blocks * wl.K
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):  # pragma: no cover
+        pass
     return {"value": rows / dt, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+            "cpu": cpu,
             "sample": f"{blocks} whole blocks ({rows} rows) of {wl.name}, fwd+bwd in "
                       f"{dt:.1f}s, numpy float64"}
 
