@@ -813,6 +813,7 @@ int dspark_shard_fwd_stats(const dspark_shape* shape, const dspark_hparams* hp,
   int st = shard_setup(shape, hp, in, workspace, workspace_bytes, &d, &L, &teacher);
   if (st) return st;
   if (!lse_part || !flags) return DSPARK_ERR_NULL;
+  if (misaligned(lse_part)) return DSPARK_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const RowState rs = row_state(ws, L, d);
@@ -862,6 +863,7 @@ int dspark_shard_merge_lse(int64_t shards, int64_t rows, const float* lse_parts,
     return DSPARK_ERR_SHAPE;
   if (rows == 0) return DSPARK_OK;
   if (!lse_parts || !lse) return DSPARK_ERR_NULL;
+  if (misaligned(lse_parts) || misaligned(lse)) return DSPARK_ERR_ALIGN;
   return hip_status(launch_shard_merge_lse(shards, rows, lse_parts, lse,
                                            static_cast<hipStream_t>(stream)));
 }
@@ -875,6 +877,7 @@ int dspark_shard_fwd_terms(const dspark_shape* shape, const dspark_hparams* hp,
   int st = shard_setup(shape, hp, in, workspace, workspace_bytes, &d, &L, &teacher);
   if (st) return st;
   if (!lse || !terms) return DSPARK_ERR_NULL;
+  if (misaligned(lse) || misaligned(terms)) return DSPARK_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const RowState rs = row_state(ws, L, d);
@@ -906,7 +909,8 @@ int dspark_shard_fwd_finish(const dspark_shape* shape, const dspark_hparams* hp,
   if (st) return st;
   if (!terms) return DSPARK_ERR_NULL;
   if (!out || !out->loss || !out->num_tokens || !out->pairs || !out->flags) return DSPARK_ERR_NULL;
-  if (misaligned(out->accept_rate) || misaligned(out->row_terms)) return DSPARK_ERR_ALIGN;
+  if (misaligned(terms) || misaligned(out->accept_rate) || misaligned(out->row_terms))
+    return DSPARK_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const RowState rs = row_state(ws, L, d);

@@ -220,3 +220,7 @@ def test_vocab_shard_validation_codes(L):
     assert L.dspark_shard_merge_lse(2, -1, FAKE, FAKE, None) == E["ERR_SHAPE"]
     assert L.dspark_shard_merge_lse(2, 10, None, FAKE, None) == E["ERR_NULL"]
     assert L.dspark_shard_merge_lse(2, 0, None, None, None) == E["OK"]
+    assert L.dspark_shard_merge_lse(2, 10, FAKE + 8, FAKE, None) == E["ERR_ALIGN"]
+    assert stats(good, lse=FAKE + 8) == E["ERR_ALIGN"]
+    assert L.dspark_shard_fwd_terms(C.byref(good), C.byref(hp), C.byref(inp), FAKE, ws, FAKE,
+                                    FAKE + 8, None) == E["ERR_ALIGN"]
