@@ -264,7 +264,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large-batch-r14336-v151936")
-    ap.add_argument("--cpu-blocks", type=int, default=60)
+    ap.add_argument("--cpu-blocks", type=int, default=72)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--store-draft-logits", action="store_true",
                     help="DSPARK_OPT_STORE_DRAFT_LOGITS: materialise the fp32 corrected draft "
