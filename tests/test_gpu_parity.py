@@ -104,6 +104,16 @@ def test_ragged_tiles_and_tails(dtype):
     _full_parity(d, HParams(ce_alpha=0.25, l1_alpha=0.75, confidence_alpha=0.6), TOL[dtype])
 
 
+def test_confidence_hidden_not_a_multiple_of_8():
+    """bf16 with Hd % 8 != 0: the confidence head's per-element paths (no
+    16-byte groups) in the logit, its weight gradient and dh_d."""
+    wl = Workload("ragged-bf16-hd44", B=1, N=5, K=7, Vd=1000, Vt=1017, H=40, Hd=44, r=24,
+                  dtype="bf16", seed=12, recipe="tiny")
+    say(f"[parity] {wl.name}")
+    d = make_inputs(wl, DEV)
+    _full_parity(d, HParams(ce_alpha=0.3, l1_alpha=0.7, confidence_alpha=0.9), TOL["bf16"])
+
+
 def test_aligned_teacher_and_no_decay():
     wl = _ragged("f32", V=520, r=8, H=16, N=3, seed=3)
     say(f"[parity] {wl.name} aligned teacher")
