@@ -226,6 +226,42 @@ def confidence_logit(inp: Inputs, rows: np.ndarray, e: np.ndarray) -> np.ndarray
     return c
 
 
+# --------------------------------------------------------------------------- heads alone
+
+def markov_head_logits(inp: Inputs, valid) -> np.ndarray:
+    """The Markov head used on its own: corrected logits per slot.
+
+    [HEADS] "Inputs and Outputs": the head adds the low-rank previous-token
+    bias W2 W1[prev] to the base logits of the valid slots, and both auxiliary
+    heads output zero for the slots that are not valid.  Reading R21: the
+    whole row of an invalid slot is zero.  Without a Markov head (rank 0) a
+    valid row is the base logits themselves.  Invalid rows are never read.
+    """
+    v = np.asarray(valid).reshape(-1) != 0
+    out = np.zeros(inp.z.shape, dtype=F64)
+    rows = np.nonzero(v)[0]
+    if len(rows):
+        out[rows] = draft_logits_corrected(inp, rows, markov_embedding(inp, rows))
+    return out
+
+
+def confidence_head_logits(inp: Inputs, valid) -> np.ndarray:
+    """The confidence head used on its own: one logit per slot.
+
+    [HEADS] "Inputs and Outputs" (input: the hidden state, with the Markov
+    embedding appended when with_markov is set; zero on invalid slots) and
+    "Checkpoint Contract" (``proj.weight`` [1, hidden (+ rank)], ``proj.bias``
+    [1]).  Invalid rows are never read and give 0.
+    """
+    v = np.asarray(valid).reshape(-1) != 0
+    out = np.zeros(inp.h_d.shape[0], dtype=F64)
+    rows = np.nonzero(v)[0]
+    if len(rows):
+        e = markov_embedding(inp, rows) if (inp.with_markov_conf and inp.has_markov) else None
+        out[rows] = confidence_logit(inp, rows, e)
+    return out
+
+
 # --------------------------------------------------------------------------- forward
 
 def _row_terms(inp: Inputs, rows: np.ndarray):

@@ -1,0 +1,91 @@
+"""GPU parity of the standalone acceptance report (dspark_accept_report,
+through the C ABI) against the oracle's accept_report ([API]
+``_acceptance_report``: per-slot acceptance summed over supervised slots, and
+per kept block the running product over the block plus one for the anchor).
+
+Denominators are counts and must match exactly; numerators are fp64 sums in
+another order: 1e-12 relative.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_draft_dspark_amd import dspark_accept_report
+from tests.gpu_common import run_gpu, say
+from speculative_decoding_draft_dspark_amd import HParams
+from workloads import get_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NUM_TOL = 1e-12
+
+
+def _case(B, N, K, seed, keep_mode):
+    rng = np.random.default_rng(seed)
+    R = B * N * K
+    acc = rng.uniform(0.0, 1.0, R).astype(np.float32)
+    acc[rng.choice(R, size=max(1, R // 17), replace=False)] = 1.0
+    acc[rng.choice(R, size=max(1, R // 23), replace=False)] = 0.0
+    ev = np.ones(R, np.uint8)
+    blocks = rng.permutation(B * N)
+    # truncated prefixes, and non-prefix rows (a gap followed by ones)
+    for b in blocks[: (B * N) // 3]:
+        ev[b * K + rng.integers(0, K):(b + 1) * K] = 0
+    for b in blocks[(B * N) // 3: (B * N) // 2]:
+        if K > 2:
+            ev[b * K + 1] = 0
+    keep = None
+    if keep_mode == "dropped":
+        keep = np.ones(B * N, np.uint8)
+        keep[blocks[-1]] = 0
+        keep[blocks[-2]] = 0
+    # garbage accept rates on unsupervised slots must not matter
+    m = oracle.effective_mask(ev, keep, B, N, K)
+    acc_bad = acc.copy()
+    acc_bad[m == 0] = np.nan
+    return acc, acc_bad, ev, keep
+
+
+@pytest.mark.parametrize("B,N,K,keep_mode", [(2, 16, 7, "none"), (2, 16, 7, "dropped"),
+                                            (3, 11, 5, "dropped"), (1, 300, 1, "dropped"),
+                                            (4, 64, 7, "none")])
+def test_accept_report_against_oracle(B, N, K, keep_mode):
+    say(f"[accept] B={B} N={N} K={K} keep={keep_mode}")
+    acc, acc_bad, ev, keep = _case(B, N, K, 7 + B * N + K, keep_mode)
+    ref = oracle.accept_report(acc.astype(np.float64), ev, keep, B, N, K)
+    kt = None if keep is None else torch.from_numpy(keep).to(DEV)
+    for a in (acc, acc_bad):
+        out = dspark_accept_report(torch.from_numpy(a).to(DEV), torch.from_numpy(ev).to(DEV), kt,
+                                   B, N, K)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert o[1] == ref[1] and o[3] == ref[3], (o, ref)
+        for i in (0, 2):
+            assert abs(o[i] - ref[i]) <= NUM_TOL * abs(ref[i]), (i, o[i], ref[i])
+
+
+def test_accept_report_matches_the_loss_pairs():
+    """On a forward's own accept rates and masks the standalone report equals
+    the loss's accept and tau pairs."""
+    wl = get_workload(1)
+    say(f"[accept] against the forward pairs of {wl.name}")
+    d = make_inputs(wl, DEV)
+    d["block_keep"][5] = 0
+    d["eval_mask"][3 * 7 + 2] = 0          # a gap in a block: the prefix stops there
+    _, f, _ = run_gpu(d, HParams(), 1.0, bwd=False)
+    out = dspark_accept_report(f.accept_rate, d["eval_mask"], d["block_keep"], wl.B, wl.N, wl.K)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    p = f.pairs.cpu().numpy()
+    assert o[1] == p[3, 1] and o[3] == p[4, 1]
+    assert abs(o[0] - p[3, 0]) <= NUM_TOL * abs(p[3, 0])
+    assert abs(o[2] - p[4, 0]) <= NUM_TOL * abs(p[4, 0])
+    ref = oracle.accept_report(f.accept_rate.cpu().double().numpy(), d["eval_mask"].cpu().numpy(),
+                               d["block_keep"].cpu().numpy(), wl.B, wl.N, wl.K)
+    assert o[1] == ref[1] and o[3] == ref[3]
+    assert abs(o[2] - ref[2]) <= NUM_TOL * abs(ref[2])

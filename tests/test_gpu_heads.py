@@ -56,11 +56,8 @@ def test_markov_logits_parity(dtype, rank):
     inp = oracle.Inputs(B=1, N=1, K=R, z=_f64(z), target_ids=np.zeros(R, np.int32),
                         eval_mask=valid.numpy(), prev_ids=prev.numpy(),
                         W1=None if W1 is None else _f64(W1), W2=None if W2 is None else _f64(W2))
-    rows = np.arange(R)
     v = valid.numpy().astype(bool)
-    e = oracle.markov_embedding(inp, rows)
-    ref = oracle.draft_logits_corrected(inp, rows, e)
-    ref[~v] = 0.0  # both heads return zero on invalid slots
+    ref = oracle.markov_head_logits(inp, valid.numpy())  # zero rows on invalid slots
     err = normwise(got, ref)
     assert err <= HEAD_TOL, f"z' normwise rel err {err:.3e}"
     assert np.all(np.abs(got - ref) <= HEAD_TOL * (1.0 + np.abs(ref)))
@@ -89,10 +86,7 @@ def test_confidence_logits_parity(dtype, with_markov, masked):
                         eval_mask=v.astype(np.uint8), prev_ids=prev.numpy(), W1=_f64(W1),
                         W2=np.zeros((8, r)), h_d=_f64(h), W_c=_f64(Wc), b_c=_f64(bc),
                         with_markov_conf=with_markov)
-    rows = np.arange(R)
-    e = oracle.markov_embedding(inp, rows)
-    ref = oracle.confidence_logit(inp, rows, e)
-    ref[~v] = 0.0
+    ref = oracle.confidence_head_logits(inp, v.astype(np.uint8))  # 0 on invalid slots
     assert not np.any(got[~v])
     err = normwise(got, ref)
     assert err <= HEAD_TOL, f"conf logit normwise rel err {err:.3e}"

@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import oracle
-from speculative_decoding_draft_dspark_amd import HParams, DSparkBatch, dspark_loss_fwd
+from speculative_decoding_draft_dspark_amd import (HParams, DSparkBatch, dspark_loss_fwd,
+                                                   dspark_workspace_size)
 from tests.common import oracle_inputs
 from tests.gpu_common import (TOL, assert_norm, assert_scalar, compare_forward, normwise, ohp,
                               run_gpu, say, to_np)
@@ -28,14 +29,14 @@ GS = 0.0125  # upstream gradient of the loss numerator
 
 
 def _full_parity(d, hp, tol, grad_tol=None, teacher="hidden", conf=True, grad_dtype=None,
-                 stored=False):
+                 stored=False, row_chunk=64):
     grad_tol = grad_tol or tol
     b, f, g = run_gpu(d, hp, GS, teacher=teacher, conf=conf, grad_dtype=grad_dtype,
                       stored=stored)
     inp = oracle_inputs(d, teacher=teacher, conf=conf)
-    fw = oracle.forward(inp, ohp(hp))
+    fw = oracle.forward(inp, ohp(hp), row_chunk=row_chunk)
     compare_forward(f, fw, tol)
-    gr = oracle.backward(inp, ohp(hp), grad_scale=GS)
+    gr = oracle.backward(inp, ohp(hp), grad_scale=GS, row_chunk=row_chunk)
     assert_norm("dz", to_np(g["d_draft_logits"]), gr.dz, grad_tol)
     if inp.has_markov:
         assert_norm("dW1", to_np(g["d_markov_w1"]), gr.dW1, grad_tol)
@@ -296,15 +297,48 @@ def test_full_size_sampled_rows(idx, count, stored):
     assert p[4, 1] == wl.B * wl.N
 
 
-@pytest.mark.parametrize("idx", [2, 3])
-def test_full_size_gradients_additive_and_sub_batch_parity(idx):
-    """Weight gradients: a sub-batch matches the oracle; the full-size launch equals
-    the sum of launches over a partition of its blocks (data-parallel additivity)."""
+def _assert_default_path(d, f):
+    """The launch took the benchmark's path: the Markov bias recomputed in
+    every sweep, which the library takes only together with the backward
+    products that read G in place.  The stored-logits option then adds the
+    4 R Vd bytes of fp32 corrected logits to the workspace (less the R Vd / 4
+    of sign bits it does not need); where it does not apply it changes
+    nothing, so a smaller default workspace shows the path."""
+    wl = d["workload"]
+    assert wl.R % 32 == 0 and wl.Vd % 32 == 0
+    ws = f.workspace.numel()
+    b = DSparkBatch.from_workload(d)
+    assert ws == dspark_workspace_size(b)
+    assert dspark_workspace_size(b, store_draft_logits=True) - ws >= 3 * wl.R * wl.Vd
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_shaped_full_oracle_parity():
+    """The Qwen3-8B-shaped workload (R = 1792, V = 151936) in full against the
+    oracle: totals, pairs, every per-row term, dz and every weight gradient,
+    on the benchmark's launch path."""
+    wl = get_workload(2)
+    say(f"[parity] {wl.name} full oracle")
+    d = make_inputs(wl, DEV)
+    hp = HParams()
+    f, g, fw, gr = _full_parity(d, hp, TOL["bf16"], row_chunk=256)
+    _assert_default_path(d, f)
+    assert int(f.flags.item()) == 0
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("idx,sub_blocks", [(2, 32), (3, 64)])
+def test_full_size_gradients_additive_and_sub_batch_parity(idx, sub_blocks):
+    """Weight gradients at V = 151936: a sub-batch of whole blocks (rows a
+    multiple of 32, so the same launch path as the benchmark) matches the
+    oracle in full; the full-size launch equals the sum of launches over a
+    partition of its blocks (data-parallel additivity)."""
     wl = get_workload(idx)
-    say(f"[parity] {wl.name} gradient additivity")
+    say(f"[parity] {wl.name} gradient additivity, {sub_blocks}-block oracle sub-batch")
     d = make_inputs(wl, DEV)
     hp = HParams()
     _, f, g = run_gpu(d, hp, GS)
+    _assert_default_path(d, f)
     nb = wl.B * wl.N
     parts = np.array_split(np.arange(nb), 4)
     acc = {k: torch.zeros_like(v, dtype=torch.float64) for k, v in g.items()
@@ -316,17 +350,22 @@ def test_full_size_gradients_additive_and_sub_batch_parity(idx):
         loss += fs.loss.item()
         for k in acc:
             acc[k] += gs[k].double()
-        if i == 0:
-            few = subset_blocks(d, blocks[:8])
-            _, fo, go = run_gpu(few, hp, GS)
-            inp = oracle_inputs(few)
-            fw = oracle.forward(inp, ohp(hp))
-            compare_forward(fo, fw, TOL["bf16"])
-            gr = oracle.backward(inp, ohp(hp), grad_scale=GS)
-            assert_norm("sub dW1", to_np(go["d_markov_w1"]), gr.dW1, TOL["bf16"])
-            assert_norm("sub dW2", to_np(go["d_markov_w2"]), gr.dW2, TOL["bf16"])
-            assert_norm("sub dW_c", to_np(go["d_conf_w"]), gr.dW_c, TOL["bf16"])
-            assert_norm("sub dz", to_np(go["d_draft_logits"]), gr.dz, TOL["bf16"])
+        del fs, gs
     assert_scalar("loss additivity", f.loss.item(), loss, 1e-9)
     for k in acc:
         assert_norm(k + " additivity", to_np(g[k]), to_np(acc[k]), 1e-4)
+    del f, g, acc
+    # oracle sub-batch: spread over the whole batch, truncated blocks included
+    rng = np.random.default_rng(200 + idx)
+    few = subset_blocks(d, np.sort(rng.choice(nb, size=sub_blocks, replace=False)))
+    _, fo, go = run_gpu(few, hp, GS)
+    _assert_default_path(few, fo)
+    inp = oracle_inputs(few)
+    fw = oracle.forward(inp, ohp(hp), row_chunk=224)
+    compare_forward(fo, fw, TOL["bf16"])
+    gr = oracle.backward(inp, ohp(hp), grad_scale=GS, row_chunk=224)
+    assert_norm("sub dz", to_np(go["d_draft_logits"]), gr.dz, TOL["bf16"])
+    assert_norm("sub dW1", to_np(go["d_markov_w1"]), gr.dW1, TOL["bf16"])
+    assert_norm("sub dW2", to_np(go["d_markov_w2"]), gr.dW2, TOL["bf16"])
+    assert_norm("sub dW_c", to_np(go["d_conf_w"]), gr.dW_c, TOL["bf16"])
+    assert_scalar("sub db_c", go["d_conf_b"].item(), gr.db_c[0], TOL["bf16"])

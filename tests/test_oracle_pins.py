@@ -373,7 +373,8 @@ def test_finite_differences_every_element():
 
 # ----------------------------------------------------------------- planted mistakes
 
-@pytest.mark.parametrize("mutation", ["tv_half", "no_decay", "sign_flip", "no_cumprod", "label_grad"])
+@pytest.mark.parametrize("mutation", ["tv_half", "no_decay", "sign_flip", "no_cumprod", "label_grad",
+                                      "rows_position_index", "head_invalid_passthrough"])
 def test_pins_catch_planted_oracle_mistakes(monkeypatch, mutation):
     """Each plausible mistake planted in the oracle makes at least one pin fail."""
     import oracle.dspark_oracle as od
@@ -401,6 +402,28 @@ def test_pins_catch_planted_oracle_mistakes(monkeypatch, mutation):
         monkeypatch.setattr(od, "effective_mask", bad_mask)
         monkeypatch.setattr(oracle, "effective_mask", bad_mask)
         pin = test_cumprod_mask_example
+    elif mutation == "rows_position_index":
+        # the subset's decay weights taken from list positions instead of row ids
+        orig = od.forward_rows
+        def bad(inp, hp, rows):
+            out = orig(inp, hp, rows)
+            dec = od.decay_weights(inp.K, hp.loss_decay_gamma)
+            out["w"] = np.where(out["m"] != 0, dec[np.arange(len(rows)) % inp.K], 0.0)
+            return out
+        monkeypatch.setattr(od, "forward_rows", bad)
+        monkeypatch.setattr(oracle, "forward_rows", bad)
+        pin = test_forward_rows_equal_the_rows_of_forward
+    elif mutation == "head_invalid_passthrough":
+        # invalid slots passed through (z) instead of zeroed
+        orig = od.markov_head_logits
+        def bad(inp, valid):
+            out = orig(inp, valid)
+            v = np.asarray(valid) == 0
+            out[v] = inp.z[v]
+            return out
+        monkeypatch.setattr(od, "markov_head_logits", bad)
+        monkeypatch.setattr(oracle, "markov_head_logits", bad)
+        pin = lambda: test_markov_head_alone(5)
     else:
         orig_sig = od.sigmoid
         monkeypatch.setattr(od, "sigmoid", lambda c: orig_sig(c) + 0.01)
@@ -536,3 +559,126 @@ def test_vocab_shard_owner_of_the_target_is_unique():
     owned = np.stack([p[:, 2] != 0 for p in parts])
     m = oracle.effective_mask(inp.eval_mask, inp.block_keep, inp.B, inp.N, inp.K) != 0
     assert np.all(owned[:, m].sum(axis=0) == 1)
+
+
+# ----------------------------------------------------------------- row subsets and heads
+
+def _ragged_problem():
+    """Truncated prefixes, a non-prefix eval row, a dropped block (B=2, N=3, K=7)."""
+    prefix = np.array([1, 1, 1, 0, 0, 0, 0] + [1] * 7 + [1, 0, 1, 1, 1, 1, 1]
+                      + [1] * 7 + [1, 1, 1, 1, 1, 0, 0] + [1] * 7)
+    inp = tiny_inputs(V=29, H=6, r=5, B=2, N=3, prefix=prefix)
+    inp.block_keep = np.array([1, 1, 1, 1, 0, 1], dtype=np.uint8)
+    return inp
+
+
+def test_forward_rows_equal_the_rows_of_forward():
+    """forward_rows / grad_rows on any subset of rows, in any order, equal the
+    matching rows of forward / backward (rows are independent)."""
+    inp = _ragged_problem()
+    hp = HParams(ce_alpha=0.2, l1_alpha=0.8, confidence_alpha=0.6)
+    fw = oracle.forward(inp, hp)
+    gr = oracle.backward(inp, hp, grad_scale=0.3)
+    rng = np.random.default_rng(3)
+    for rows in (np.arange(inp.R), rng.permutation(inp.R), rng.permutation(inp.R)[:9],
+                 np.array([inp.R - 1, 0, 15, 15])):
+        fr = oracle.forward_rows(inp, hp, rows)
+        for k in ("ce", "l1", "S", "bce", "conf_logit", "lse_z", "lse_t", "accept", "w", "m"):
+            ref = getattr(fw, k)[rows]
+            assert np.allclose(fr[k], ref, rtol=1e-13, atol=1e-15), k
+        dz = oracle.grad_rows(inp, hp, rows, grad_scale=0.3)
+        assert np.allclose(dz, gr.dz[rows], rtol=1e-13, atol=1e-16)
+    # the decay weights of the rows follow the slot of each row, not its position in the list
+    rows = np.array([5, 3, 1])
+    assert np.allclose(oracle.forward_rows(inp, hp, rows)["w"],
+                       oracle.decay_weights(7, hp.loss_decay_gamma)[[5, 3, 1]] * (fw.m[rows] != 0))
+
+
+def _torch_conf_only(inp, rows):
+    """F.linear of the confidence features: [h] alone, or [h ; W1[prev]]."""
+    h = _t(inp.h_d[rows])
+    if inp.with_markov_conf and inp.has_markov:
+        h = torch.cat([h, F.embedding(torch.tensor(inp.prev_ids[rows].astype(np.int64)),
+                                      _t(inp.W1))], 1)
+    return F.linear(h, _t(inp.W_c), _t(inp.b_c)).squeeze(1).numpy()
+
+
+def test_confidence_logit_without_markov_features():
+    """with_markov=False: proj [1, hidden] over the hidden state alone ([HEADS]
+    "Checkpoint Contract"); the embedding gets no confidence gradient."""
+    inp = _ragged_problem()
+    Hd = inp.h_d.shape[1]
+    nm = clone_inputs(inp, with_markov_conf=False, W_c=inp.W_c[:, :Hd].copy())
+    hp = HParams(ce_alpha=0.2, l1_alpha=0.8, confidence_alpha=0.6)
+    fw = oracle.forward(nm, hp)
+    v = np.nonzero(fw.m)[0]
+    assert np.allclose(fw.conf_logit[v], _torch_conf_only(nm, v), rtol=1e-13)
+    assert not np.any(fw.conf_logit[fw.m == 0])
+    # autograd of the same objective with the hidden-only head
+    B, N, K = nm.B, nm.N, nm.K
+    m = torch.tensor(fw.m, dtype=torch.float64)
+    z = _t(nm.z).requires_grad_(); W1 = _t(nm.W1).requires_grad_(); W2 = _t(nm.W2).requires_grad_()
+    Wc = _t(nm.W_c).requires_grad_(); bc = _t(nm.b_c).requires_grad_(); hd = _t(nm.h_d).requires_grad_()
+    e = W1[torch.tensor(nm.prev_ids.astype(np.int64))]
+    zp = z + F.linear(e, W2)
+    tl = F.linear(_t(nm.H_t), _t(nm.LM))
+    ce = F.cross_entropy(zp, torch.tensor(nm.target_ids.astype(np.int64)), reduction="none")
+    l1 = (F.softmax(zp, -1) - F.softmax(tl, -1)).abs().sum(-1)
+    acc = (1 - 0.5 * l1).clamp(0, 1).detach()
+    c = F.linear(hd, Wc, bc).squeeze(1)
+    bce = F.binary_cross_entropy_with_logits(c, acc, reduction="none")
+    w = m * torch.exp(-(torch.arange(nm.R) % K).double() / hp.loss_decay_gamma)
+    term = hp.ce_alpha * ce + hp.l1_alpha * l1 + hp.confidence_alpha * bce
+    loss = torch.where(m != 0, w * term, torch.zeros_like(term)).sum()
+    (loss * 0.3).backward()
+    assert fw.loss == pytest.approx(float(loss.detach()), rel=1e-13)
+    gr = oracle.backward(nm, hp, grad_scale=0.3)
+    for k, ref in (("dz", z.grad), ("dW1", W1.grad), ("dW2", W2.grad), ("dW_c", Wc.grad),
+                   ("db_c", bc.grad), ("dh_d", hd.grad)):
+        mine = getattr(gr, k)
+        assert mine.shape == tuple(ref.shape) or mine.size == ref.numel(), k
+        assert np.allclose(mine, ref.numpy().reshape(mine.shape), rtol=1e-10, atol=1e-14), k
+
+
+@pytest.mark.parametrize("rank", [5, 0])
+def test_markov_head_alone(rank):
+    """The Markov head on its own: z + W2(W1[prev]) on valid slots ([TS132]
+    "Testing": the bias equals W2 applied to W1[prev]); zero rows on invalid
+    slots, never read there ([HEADS] "Inputs and Outputs")."""
+    inp = _ragged_problem()
+    if rank == 0:
+        inp = clone_inputs(inp, W1=None, W2=None, prev_ids=None)
+    valid = (np.arange(inp.R) % 3 != 1).astype(np.uint8)
+    out = oracle.markov_head_logits(inp, valid)
+    v = valid != 0
+    ref = _t(inp.z[v])
+    if rank:
+        ref = ref + F.linear(F.embedding(torch.tensor(inp.prev_ids[v].astype(np.int64)),
+                                         _t(inp.W1)), _t(inp.W2))
+    assert np.allclose(out[v], ref.numpy(), rtol=1e-14, atol=1e-15)
+    assert not np.any(out[~v])
+    bad = clone_inputs(inp)
+    bad.z[~v] = np.nan
+    if rank:
+        bad.prev_ids[~v] = -7
+    assert np.array_equal(oracle.markov_head_logits(bad, valid), out)
+
+
+@pytest.mark.parametrize("with_markov", [True, False])
+def test_confidence_head_alone(with_markov):
+    inp = _ragged_problem()
+    Hd = inp.h_d.shape[1]
+    if not with_markov:
+        inp = clone_inputs(inp, with_markov_conf=False, W_c=inp.W_c[:, :Hd].copy())
+    valid = (np.arange(inp.R) % 4 != 2).astype(np.uint8)
+    v = valid != 0
+    out = oracle.confidence_head_logits(inp, valid)
+    assert np.allclose(out[v], _torch_conf_only(inp, np.nonzero(v)[0]), rtol=1e-13)
+    assert not np.any(out[~v])
+    bad = clone_inputs(inp)
+    bad.h_d[~v] = np.inf
+    bad.prev_ids[~v] = -3
+    assert np.array_equal(oracle.confidence_head_logits(bad, valid), out)
+    # with the loss's own mask the head is the loss's confidence logit
+    fw = oracle.forward(inp, HParams())
+    assert np.allclose(oracle.confidence_head_logits(inp, fw.m), fw.conf_logit, rtol=1e-14)
