@@ -63,7 +63,8 @@ enum {
   DSPARK_ERR_NO_TARGET = -4,  /* L1 term or confidence head requested without a teacher */
   DSPARK_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than dspark_workspace_size() */
   DSPARK_ERR_ALIGN = -6,      /* a device pointer is not 16-byte aligned */
-  DSPARK_ERR_HIP = -7         /* a HIP launch failed; see dspark_last_hip_error() */
+  DSPARK_ERR_HIP = -7,        /* a HIP launch failed; see dspark_last_hip_error() */
+  DSPARK_ERR_SCRATCH = -8     /* the problem needs more than the no-allocation entry point's scratch */
 };
 
 /* Bits of dspark_shape.options; an unknown bit makes the shape invalid
@@ -231,6 +232,29 @@ int dspark_confidence_logits(int64_t rows, int64_t draft_hidden, int64_t target_
                              const uint8_t *valid_mask, const void *markov_w1,
                              const void *conf_w, const void *conf_b, float *out,
                              void *workspace, size_t workspace_bytes, dspark_stream_t stream);
+
+/* ---- no-allocation variant (for callers that cannot allocate) ---------------
+ * For code under HIP graph capture, tight serving loops and harnesses that
+ * forbid hipMalloc: dspark_confidence_logits with its workspace replaced by a
+ * library-owned device array of DSPARK_NOALLOC_SCRATCH_BYTES per GPU (a
+ * file-scope __device__ array, present on every GPU the library runs on until
+ * the process ends; nothing is allocated or freed by the call).  Same
+ * arguments, results and errors as dspark_confidence_logits without
+ * workspace / workspace_bytes; a problem whose workspace
+ * (dspark_confidence_logits_workspace_size) exceeds the scratch returns
+ * DSPARK_ERR_SCRATCH (with bf16 and markov rank 256: up to about 32000 rows).
+ * The stream must belong to the current device.  Every call on one GPU uses
+ * that GPU's one scratch array (which keeps the last call's contents; no part
+ * of it needs to start at zero): calls that overlap in time on one GPU --
+ * concurrent streams, or host threads on one device -- race and must be
+ * ordered by the caller. */
+#define DSPARK_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dspark_confidence_logits_noalloc(int64_t rows, int64_t draft_hidden, int64_t target_vocab,
+                                     int64_t markov_rank, int32_t with_markov_conf, int32_t dtype,
+                                     const void *hidden, const int32_t *prev_ids,
+                                     const uint8_t *valid_mask, const void *markov_w1,
+                                     const void *conf_w, const void *conf_b, float *out,
+                                     dspark_stream_t stream);
 
 /* ---- batch construction (the step before the loss) --------------------------
  * TorchSpec pull request #132, PR description: labels are the next tokens

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "dspark.h")
 
 DSPARK_F32, DSPARK_BF16 = 0, 1
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_NO_TARGET",
-          -5: "ERR_WORKSPACE", -6: "ERR_ALIGN", -7: "ERR_HIP"}
+          -5: "ERR_WORKSPACE", -6: "ERR_ALIGN", -7: "ERR_HIP", -8: "ERR_SCRATCH"}
 FLAG_TARGET_ID_RANGE, FLAG_PREV_ID_RANGE, FLAG_NONFINITE, FLAG_NO_TEACHER = 1, 2, 4, 8
 OPT_STORE_DRAFT_LOGITS = 1
 
@@ -93,6 +93,11 @@ def lib():
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                            C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     L.dspark_confidence_logits.restype = C.c_int
+    L.dspark_confidence_logits_noalloc.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                                   C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                                   C.c_void_p, C.c_void_p]
+    L.dspark_confidence_logits_noalloc.restype = C.c_int
     L.dspark_build_blocks.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int64] + \
         [C.c_void_p] * 9
     L.dspark_build_blocks.restype = C.c_int

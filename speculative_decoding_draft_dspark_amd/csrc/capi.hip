@@ -330,6 +330,77 @@ int shard_setup(const dspark_shape* shape, const dspark_hparams* hp, const dspar
   return DSPARK_OK;
 }
 
+// Argument checks of the confidence-head op (both entry points).
+int conf_head_check(int64_t rows, int64_t draft_hidden, int64_t target_vocab, int64_t markov_rank,
+                    int32_t with_markov_conf, int32_t dtype, const void* hidden,
+                    const int32_t* prev_ids, const void* markov_w1, const void* conf_w,
+                    const void* conf_b, const float* out) {
+  const bool wm = with_markov_conf != 0 && markov_rank > 0;
+  int st = head_dims(rows, 0, target_vocab, wm ? markov_rank : 0, dtype);
+  if (st) return st;
+  if (draft_hidden < 1 || draft_hidden > (int64_t{1} << 20)) return DSPARK_ERR_SHAPE;
+  if (!hidden || !conf_w || !conf_b || !out) return DSPARK_ERR_NULL;
+  if (wm && (!prev_ids || !markov_w1)) return DSPARK_ERR_NULL;
+  if (misaligned(hidden) || misaligned(out) || misaligned(prev_ids) || misaligned(markov_w1) ||
+      misaligned(conf_w))
+    return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+// The confidence-head launches on a checked call; `workspace` holds the
+// gathered embeddings and, when the caller passes no mask, a ones mask.
+int conf_head_launch(int64_t rows, int64_t draft_hidden, int64_t target_vocab,
+                     int64_t markov_rank, int32_t with_markov_conf, int32_t dtype,
+                     const void* hidden, const int32_t* prev_ids, const uint8_t* valid_mask,
+                     const void* markov_w1, const void* conf_w, const void* conf_b, float* out,
+                     void* workspace, hipStream_t s) {
+  const bool wm = with_markov_conf != 0 && markov_rank > 0;
+  if (rows == 0) return DSPARK_OK;
+  const size_t esize = dtype == DSPARK_BF16 ? 2 : 4;
+  const size_t eb = up(static_cast<size_t>(rows) * markov_rank * esize);
+  if (wm) {
+    // valid_mask NULL: every slot valid (a ones mask after the embeddings)
+    const uint8_t* mask = valid_mask;
+    if (!mask) {
+      char* mz = static_cast<char*>(workspace) + eb;
+      DSPARK_TRY(launch_fill_u32(mz, (rows + 3) / 4, 0x01010101u, s));
+      mask = reinterpret_cast<const uint8_t*>(mz);
+    }
+    DSPARK_TRY(launch_gather_embed(dtype, rows, markov_rank, target_vocab, prev_ids, mask,
+                                   markov_w1, workspace, s));
+  }
+  DSPARK_TRY(launch_conf_logits(dtype, rows, draft_hidden, wm ? markov_rank : 0, wm ? 1 : 0, hidden,
+                                workspace, conf_w, conf_b, valid_mask, out, s));
+  return DSPARK_OK;
+}
+
+// ---- the no-allocation entry point's scratch
+// Device memory of dspark_confidence_logits_noalloc: one array per GPU the
+// library runs on, held until the process ends.  Host code uses the address
+// hipGetSymbolAddress returns for the current device, never the array's
+// name (on the host that name is a stand-in, not a device address).
+__device__ __align__(256) unsigned char scratch[DSPARK_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_address(void** out) {
+  int dev = 0;
+  DSPARK_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return DSPARK_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DSPARK_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return DSPARK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSPARK_OK;
+}
+
 }  // namespace
 }  // namespace dspark
 
@@ -353,6 +424,8 @@ const char* dspark_status_string(int status) {
     case DSPARK_ERR_WORKSPACE: return "workspace NULL or smaller than dspark_workspace_size()";
     case DSPARK_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case DSPARK_ERR_HIP: return "HIP launch failure (see dspark_last_hip_error)";
+    case DSPARK_ERR_SCRATCH:
+      return "problem larger than the no-allocation entry point's scratch (DSPARK_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -739,36 +812,41 @@ int dspark_confidence_logits(int64_t rows, int64_t draft_hidden, int64_t target_
                              const void* conf_w, const void* conf_b, float* out,
                              void* workspace, size_t workspace_bytes, dspark_stream_t stream) {
   const bool wm = with_markov_conf != 0 && markov_rank > 0;
-  int st = head_dims(rows, 0, target_vocab, wm ? markov_rank : 0, dtype);
+  int st = conf_head_check(rows, draft_hidden, target_vocab, markov_rank, with_markov_conf, dtype,
+                           hidden, prev_ids, markov_w1, conf_w, conf_b, out);
   if (st) return st;
-  if (draft_hidden < 1 || draft_hidden > (int64_t{1} << 20)) return DSPARK_ERR_SHAPE;
-  if (!hidden || !conf_w || !conf_b || !out) return DSPARK_ERR_NULL;
-  if (wm && (!prev_ids || !markov_w1 || !workspace)) return DSPARK_ERR_NULL;
-  if (misaligned(hidden) || misaligned(out) || misaligned(prev_ids) || misaligned(markov_w1) ||
-      misaligned(conf_w) || misaligned(workspace))
-    return DSPARK_ERR_ALIGN;
-  const size_t esize = dtype == DSPARK_BF16 ? 2 : 4;
-  const size_t eb = up(static_cast<size_t>(rows) * markov_rank * esize);
+  if (wm && !workspace) return DSPARK_ERR_NULL;
+  if (misaligned(workspace)) return DSPARK_ERR_ALIGN;
   if (workspace_bytes < dspark_confidence_logits_workspace_size(rows, markov_rank,
                                                                 with_markov_conf, dtype))
     return DSPARK_ERR_WORKSPACE;
-  if (rows == 0) return DSPARK_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (wm) {
-    // valid_mask NULL: every slot valid (a ones mask after the embeddings)
-    const uint8_t* mask = valid_mask;
-    if (!mask) {
-      char* mz = static_cast<char*>(workspace) + eb;
-      DSPARK_TRY(launch_fill_u32(mz, (rows + 3) / 4, 0x01010101u, s));
-      mask = reinterpret_cast<const uint8_t*>(mz);
-    }
-    DSPARK_TRY(launch_gather_embed(dtype, rows, markov_rank, target_vocab, prev_ids, mask,
-                                   markov_w1, workspace, s));
-  }
-  DSPARK_TRY(launch_conf_logits(dtype, rows, draft_hidden, wm ? markov_rank : 0, wm ? 1 : 0, hidden,
-                                workspace, conf_w, conf_b, valid_mask, out, s));
-  return DSPARK_OK;
+  return conf_head_launch(rows, draft_hidden, target_vocab, markov_rank, with_markov_conf, dtype,
+                          hidden, prev_ids, valid_mask, markov_w1, conf_w, conf_b, out,
+                          workspace, static_cast<hipStream_t>(stream));
 }
+
+int dspark_confidence_logits_noalloc(int64_t rows, int64_t draft_hidden, int64_t target_vocab,
+                                     int64_t markov_rank, int32_t with_markov_conf, int32_t dtype,
+                                     const void* hidden, const int32_t* prev_ids,
+                                     const uint8_t* valid_mask, const void* markov_w1,
+                                     const void* conf_w, const void* conf_b, float* out,
+                                     dspark_stream_t stream) {
+  int st = conf_head_check(rows, draft_hidden, target_vocab, markov_rank, with_markov_conf, dtype,
+                           hidden, prev_ids, markov_w1, conf_w, conf_b, out);
+  if (st) return st;
+  const size_t need = dspark_confidence_logits_workspace_size(rows, markov_rank, with_markov_conf,
+                                                              dtype);
+  if (need > DSPARK_NOALLOC_SCRATCH_BYTES) return DSPARK_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st) return st;
+  }
+  return conf_head_launch(rows, draft_hidden, target_vocab, markov_rank, with_markov_conf, dtype,
+                          hidden, prev_ids, valid_mask, markov_w1, conf_w, conf_b, out, ws,
+                          static_cast<hipStream_t>(stream));
+}
+
 
 int dspark_build_blocks(int64_t batch, int64_t seq_len, int64_t num_blocks, int64_t block_size,
                         const int32_t* input_ids, const uint8_t* loss_mask,

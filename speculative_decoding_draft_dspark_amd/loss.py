@@ -305,6 +305,32 @@ def confidence_logits(draft_hidden: torch.Tensor, conf_w: torch.Tensor, conf_b: 
     return out.reshape(draft_hidden.shape[:-1])
 
 
+def confidence_logits_noalloc(draft_hidden: torch.Tensor, conf_w: torch.Tensor,
+                              conf_b: torch.Tensor, prev_ids: Optional[torch.Tensor] = None,
+                              markov_w1: Optional[torch.Tensor] = None,
+                              valid_mask: Optional[torch.Tensor] = None,
+                              with_markov: bool = False, out: Optional[torch.Tensor] = None,
+                              stream=None) -> torch.Tensor:
+    """``dspark_confidence_logits_noalloc``: as ``confidence_logits``, with the
+    library's per-GPU scratch array in place of a workspace (the library
+    allocates nothing; pass ``out`` to allocate nothing here either)."""
+    h = draft_hidden.reshape(-1, draft_hidden.shape[-1])
+    rows, Hd = h.shape
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    Vt = 0 if markov_w1 is None else markov_w1.shape[0]
+    dt = _DT[h.dtype]
+    mask = _u8_mask(None if valid_mask is None else valid_mask.reshape(-1))
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=h.device)
+    pid = None if prev_ids is None else prev_ids.reshape(-1)
+    st = capi.lib().dspark_confidence_logits_noalloc(rows, Hd, Vt, r, int(with_markov), dt,
+                                                     _ptr(h), _ptr(pid), _ptr(mask),
+                                                     _ptr(markov_w1), _ptr(conf_w), _ptr(conf_b),
+                                                     _ptr(out), _stream(stream))
+    capi.check(st, "dspark_confidence_logits_noalloc")
+    return out.reshape(draft_hidden.shape[:-1])
+
+
 def dspark_loss(b: DSparkBatch, hp: HParams = HParams(), **kw):
     """The API page's 3-tuple: (loss numerator, num_tokens, {metric: [num, den]})."""
     f = dspark_loss_fwd(b, hp, **kw)

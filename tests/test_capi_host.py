@@ -173,6 +173,20 @@ def test_head_ops_validation_codes(L):
                                       fake, fake, fake, cw, None) == E["ERR_NULL"]
     assert L.dspark_confidence_logits(100, 32, 600, 64, 1, 1, fake, fake, None, fake, fake,
                                       fake, fake, fake, cw - 1, None) == E["ERR_WORKSPACE"]
+    # the no-allocation variant: same checks, and a problem beyond its scratch
+    # (bf16 rank 256: 40000 rows need 20.5 MB of embeddings) is rejected up front
+    na = L.dspark_confidence_logits_noalloc
+    assert na(100, 0, 600, 64, 1, 1, fake, fake, None, fake, fake, fake, fake, None) == \
+        E["ERR_SHAPE"]
+    assert na(100, 32, 600, 64, 1, 1, None, fake, None, fake, fake, fake, fake, None) == \
+        E["ERR_NULL"]
+    assert na(100, 32, 600, 64, 1, 1, fake, None, None, fake, fake, fake, fake, None) == \
+        E["ERR_NULL"]
+    assert na(100, 32, 600, 64, 1, 1, fake, fake, None, fake, fake, fake, C.c_void_p(4100),
+              None) == E["ERR_ALIGN"]
+    assert L.dspark_confidence_logits_workspace_size(40000, 256, 1, 1) > 16 << 20
+    assert na(40000, 32, 600, 256, 1, 1, fake, fake, None, fake, fake, fake, fake, None) == \
+        E["ERR_SCRATCH"]
 
 
 def test_build_blocks_validation_codes(L):
