@@ -24,7 +24,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
-def _gpu_leg(args):
+def _gpu_leg(args, workload=None):
     import torch
 
     from speculative_decoding_draft_dspark_amd import (DSparkBatch, HParams, _capi,
@@ -33,7 +33,7 @@ def _gpu_leg(args):
     from workloads import get_workload, make_inputs
 
     _capi.lib()  # fail loudly without the HIP library
-    wl = get_workload(args.workload)
+    wl = get_workload(workload or args.workload)
     dev = "cuda:0"
     t0 = time.time()
     d = make_inputs(wl, dev)
@@ -68,8 +68,11 @@ def _gpu_leg(args):
     _capi.profile_enable(False)
     loss = f.loss.item()
     flags = int(f.flags.item())
-    print(f"[bench] {args.steps} steps in {elapsed:.3f}s, loss numerator {loss:.4f}, "
-          f"flags {flags}", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: {args.steps} steps in {elapsed:.3f}s, loss numerator "
+          f"{loss:.4f}, flags {flags}", file=sys.stderr, flush=True)
+    del b, d, ws, fwd, grads, f
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return wl, elapsed, stages
 
 
@@ -266,6 +269,9 @@ def main():
     ap.add_argument("--workload", default="large-batch-r14336-v151936")
     ap.add_argument("--cpu-blocks", type=int, default=72)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", nargs="*", default=["qwen3-8b-r1792-v151936"],
+                    help="further workloads timed after the headline one, reported in "
+                         "other_workloads (default: the Qwen3-8B-shaped workload)")
     ap.add_argument("--store-draft-logits", action="store_true",
                     help="DSPARK_OPT_STORE_DRAFT_LOGITS: materialise the fp32 corrected draft "
                          "logits instead of recomputing the Markov bias in each sweep")
@@ -293,6 +299,44 @@ def main():
         _vocab_shard(args)
         return
     wl, elapsed, stages = _gpu_leg(args)
+    summary = _summary(args, wl, elapsed, stages)
+    roofline, sweeps, stage_ms = summary["roofline"], summary["sweeps"], summary["stage_ms"]
+    ms_step, rows_per_s = summary["ms_per_step"], summary["rows_per_s"]
+    R, V, H, r = wl.R, wl.Vd, wl.H, wl.r
+    # the other V = 151936 workload the metric names, as an extra block
+    others = {}
+    for name in args.also:
+        owl, oel, ost = _gpu_leg(args, name)
+        others[owl.name] = _summary(args, owl, oel, ost)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_leg(wl, args.cpu_blocks)
+
+    line = {
+        "metric": "DSpark loss fwd+bwd rows/s at V=151936",
+        "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded workloads package)",
+        "config": {"workload": wl.name, "rows": R, "batch": wl.B, "num_blocks": wl.N,
+                   "block_size": wl.K, "draft_vocab": V, "target_vocab": wl.Vt, "hidden": H,
+                   "markov_rank": r, "confidence_head": "with_markov", "gamma": wl.gamma,
+                   "parallelism": "single GPU",
+                   "corrected_draft_logits": ("stored fp32" if args.store_draft_logits
+                                              else "recomputed per sweep")},
+        "roofline": roofline,
+        "sweeps": sweeps,
+        "stage_ms": stage_ms,
+        "other_workloads": others,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _summary(args, wl, elapsed, stages):
+    """rows/s, the teacher projection against the bf16 MFMA peak, the sweeps
+    against the HBM peak, and per-stage milliseconds of one workload's run."""
     R, V, H, r = wl.R, wl.Vd, wl.H, wl.r
     ms_step = 1000.0 * elapsed / args.steps
     rows_per_s = R * args.steps / elapsed
@@ -309,7 +353,8 @@ def main():
     roofline = {"bound": "mfma", "kernel": kname,
                 "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if stored else _traffic("logits_gemm"),
+                "traffic": (None if stored or wl.name != args.workload
+                            else _traffic("logits_gemm")),
                 "flops_per_launch": gemm_flops, "avg_ms": round(gemm_ms, 4)}
 
     # vocabulary sweeps: algorithmic HBM bytes per (row, column) / average
@@ -331,29 +376,8 @@ def main():
                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                             "bytes_per_row": bytes_per_elem * V}
     stage_ms = {k: round(v[0] / args.steps, 4) for k, v in stages.items() if v[1]}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = _cpu_leg(wl, args.cpu_blocks)
-
-    line = {
-        "metric": "DSpark loss fwd+bwd rows/s at V=151936",
-        "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded workloads package)",
-        "config": {"workload": wl.name, "rows": R, "batch": wl.B, "num_blocks": wl.N,
-                   "block_size": wl.K, "draft_vocab": V, "target_vocab": wl.Vt, "hidden": H,
-                   "markov_rank": r, "confidence_head": "with_markov", "gamma": wl.gamma,
-                   "parallelism": "single GPU",
-                   "corrected_draft_logits": ("stored fp32" if args.store_draft_logits
-                                              else "recomputed per sweep")},
-        "roofline": roofline,
-        "sweeps": sweeps,
-        "stage_ms": stage_ms,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(line), flush=True)
+    return {"rows": R, "rows_per_s": round(rows_per_s, 1), "ms_per_step": round(ms_step, 4),
+            "roofline": roofline, "sweeps": sweeps, "stage_ms": stage_ms}
 
 
 if __name__ == "__main__":

@@ -80,7 +80,16 @@ enum {
    * comparison.  Ignored where the default does not apply (fp32 inputs, other
    * ranks: the logits are always stored there) and without a Markov head
    * (the sweeps read z directly). */
-  DSPARK_OPT_STORE_DRAFT_LOGITS = 1u
+  DSPARK_OPT_STORE_DRAFT_LOGITS = 1u,
+  /* dspark_loss_bwd's d_markov_w1 (and dspark_shard_bwd_finish's): by default
+   * the rows' embedding gradients are scattered with fp32 atomics, so the
+   * order of the additions, and the last bits of rows that several slots
+   * share, vary from run to run.  This bit adds them as 64-bit fixed-point
+   * integers instead (scale from the largest term; each term rounded once to
+   * far below a float ulp of the sums), which makes d_markov_w1 bitwise
+   * reproducible; workspace + 8 Vt r bytes.  With a non-finite term the
+   * gradient falls back to the fp32 atomics (the forward flags the loss). */
+  DSPARK_OPT_DETERMINISTIC = 2u
 };
 
 /* Bits of the device word dspark_fwd_out.flags (OR-ed, never cleared by bwd). */

@@ -18,6 +18,7 @@ STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_NO
           -5: "ERR_WORKSPACE", -6: "ERR_ALIGN", -7: "ERR_HIP", -8: "ERR_SCRATCH"}
 FLAG_TARGET_ID_RANGE, FLAG_PREV_ID_RANGE, FLAG_NONFINITE, FLAG_NO_TEACHER = 1, 2, 4, 8
 OPT_STORE_DRAFT_LOGITS = 1
+OPT_DETERMINISTIC = 2
 
 
 class Shape(C.Structure):

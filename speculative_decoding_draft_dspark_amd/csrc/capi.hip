@@ -41,6 +41,7 @@ struct Dims {
   // z' = z + E W2^T (ranks the bias sweeps support, with the in-place backward)
   bool bias_path;
   int64_t bsplits;  // vocabulary splits of the bias sweeps
+  bool det;         // dW1 as fixed-point integer sums (order-independent)
 };
 
 struct Layout {
@@ -48,6 +49,7 @@ struct Layout {
   size_t pl1, ps;  // bias path: L1 / S split partials
   size_t sg;       // bias path: sign bits of p - q (L1 pass -> gradient pass)
   size_t w2t, eblk, blkhi, blklo, dw2part;  // bf16 backward operands
+  size_t dw1acc, dw1max;  // deterministic dW1: fixed-point sums, the term maximum
   size_t total;
 };
 
@@ -63,7 +65,8 @@ int make_dims(const dspark_shape* sh, Dims* d) {
   if (sh->markov_rank < 0 || sh->markov_rank % 8) return DSPARK_ERR_SHAPE;
   if (sh->hidden < 0 || sh->hidden % 8) return DSPARK_ERR_SHAPE;
   if (sh->conf_hidden < 0) return DSPARK_ERR_SHAPE;
-  if (sh->options & ~static_cast<int32_t>(DSPARK_OPT_STORE_DRAFT_LOGITS)) return DSPARK_ERR_SHAPE;
+  if (sh->options & ~static_cast<int32_t>(DSPARK_OPT_STORE_DRAFT_LOGITS | DSPARK_OPT_DETERMINISTIC))
+    return DSPARK_ERR_SHAPE;
   if (sh->markov_rank > 0 && sh->target_vocab <= 0) return DSPARK_ERR_SHAPE;
   if (sh->draft_vocab > (int64_t{1} << 26) || sh->hidden > (int64_t{1} << 20) ||
       sh->markov_rank > 4096)
@@ -116,6 +119,7 @@ int make_dims(const dspark_shape* sh, Dims* d) {
                  (!d->markov ||
                   (d->direct_bwd && (sh->options & DSPARK_OPT_STORE_DRAFT_LOGITS) == 0));
   d->bsplits = d->bias_path ? bias_grid(d->R, d->Vd).splits : 0;
+  d->det = d->markov && (sh->options & DSPARK_OPT_DETERMINISTIC) != 0;
   d->conf_chunks = d->R < 256 ? static_cast<int>(d->R) : 256;
   d->F = d->Hd + (d->conf_markov ? d->r : 0);
   d->R32 = (d->R + 31) / 32 * 32;
@@ -160,6 +164,11 @@ Layout make_layout(const Dims& d) {
   L.dEpart = o; o = up(o + static_cast<size_t>(d.splits) * d.R * d.r * 4);
   L.dE = o; o = up(o + static_cast<size_t>(d.R) * d.r * 4);
   L.confpart = o; o = up(o + static_cast<size_t>(d.conf_chunks) * (d.F + 1) * 4);
+  L.dw1acc = L.dw1max = o;
+  if (d.det) {
+    L.dw1acc = o; o = up(o + static_cast<size_t>(d.Vt) * d.r * 8);
+    L.dw1max = o; o = up(o + 4);
+  }
   L.total = o;
   return L;
 }
@@ -285,6 +294,20 @@ int check_inputs(const Dims& d, const dspark_hparams* hp, const dspark_inputs* i
   for (const void* p : ptrs)
     if (p && misaligned(p)) return DSPARK_ERR_ALIGN;
   return DSPARK_OK;
+}
+
+// dW1 = scatter of dE over the previous-token ids (zeroed first): fp32
+// atomics, or with the deterministic option fixed-point integer sums.
+hipError_t dw1_stage(const Dims& d, const Layout& L, char* ws, const int32_t* prev,
+                     const uint8_t* mask, const float* dE, float* dW1, hipStream_t s) {
+  hipError_t e = launch_fill_u32(dW1, d.Vt * d.r, 0u, s);
+  if (e != hipSuccess) return e;
+  if (!d.det) return launch_dw1_scatter(d.R, d.r, d.Vt, prev, mask, dE, dW1, s);
+  e = launch_fill_u32(ws + L.dw1acc, 2 * d.Vt * d.r, 0u, s);
+  if (e != hipSuccess) return e;
+  return launch_dw1_scatter_fixed(d.R, d.r, d.Vt, prev, mask, dE,
+                                  reinterpret_cast<float*>(ws + L.dw1max),
+                                  reinterpret_cast<unsigned long long*>(ws + L.dw1acc), dW1, s);
 }
 
 // In-place bf16 backward products (R and Vd multiples of 32).  dE partials =
@@ -597,9 +620,7 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
       DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
                                                dEpart, rs, d.conf_markov, in->conf_w, d.Hd, g,
                                                c_a, dE, s));
-      DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
-      DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
-                                            out->d_markov_w1, s));
+      DSPARK_STAGE(kDw1, dw1_stage(d, L, ws, in->prev_ids, rs.mask, dE, out->d_markov_w1, s));
       {  // dW2 over row splits, then summed
         float* part = reinterpret_cast<float*>(ws + L.dw2part);
         DSPARK_STAGE(kDw2Gemm, dw2_parts_direct(d, gA, glo, E, part, s));
@@ -635,9 +656,7 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
       DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
                                                dEpart, rs, d.conf_markov, in->conf_w, d.Hd, g,
                                                c_a, dE, s));
-      DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
-      DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
-                                            out->d_markov_w1, s));
+      DSPARK_STAGE(kDw1, dw1_stage(d, L, ws, in->prev_ids, rs.mask, dE, out->d_markov_w1, s));
       DSPARK_STAGE(kOperandPrep, launch_embed_blocked(d.R, rgroups, d.r, E, eblk, s));
       {  // dW2 = G^T . E: hi and lo segments as two splits, then summed
         float* part = reinterpret_cast<float*>(ws + L.dw2part);
@@ -675,9 +694,7 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
       DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
                                                dEpart, rs, d.conf_markov, in->conf_w, d.Hd, g,
                                                c_a, dE, s));
-      DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
-      DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
-                                            out->d_markov_w1, s));
+      DSPARK_STAGE(kDw1, dw1_stage(d, L, ws, in->prev_ids, rs.mask, dE, out->d_markov_w1, s));
       {  // dW2 = G^T . E (reduction over rows)
         Operand A{}, B{};
         A.seg[0] = A.seg[1] = gA; A.kseg = d.R; A.kpad = gemm_kpad(d.R, 4);
@@ -1071,9 +1088,7 @@ int dspark_shard_bwd_finish(const dspark_shape* shape, const dspark_hparams* hp,
     // the confidence term of dE once, on the shard-summed vocabulary term
     DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, 1, d_embed, rs, d.conf_markov,
                                              in->conf_w, d.Hd, grad_scale, c_a, dE, s));
-    DSPARK_STAGE(kDw1, launch_fill_u32(out->d_markov_w1, d.Vt * d.r, 0u, s));
-    DSPARK_STAGE(kDw1, launch_dw1_scatter(d.R, d.r, d.Vt, in->prev_ids, rs.mask, dE,
-                                          out->d_markov_w1, s));
+    DSPARK_STAGE(kDw1, dw1_stage(d, L, ws, in->prev_ids, rs.mask, dE, out->d_markov_w1, s));
   }
   if (d.conf) {
     float* part = reinterpret_cast<float*>(ws + L.confpart);

@@ -82,6 +82,11 @@ hipError_t launch_de_reduce(int dtype, int64_t R, int64_t rank, int splits, cons
                             float c_a, float* dE, hipStream_t s);
 hipError_t launch_dw1_scatter(int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
                               const uint8_t* mask, const float* dE, float* dW1, hipStream_t s);
+// Deterministic dW1 (fixed-point integer sums, see rowwise.hip): acc [Vt, r]
+// 64-bit zeroed and dW1 zeroed by the caller; maxp: one float of scratch.
+hipError_t launch_dw1_scatter_fixed(int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
+                                    const uint8_t* mask, const float* dE, float* maxp,
+                                    unsigned long long* acc, float* dW1, hipStream_t s);
 hipError_t launch_conf_bwd(int dtype, int64_t R, int64_t Hd, int64_t rank, int conf_markov,
                            const void* hd, const void* E, const void* Wc, RowState rs, float g,
                            float c_a, float* part, int chunks, float* dWc, float* db, float* dh,

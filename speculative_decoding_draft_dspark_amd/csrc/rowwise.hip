@@ -825,6 +825,92 @@ hipError_t launch_dw1_scatter(int64_t R, int64_t rank, int64_t Vt, const int32_t
   return hipGetLastError();
 }
 
+// ---- deterministic dW1: fixed-point integer sums
+// dW1[v, :] = sum of dE[r, :] over the supervised rows with prev_r = v, with
+// the terms added as 64-bit fixed-point integers: integer addition is exact
+// and associative, so the result does not depend on the order the atomics
+// land in.  The fixed-point scale comes from the largest |dE| term M = 2^e m
+// (m in [0.5, 1)): f = 62 - e - ceil(log2(R + 1)) fraction bits keep any sum of
+// at most R terms below 2^62 in magnitude, and each term is rounded once, to
+// a step of 2^-f, far below a float ulp of the sums.
+
+// *out = max |dE| over supervised rows (one workgroup; any order gives the
+// same maximum).
+__global__ __launch_bounds__(kRedThreads) void dw1_absmax_kernel(int64_t R, int64_t rank,
+                                                                 const uint8_t* mask,
+                                                                 const float* dE, float* out) {
+  __shared__ float scr[kRedThreads / kWave];
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < R * rank; i += kRedThreads) {
+    const float a = fabsf(dE[i]);
+    // NaN compares false: carry it as +inf so the caller sees a non-finite maximum
+    const float v = a == a ? a : INFINITY;
+    m = mask[i / rank] ? fmaxf(m, v) : m;
+  }
+  m = block_max<kRedThreads>(m, scr);
+  if (threadIdx.x == 0) *out = m;
+}
+
+__device__ __forceinline__ int dw1_fraction_bits(float maxabs, int64_t R) {
+  int e = 0;
+  frexpf(maxabs, &e);
+  int lr = 0;
+  while ((int64_t{1} << lr) < R + 1) ++lr;
+  return 62 - e - lr;
+}
+
+// Each supervised row's terms as fixed-point integers added into acc [Vt, r]
+// (zeroed by the caller).  A non-finite or zero maximum: plain float atomics
+// into dW1 (zeroed by the caller) instead, so NaN / Inf propagate as without
+// this mode.
+__global__ void dw1_scatter_fixed_kernel(int64_t R, int64_t rank, int64_t Vt,
+                                         const int32_t* prev, const uint8_t* mask,
+                                         const float* dE, const float* maxp,
+                                         unsigned long long* acc, float* dW1) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= R * rank) return;
+  const int64_t r = i / rank, j = i - r * rank;
+  if (!mask[r]) return;
+  const int32_t pv = prev[r];
+  if (pv < 0 || pv >= Vt) return;
+  const float mx = *maxp;
+  if (!(mx < INFINITY) || mx == 0.f) {
+    atomicAdd(dW1 + pv * rank + j, dE[i]);
+    return;
+  }
+  const int f = dw1_fraction_bits(mx, R);
+  const long long q = __double2ll_rn(ldexp(static_cast<double>(dE[i]), f));
+  atomicAdd(acc + pv * rank + j, static_cast<unsigned long long>(q));
+}
+
+// dW1 = acc 2^-f (rounded once to float), when the maximum was finite and
+// nonzero; otherwise dW1 already holds the float sums.
+__global__ void dw1_from_fixed_kernel(int64_t n, int64_t R, const unsigned long long* acc,
+                                      const float* maxp, float* dW1) {
+  const float mx = *maxp;
+  if (!(mx < INFINITY) || mx == 0.f) return;
+  const int f = dw1_fraction_bits(mx, R);
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    dW1[i] = static_cast<float>(ldexp(static_cast<double>(static_cast<long long>(acc[i])), -f));
+}
+
+hipError_t launch_dw1_scatter_fixed(int64_t R, int64_t rank, int64_t Vt, const int32_t* prev,
+                                    const uint8_t* mask, const float* dE, float* maxp,
+                                    unsigned long long* acc, float* dW1, hipStream_t s) {
+  const int64_t n = R * rank;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dw1_absmax_kernel, dim3(1), dim3(kRedThreads), 0, s, R, rank, mask, dE, maxp);
+  hipLaunchKernelGGL(dw1_scatter_fixed_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)),
+                     dim3(256), 0, s, R, rank, Vt, prev, mask, dE, maxp, acc, dW1);
+  const int64_t m = Vt * rank;
+  int64_t blocks = (m + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(dw1_from_fixed_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
+                     m, R, acc, maxp, dW1);
+  return hipGetLastError();
+}
+
 // Confidence-head gradients.  Column f of the feature [h ; e] (f < F = Hd (+ r))
 // and the bias (column F) are reduced over row chunks into part[chunk, F + 1];
 // dh[r, i] = dc_r W_c[i].

@@ -120,13 +120,14 @@ def _inputs(b: DSparkBatch) -> capi.InputsC:
                         _ptr(b.conf_b))
 
 
-def _options(store_draft_logits: bool) -> int:
-    return capi.OPT_STORE_DRAFT_LOGITS if store_draft_logits else 0
+def _options(store_draft_logits: bool, deterministic: bool = False) -> int:
+    return ((capi.OPT_STORE_DRAFT_LOGITS if store_draft_logits else 0)
+            | (capi.OPT_DETERMINISTIC if deterministic else 0))
 
 
 def dspark_workspace_size(b: DSparkBatch, grad_dtype: Optional[torch.dtype] = None,
-                          store_draft_logits: bool = False) -> int:
-    sh = make_shape(b, grad_dtype, _options(store_draft_logits))
+                          store_draft_logits: bool = False, deterministic: bool = False) -> int:
+    sh = make_shape(b, grad_dtype, _options(store_draft_logits, deterministic))
     n = capi.lib().dspark_workspace_size(C.byref(sh))
     if n == 0:
         raise capi.DSparkError("invalid shape for dspark_workspace_size")
@@ -156,13 +157,16 @@ class FwdResult:
 
 def dspark_loss_fwd(b: DSparkBatch, hp: HParams = HParams(), *, workspace=None,
                     grad_dtype: Optional[torch.dtype] = None, row_outputs: bool = True,
-                    store_draft_logits: bool = False, stream=None) -> FwdResult:
+                    store_draft_logits: bool = False, deterministic: bool = False,
+                    stream=None) -> FwdResult:
     """Forward of the DSpark loss (``dspark_loss_fwd`` of the C ABI).
 
     ``store_draft_logits`` sets DSPARK_OPT_STORE_DRAFT_LOGITS (materialise the
-    fp32 corrected draft logits instead of recomputing the Markov bias)."""
+    fp32 corrected draft logits instead of recomputing the Markov bias);
+    ``deterministic`` sets DSPARK_OPT_DETERMINISTIC (the backward's d_markov_w1
+    bitwise reproducible); both carry over to ``dspark_loss_bwd``."""
     dev = b.draft_logits.device
-    opts = _options(store_draft_logits)
+    opts = _options(store_draft_logits, deterministic)
     sh = make_shape(b, grad_dtype, opts)
     L = capi.lib()
     need = L.dspark_workspace_size(C.byref(sh))

@@ -46,9 +46,24 @@ def test_workspace_size(L):
     assert n >= 2 * R * V * 4            # fp32 teacher + corrected draft logits
     assert n % 256 == 0
     for bad in (dict(batch=0), dict(draft_vocab=1001), dict(markov_rank=12), dict(dtype=7),
-                dict(hidden=-8), dict(target_vocab=0), dict(options=2), dict(options=-1)):
+                dict(hidden=-8), dict(target_vocab=0), dict(options=4), dict(options=-1)):
         assert L.dspark_workspace_size(C.byref(_shape(**bad))) == 0, bad
     assert L.dspark_workspace_size(None) == 0
+
+
+def test_deterministic_option_adds_the_fixed_point_accumulator(L):
+    """DSPARK_OPT_DETERMINISTIC: 64-bit fixed-point sums [Vt, r] for dW1 (plus one
+    float), only with a Markov head."""
+    base = _shape()
+    det = _shape(options=2)
+    n0 = L.dspark_workspace_size(C.byref(base))
+    n1 = L.dspark_workspace_size(C.byref(det))
+    assert n1 - n0 >= 8 * base.target_vocab * base.markov_rank
+    assert n1 - n0 <= 8 * base.target_vocab * base.markov_rank + 512
+    nm = dict(markov_rank=0)
+    assert L.dspark_workspace_size(C.byref(_shape(options=2, **nm))) == \
+        L.dspark_workspace_size(C.byref(_shape(**nm)))
+    assert L.dspark_workspace_size(C.byref(_shape(options=3))) > 0
 
 
 def test_store_draft_logits_option_adds_the_corrected_logits_buffer(L):
