@@ -33,6 +33,9 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 // past the end read as zero and stores there are dropped, so every load and
 // store is issued unconditionally and the compiler's wait counts stay exact.
 constexpr uint32_t kOOB = 0xffffffffu;
+// A lane offset past every buffer that stays so with the in-instruction
+// offsets added (buffers here hold fewer than 2^31 bytes).
+constexpr uint32_t kFar = 0x80000000u;
 // Cache policy of the statistics sweep's z stream: non-temporal, so it does
 // not evict the W2 slices every row tile re-reads (measured faster there; the
 // L1 and gradient sweeps' streams measured faster with the default policy).
@@ -123,22 +126,24 @@ struct BiasEngine {
       }
     }
   }
-  // Queue W2 rows [v0, v0 + 64) into a ring stage (rows past vend read zero):
-  // the wave's p-th load fills chunks [(wave kPer + p) 64, + 64) of the stage,
-  // lane l the one at + l, i.e. row idx / CPR, slot idx % CPR, which holds
-  // chunk slot ^ (lane_of(row) & SWM).  kPer loads per thread, always issued.
+  // Queue W2 rows [v0, v0 + 64) into a ring stage.  The buffer resource ends
+  // at row vend, so rows past it read zero with no per-lane test; kPer loads
+  // per thread, always issued.
   __device__ __forceinline__ void dma(const bf16_t* W2, int64_t v0, int64_t vend, u32x4* stage) const {
     if (RANK == 0) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6;
+    const int64_t nv = vend - v0;
+    const int64_t nrow = nv <= 0 ? int64_t{0} : (nv < int64_t{kSliceV} ? nv : int64_t{kSliceV});
     const __amdgpu_buffer_rsrc_t rs =
-        rsrc_of(W2 + (v0 < vend ? v0 : 0) * RANK, kSliceV * RANK * 2);
+        rsrc_of(W2 + (nv > 0 ? v0 : int64_t{0}) * RANK, static_cast<uint32_t>(nrow * RANK * 2));
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
+      // lane l of the wave's p-th load fills chunk idx of the stage: row
+      // idx / CPR, slot idx % CPR, which holds chunk slot ^ (lane_of(row) & SWM)
       const int idx = (wave * kPer + p) * 64 + lane;
       const int v = idx / CPR, c = (idx % CPR) ^ (lane_of(v) & SWM);
-      const uint32_t off = (idx < kChunks && v0 + v < vend)
-                               ? static_cast<uint32_t>((v * RANK + 8 * c) * 2)
-                               : kOOB;
+      const uint32_t off = idx < kChunks ? static_cast<uint32_t>((v * RANK + 8 * c) * 2) : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + (wave * kPer + p) * 64), 16,
                                                off, 0, 0, 0);
     }
@@ -236,10 +241,16 @@ struct Sweep {
   bool rowok[2], sup[2];
   float lz[2], lt[2], Sr[2], cc[2], cl1[2];  // lz, lt: lse_z, lse_t times log2 e
   int yl[2];          // target column within the range, -1 if outside
-  uint32_t ebase[2];  // element offset of (row r0 + 16 rb + cl, column vb) from row r0
-  __amdgpu_buffer_rsrc_t rz, rt;      // z and T from row r0
-  __amdgpu_buffer_rsrc_t rd, rh, rl;  // dz, G hi, G lo from row r0
-  __amdgpu_buffer_rsrc_t rsg;         // the wave's sign words
+  // Per-lane element offset of (row r0 + 16 rb + cl, column 8 g) from a
+  // slice's origin (row r0, its first column); rows past R: kFar, past every
+  // buffer.  Each step builds its buffer resources at the slice's origin
+  // (scalar arithmetic), so the lane offsets never change and no load needs
+  // per-element address arithmetic; a resource ends at the end of the wave's
+  // 32 rows, so no access leaves them.
+  uint32_t eoff[2];
+  uint32_t span;      // elements from row r0 to the end of the wave's rows below R
+  uint32_t stoff;     // statistics pass: byte offset of the lane's tile store (lanes g = rb < 2)
+  int64_t orig;       // element offset of the range's origin (row r0, column vb)
   double a_l1[2], a_s[2];  // L1 pass accumulators
   uint32_t wsg[2];         // L1 pass: sign words of the slice in progress
   float c0[2];             // gradient: g w (ce_a - l1_a S); + / - g w l1_a for sign +1 / -1
@@ -256,16 +267,13 @@ struct Sweep {
     ve = (vb + P.vsplit) < P.V ? (vb + P.vsplit) : P.V;
     nsl = vb < ve ? static_cast<int>((ve - vb + kSliceV - 1) / kSliceV) : 0;
     vlen = static_cast<int>(ve > vb ? ve - vb : 0);
-    const uint32_t span = static_cast<uint32_t>(kRowsPerWave * P.V);  // elements
-    rz = rsrc_of(P.z + r0 * P.V, span * 2);
-    rt = rsrc_of(kLoadT ? P.T + r0 * P.V : P.T, kLoadT ? span * 4 : 0);
-    rsg = rsrc_of(TEACHER ? P.signs + (r0 / kRowsPerWave) * P.nstat * 64 : P.signs,
-                  TEACHER ? static_cast<uint32_t>(P.nstat * 64 * 8) : 0);
-    if (MODE == kGrad) {
-      rd = rsrc_of(static_cast<char*>(P.dz) + r0 * P.V * sizeof(GT), span * sizeof(GT));
-      rh = rsrc_of(P.ghi ? P.ghi + r0 * P.V : P.ghi, P.ghi ? span * 2 : 0);
-      rl = rsrc_of(P.glo ? P.glo + r0 * P.V : P.glo, P.glo ? span * 2 : 0);
+    {
+      const int64_t rows = P.R - r0 < kRowsPerWave ? P.R - r0 : kRowsPerWave;
+      span = rows > 0 ? static_cast<uint32_t>(rows * P.V) : 0u;
     }
+    orig = r0 * P.V + vb;
+    stoff = g < 2 && r0 + 16 * g + cl < P.R
+                ? static_cast<uint32_t>((16 * g + cl) * P.nstat * 8) : kOOB;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int64_t row = r0 + 16 * rb + cl;
@@ -289,7 +297,7 @@ struct Sweep {
         else y = t < 0 ? 0 : (t >= P.V ? P.V - 1 : t);
       }
       yl[rb] = (y >= vb && y < ve) ? static_cast<int>(y - vb) : -1;
-      ebase[rb] = static_cast<uint32_t>((16 * rb + cl) * P.V + vb);
+      eoff[rb] = rowok[rb] ? static_cast<uint32_t>((16 * rb + cl) * P.V + 8 * g) : kFar;
       a_l1[rb] = a_s[rb] = 0.0;
     }
   }
@@ -297,33 +305,54 @@ struct Sweep {
   __device__ __forceinline__ int64_t col0(int s) const { return vb + static_cast<int64_t>(s) * kSliceV; }
   __device__ __forceinline__ u32x4* stage(int t) const { return ring + (t % kStages) * Eng::kStageCh; }
 
-  // The lane's z and T of the slice at column cs of the range (columns past
-  // the range, rows past R read zero).
+  // Buffer resource over an [R, V] array from the origin of the slice at
+  // column cs of the range to the end of the wave's rows (its last row below
+  // R), so that no access leaves the array.
+  template <typename E>
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const E* base, int cs) const {
+    const uint32_t o = static_cast<uint32_t>(vb + cs);
+    return rsrc_of(base + orig + cs, span > o ? (span - o) * static_cast<uint32_t>(sizeof(E)) : 0u);
+  }
+  // The lane's byte offset for element offset eo (kFar stays past the end).
+  template <int ES>
+  __device__ __forceinline__ static uint32_t bo(uint32_t eo) {
+    return eo == kFar ? kFar : eo * ES;
+  }
+
+  // The lane's z and T of the slice at column cs of the range.  Rows past R
+  // read zero; columns past the range read the neighbouring range's values
+  // (or zero past the wave's rows), which the work on the slice masks out.
   __device__ __forceinline__ void load(SD& d, int cs) const {
+    const __amdgpu_buffer_rsrc_t rzs = slice_rsrc(P.z, cs);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        // V % 8 == 0: the lane's 8 columns are all in or all out
-        const int col = cs + 32 * h + 8 * g;
-        const bool ok = rowok[rb] && col < vlen;
-        const uint32_t e = ebase[rb] + static_cast<uint32_t>(col);
-        d.z[h][rb] = __builtin_amdgcn_raw_buffer_load_b128(rz, ok ? e * 2 : kOOB, 0,
+      for (int rb = 0; rb < 2; ++rb)
+        d.z[h][rb] = __builtin_amdgcn_raw_buffer_load_b128(rzs, bo<2>(eoff[rb]) + 64 * h, 0,
                                                            MODE == kStats ? kStream : 0);
-        if (kLoadT) {
+    if (kLoadT) {
+      const __amdgpu_buffer_rsrc_t rts = slice_rsrc(P.T, cs);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int q = 0; q < 2; ++q)
-            d.t[h][rb][q] =
-                __builtin_amdgcn_raw_buffer_load_b128(rt, ok ? (e + 4 * q) * 4 : kOOB, 0, 0);
-        }
-      }
+            d.t[h][rb][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                rts, bo<4>(eoff[rb]) + 128 * h + 16 * q, 0, 0);
+    }
     if (kLoadS) {
-      // slices past the range: an offset past the buffer, reads zeros
+      // the wave's words of slice tn: slices past the range read zeros
       const int tn = (static_cast<int>(vb) + cs) / kSliceV;
       const int lane = threadIdx.x & 63;
-      d.sg = __builtin_amdgcn_raw_buffer_load_b64(
-          rsg, cs < vlen ? static_cast<uint32_t>((tn * 64 + lane) * 8) : kOOB, 0, 0);
+      const __amdgpu_buffer_rsrc_t rs = sign_rsrc(tn);
+      d.sg = __builtin_amdgcn_raw_buffer_load_b64(rs, cs < vlen ? lane * 8u : kOOB, 0, 0);
     }
+  }
+  // The wave's sign words from slice tn on.
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t sign_rsrc(int tn) const {
+    const int64_t w = (r0 / kRowsPerWave) * P.nstat * 64 + static_cast<int64_t>(tn) * 64;
+    return rsrc_of(P.signs + w, tn < P.nstat ? static_cast<uint32_t>((P.nstat - tn) * 64 * 8) : 0u);
   }
 
   // Slice s, whose z / T are in `cur`; queues W2 of slice s + 3 into the ring
@@ -369,8 +398,8 @@ struct Sweep {
     if (MODE == kL1) {  // every slice's words, stored unconditionally
       const int tn = (static_cast<int>(vb) + cs) / kSliceV;
       const int lane = threadIdx.x & 63;
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{wsg[0], wsg[1]}, rsg,
-                                            static_cast<uint32_t>((tn * 64 + lane) * 8), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{wsg[0], wsg[1]}, sign_rsrc(tn), lane * 8u, 0,
+                                            0);
     }
   }
 
@@ -408,12 +437,11 @@ struct Sweep {
     const int rb = g & 1;
     const float2 o = rb == 0 ? out[0] : out[1];
     const int64_t tn = (vb + cs) / kSliceV;
-    const bool ok = g < 2 && (rb == 0 ? rowok[0] : rowok[1]);
     const __amdgpu_buffer_rsrc_t rs =
-        rsrc_of(P.sz + r0 * P.nstat + tn, static_cast<uint32_t>(kRowsPerWave * P.nstat * 8));
+        rsrc_of(P.sz + r0 * P.nstat + tn,
+                static_cast<uint32_t>((kRowsPerWave * P.nstat - tn) * 8));
     const u32x2 v = {__float_as_uint(o.x), __float_as_uint(o.y)};
-    __builtin_amdgcn_raw_buffer_store_b64(
-        v, rs, ok ? static_cast<uint32_t>((16 * rb + cl) * P.nstat * 8) : kOOB, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, stoff, 0, 0);
   }
 
   // The lane's column i of 8 holding the row's target, or -1.
@@ -480,25 +508,29 @@ struct Sweep {
       u32x4 hv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) hv[j] = pack_bf16x2(G[2 * j], G[2 * j + 1]);
-      const bool ok = rowok[rb] && col < vlen;
-      const uint32_t e = ebase[rb] + static_cast<uint32_t>(col);
+      // columns past the range belong to another workgroup: never written
+      const uint32_t eo = col < vlen ? eoff[rb] : kFar;
       if (sizeof(GT) == 2) {
-        __builtin_amdgcn_raw_buffer_store_b128(hv, rd, ok ? e * 2 : kOOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(hv, slice_rsrc(static_cast<GT*>(P.dz), cs),
+                                               bo<2>(eo) + 64 * h, 0, 0);
       } else {
+        const __amdgpu_buffer_rsrc_t rds = slice_rsrc(static_cast<GT*>(P.dz), cs);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const u32x4 gv = {__float_as_uint(G[4 * q]), __float_as_uint(G[4 * q + 1]),
                             __float_as_uint(G[4 * q + 2]), __float_as_uint(G[4 * q + 3])};
-          __builtin_amdgcn_raw_buffer_store_b128(gv, rd, ok ? (e + 4 * q) * 4 : kOOB, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(gv, rds, bo<4>(eo) + 128 * h + 16 * q, 0, 0);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(hv, rh, ok ? e * 2 : kOOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(hv, slice_rsrc(P.ghi, cs), bo<2>(eo) + 64 * h, 0,
+                                               0);
         if (P.glo) {  // G - hi, rounded: the second K segment of the weight products
           u32x4 lv;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             lv[j] = pack_bf16x2(G[2 * j] - __uint_as_float(hv[j] << 16),
                                 G[2 * j + 1] - __uint_as_float(hv[j] & 0xffff0000u));
-          __builtin_amdgcn_raw_buffer_store_b128(lv, rl, ok ? e * 2 : kOOB, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(lv, slice_rsrc(P.glo, cs), bo<2>(eo) + 64 * h, 0,
+                                                 0);
         }
       }
     }

@@ -105,6 +105,22 @@ def test_ragged_tiles_and_tails(dtype):
     _full_parity(d, HParams(ce_alpha=0.25, l1_alpha=0.75, confidence_alpha=0.6), TOL[dtype])
 
 
+def test_recompute_path_partial_last_slice():
+    """Bias-recompute sweeps with a vocabulary that is a multiple of 32 but not
+    of the 64-column slice (V = 800): the last slice of a range is half
+    outside it, and its columns past the range must be masked (reads) and
+    never written (dz)."""
+    wl = Workload("ragged-bf16-v800", B=1, N=32, K=7, Vd=800, Vt=907, H=40, Hd=48, r=32,
+                  dtype="bf16", seed=14, recipe="tiny")
+    say(f"[parity] {wl.name}")
+    d = make_inputs(wl, DEV)
+    d["eval_mask"][7 * 3 + 4:7 * 4] = 0
+    d["block_keep"][5] = 0
+    f, g, fw, gr = _full_parity(d, HParams(ce_alpha=0.2, l1_alpha=0.8, confidence_alpha=0.7),
+                                TOL["bf16"])
+    _assert_default_path(d, f)
+
+
 def test_confidence_hidden_not_a_multiple_of_8():
     """bf16 with Hd % 8 != 0: the confidence head's per-element paths (no
     16-byte groups) in the logit, its weight gradient and dh_d."""
