@@ -27,6 +27,7 @@ from tests.common import oracle_inputs
 from tests.gpu_common import (TOL, assert_norm, assert_scalar, compare_forward, ohp, run_gpu,
                               say, to_np)
 from workloads import Workload, get_workload, make_inputs
+from workloads.synth import subset_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +179,70 @@ def test_vocab_shards_flag_a_target_no_shard_owns():
     d["target_ids"][r] = wl.Vd + 5
     _, _, fwd, _, _ = _run_shards(d, hp, spans)
     assert int(fwd.flags.item()) & 1
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("G", [4, 8])
+def test_vocab_shards_full_vocabulary(G):
+    """G shards of the full 151936-column vocabulary on the Qwen3-8B-shaped
+    rows (widths multiples of 32, the last shard the remainder, as one rank of
+    a G-way tensor-parallel group would hold): the merged loss, row terms and
+    gradients equal the unsplit GPU path, which the full-size oracle test
+    checks; on a sample of blocks every shard's log-sum-exp parts,
+    (L1, S, z'_y) parts, dz columns and dE rows match the oracle's per-shard
+    protocol."""
+    wl = get_workload(2)
+    say(f"[shard] {wl.name} G={G} full vocabulary")
+    d = make_inputs(wl, DEV)
+    Vs = wl.Vd // G // 32 * 32
+    spans = _cuts(wl.Vd, [Vs] * (G - 1) + [wl.Vd - Vs * (G - 1)])
+    hp = HParams()
+    b, shards, fwd, per, rep = _run_shards(d, hp, spans)
+    # the unsplit GPU path
+    _, f1, g1 = run_gpu(d, hp, GS)
+    assert int(fwd.flags.item()) == int(f1.flags.item()) == 0
+    assert int(f1.num_tokens.item()) == int(fwd.num_tokens.item())
+    assert_scalar("loss vs unsplit", fwd.loss.item(), f1.loss.item(), 1e-5)
+    assert_norm("row terms vs unsplit", to_np(fwd.row_terms), to_np(f1.row_terms), 1e-5)
+    dz = torch.cat([p["d_draft_logits"] for p in per], dim=1)
+    assert_norm("dz vs unsplit", to_np(dz), to_np(g1["d_draft_logits"]), 1e-3)
+    dW2 = torch.cat([p["d_markov_w2"] for p in per], dim=0)
+    assert_norm("dW2 vs unsplit", to_np(dW2), to_np(g1["d_markov_w2"]), 1e-3)
+    assert_norm("dW1 vs unsplit", to_np(rep["d_markov_w1"]), to_np(g1["d_markov_w1"]), 1e-3)
+    assert_norm("dW_c vs unsplit", to_np(rep["d_conf_w"]), to_np(g1["d_conf_w"]), 1e-3)
+    del dz, dW2, g1, f1
+    # sampled blocks against the oracle's per-shard protocol
+    nb = wl.B * wl.N
+    blocks = np.sort(np.random.default_rng(300 + G).choice(nb, size=12, replace=False))
+    rows = (blocks[:, None] * wl.K + np.arange(wl.K)[None, :]).reshape(-1)
+    inp = oracle_inputs(subset_blocks(d, blocks))
+    tol = TOL["bf16"]
+    stats = [oshard.shard_stats(inp, v0, v1) for v0, v1 in spans]
+    lse_ref = oshard.merge_stats(stats)
+    parts = torch.stack([s.fwd_stats() for s in shards])
+    lse = merge_lse(parts)
+    torch.cuda.synchronize()
+    valid = np.isfinite(stats[0][:, 0])
+    assert valid.any()
+    for g, st in enumerate(stats):
+        got = to_np(parts[g])[rows]
+        assert np.all(np.isneginf(got[~valid])), "unsupervised rows must give -inf"
+        ref = st[valid][:, [0, 2]] + np.log(st[valid][:, [1, 3]])
+        assert_norm(f"shard {g} lse parts", got[valid], ref, 1e-5)
+    assert_norm("merged lse", to_np(lse)[rows][valid], lse_ref[valid], 1e-5)
+    terms_ref = [oshard.shard_terms(inp, v0, v1, lse_ref) for v0, v1 in spans]
+    S_ref = np.sum([t[:, 1] for t in terms_ref], axis=0)
+    y = inp.target_ids.astype(np.int64)
+    for g, (v0, v1) in enumerate(spans):
+        got = to_np(shards[g].fwd_terms(lse))[rows]
+        owned = valid & (y >= v0) & (y < v1)
+        assert np.array_equal(got[:, 3], owned.astype(np.float64)), "owner column"
+        for j, k in enumerate(("L1_g", "S_g", "z'_y")):
+            if np.any(terms_ref[g][:, j]):
+                assert_norm(f"shard {g} {k}", got[:, j], terms_ref[g][:, j], tol)
+            else:
+                assert not np.any(got[:, j]), k
+        dz_ref, dE_ref, _ = oshard.shard_grad(inp, ohp(hp), v0, v1, lse_ref, S_ref, GS)
+        assert_norm(f"shard {g} dz", to_np(per[g]["d_draft_logits"][torch.as_tensor(rows, device=DEV)]),
+                    dz_ref, tol)
+        assert_norm(f"shard {g} dE", to_np(per[g]["d_embed"])[rows], dE_ref, tol)
