@@ -162,6 +162,47 @@ def _copy_probe(nbytes: int, reps: int = 3):
                       "read_plus_write_GB/s": round(2 * n * 4 / best / 1e6, 1)}), flush=True)
 
 
+def _library_gemm(args, reps: int = 5):
+    """The vendor library's GEMM (torch.matmul, i.e. hipBLASLt) on the teacher
+    projection's shape [R, H] x [V, H]^T of the workload, as a reference point
+    for the logits kernel: bf16 output, and fp32 output where torch offers it
+    (the logits kernel writes fp32 T plus tile statistics).  Prints one JSON
+    line; not the benchmark line."""
+    import torch
+
+    from workloads import get_workload
+
+    wl = get_workload(args.workload)
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    a = torch.randn(wl.R, wl.H, device="cuda:0", generator=g).to(torch.bfloat16)
+    b = (0.02 * torch.randn(wl.Vd, wl.H, device="cuda:0", generator=g)).to(torch.bfloat16)
+    flops = 2.0 * wl.R * wl.Vd * wl.H
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {"mode": "library-gemm", "workload": wl.name, "M": wl.R, "N": wl.Vd, "K": wl.H,
+           "reps": reps}
+    ms = timed(lambda: torch.matmul(a, b.T))
+    out["bf16_out_ms"] = round(ms, 4)
+    out["bf16_out_TFLOP/s"] = round(flops / ms / 1e9, 1)
+    try:
+        ms = timed(lambda: torch.mm(a, b.T, out_dtype=torch.float32))
+        out["fp32_out_ms"] = round(ms, 4)
+        out["fp32_out_TFLOP/s"] = round(flops / ms / 1e9, 1)
+    except (TypeError, RuntimeError) as e:
+        out["fp32_out"] = f"unavailable: {type(e).__name__}"
+    print(json.dumps(out), flush=True)
+
+
 def _vocab_shard(args, reps: int = 10):
     """One tensor-parallel rank's share of the loss: the large-batch rows over
     the first of G vocabulary shards (widths multiples of 32, the last shard
@@ -280,6 +321,9 @@ def main():
     ap.add_argument("--vocab-shards", type=int, default=0, metavar="G",
                     help="only time one of G draft-vocabulary shards of the workload (one "
                          "tensor-parallel rank's share, exchanges excluded)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the vendor library GEMM on the teacher projection's shape "
+                         "(reference point for the logits kernel)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (rocprofv3 byte-counter calibration)")
     args = ap.parse_args()
@@ -294,6 +338,9 @@ def main():
         return
     if args.side_ops:
         _side_ops(args)
+        return
+    if args.library_gemm:
+        _library_gemm(args)
         return
     if args.vocab_shards:
         _vocab_shard(args)
