@@ -177,7 +177,7 @@ int dspark_loss_fwd(const dspark_shape *shape, const dspark_hparams *hp, const d
 
 /* Backward of `loss` with upstream gradient `grad_scale` (Megatron-Core scales
  * by 1 / global num_tokens).  Outputs are overwritten, not accumulated.  The
- * teacher gets no gradient (API page: the teacher is "already detached"), and
+ * teacher gets no gradient (API page: the teacher arrives detached), and
  * the BCE label is treated as a constant.  With bf16 inputs the Markov weight
  * gradients contract the logit gradient G at the precision of d_draft_logits:
  * grad_dtype bf16 -> the bf16 G that is written out (as a bf16 autograd would;
@@ -215,8 +215,8 @@ size_t dspark_markov_logits_workspace_size(int64_t rows, int64_t draft_vocab,
                                            int64_t markov_rank, int32_t dtype);
 
 /* Markov head: out [rows, draft_vocab] fp32 = z + W2 W1[prev] on valid slots
- * and 0 on the others ([HEADS] "Inputs and Outputs": the bias is added on
- * valid slots and both heads return zero for invalid ones; TorchSpec pull
+ * and 0 on the others ([HEADS] "Inputs and Outputs": the bias applies only
+ * where a slot is valid, and each head outputs zeros elsewhere; TorchSpec pull
  * request #132, "Testing": bias == W2(W1[prev])).  markov_rank 0: out = z on
  * valid slots.  z is draft_logits [rows, draft_vocab]. */
 int dspark_markov_logits(int64_t rows, int64_t draft_vocab, int64_t target_vocab,

@@ -5,9 +5,9 @@ only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` call it.  It shares no code with the HIP path.
 
 It is the plain, unchunked definition of what the method computes, written in
-float64 with numpy.  Rows are independent (the API page says chunking the rows
-"does not change the result"), so rows are visited in groups of ``row_chunk``
-only to bound host memory; each row is the textbook formula.
+float64 with numpy.  Rows are independent (per the API page, splitting the
+rows into chunks leaves the result unchanged), so rows are visited in groups
+of ``row_chunk`` only to bound host memory; each row is the textbook formula.
 
 Sources (the pages; cited by title and section):
   [API]   Megatron-Bridge API page ``bridge.training.post_training.dspark.loss``
@@ -295,7 +295,7 @@ def forward(inp: Inputs, hp: HParams, row_chunk: int = 64) -> Forward:
     """``dspark_loss`` of the [API] page, with the fused Markov / confidence heads.
 
     loss      = sum_r w_r (ce_alpha CE_r + l1_alpha L1_r + confidence_alpha BCE_r)
-                ([API] module docstring "three position-weighted terms";
+                ([API] module docstring: three terms, each weighted by position;
                 defaults 0.1 / 0.9 / 1.0 from the ``dspark_loss`` signature)
     accept_r  = clamp(1 - L1_r / 2, 0, 1)  ([API] docstring; clamp from the
                 [PR5241] merge note)
