@@ -834,21 +834,25 @@ hipError_t launch_dw1_scatter(int64_t R, int64_t rank, int64_t Vt, const int32_t
 // at most R terms below 2^62 in magnitude, and each term is rounded once, to
 // a step of 2^-f, far below a float ulp of the sums.
 
-// *out = max |dE| over supervised rows (one workgroup; any order gives the
-// same maximum).
+// *out = max |dE| over supervised rows, as the bits of a non-negative float
+// (zeroed by the caller).  Each workgroup's maximum is merged by an integer
+// atomic maximum, which orders non-negative floats as their values; any order
+// gives the same maximum.
 __global__ __launch_bounds__(kRedThreads) void dw1_absmax_kernel(int64_t R, int64_t rank,
                                                                  const uint8_t* mask,
-                                                                 const float* dE, float* out) {
+                                                                 const float* dE, unsigned* out) {
   __shared__ float scr[kRedThreads / kWave];
   float m = 0.f;
-  for (int64_t i = threadIdx.x; i < R * rank; i += kRedThreads) {
+  const int64_t n = R * rank;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kRedThreads) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kRedThreads) {
     const float a = fabsf(dE[i]);
     // NaN compares false: carry it as +inf so the caller sees a non-finite maximum
     const float v = a == a ? a : INFINITY;
     m = mask[i / rank] ? fmaxf(m, v) : m;
   }
   m = block_max<kRedThreads>(m, scr);
-  if (threadIdx.x == 0) *out = m;
+  if (threadIdx.x == 0) atomicMax(out, __float_as_uint(m));
 }
 
 __device__ __forceinline__ int dw1_fraction_bits(float maxabs, int64_t R) {
@@ -900,7 +904,12 @@ hipError_t launch_dw1_scatter_fixed(int64_t R, int64_t rank, int64_t Vt, const i
                                     unsigned long long* acc, float* dW1, hipStream_t s) {
   const int64_t n = R * rank;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(dw1_absmax_kernel, dim3(1), dim3(kRedThreads), 0, s, R, rank, mask, dE, maxp);
+  hipError_t e = launch_fill_u32(maxp, 1, 0u, s);
+  if (e != hipSuccess) return e;
+  int64_t mblocks = (n + kRedThreads - 1) / kRedThreads;
+  if (mblocks > 512) mblocks = 512;
+  hipLaunchKernelGGL(dw1_absmax_kernel, dim3(static_cast<uint32_t>(mblocks)), dim3(kRedThreads), 0,
+                     s, R, rank, mask, dE, reinterpret_cast<unsigned*>(maxp));
   hipLaunchKernelGGL(dw1_scatter_fixed_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)),
                      dim3(256), 0, s, R, rank, Vt, prev, mask, dE, maxp, acc, dW1);
   const int64_t m = Vt * rank;
