@@ -72,6 +72,20 @@ def test_small_bf16_fp32_grads(stored):
                  TOL["bf16"], grad_tol=TOL["bf16"], grad_dtype=torch.float32, stored=stored)
 
 
+@pytest.mark.parametrize("stored", [False, True], ids=["recompute", "stored"])
+def test_markov_rank_128_full_parity(stored):
+    """Markov rank 128: of the ranks the recomputing sweeps take (0, 32, 64,
+    128, 256) the one no other workload uses; full oracle parity on both
+    draft-logit paths."""
+    wl = Workload("rank128-bf16-v4096", B=1, N=32, K=7, Vd=4096, Vt=4133, H=128, Hd=136, r=128,
+                  dtype="bf16", seed=21, recipe="tiny")
+    say(f"[parity] {wl.name} stored_draft_logits={stored}")
+    d = make_inputs(wl, DEV)
+    f, _, _, _ = _full_parity(d, HParams(), TOL["bf16"], stored=stored)
+    if not stored:
+        _assert_default_path(d, f)
+
+
 def test_recompute_bias_matches_stored_path():
     """The two draft-logit paths agree with each other (beyond both meeting the oracle):
     same token count, loss within bf16 tolerance, identical flags."""
