@@ -266,11 +266,11 @@ int dspark_confidence_logits_noalloc(int64_t rows, int64_t draft_hidden, int64_t
                                      dspark_stream_t stream);
 
 /* ---- batch construction (the step before the loss) --------------------------
- * TorchSpec pull request #132, PR description: labels are the next tokens
- * (slot k of a block predicts anchor + k + 1, every slot supervised), the eval
- * mask is the contiguous supervised prefix (cumprod), the Markov previous
- * token is anchor-seeded, and an anchor needs both itself and its first
- * target to be valid.  "Valid" is the loss mask here: an anchor a is kept when
+ * TorchSpec pull request #132, PR description: slot k of a block is labelled
+ * by the token at anchor + k + 1 and every slot is supervised, the eval mask
+ * is a running product over the block (so a prefix), the Markov head's
+ * previous-token input starts from the anchor, and an anchor is drawn only
+ * where both it and its first label are valid.  "Valid" is the loss mask here: an anchor a is kept when
  * 0 <= a, a + 1 < seq_len and loss_mask[a], loss_mask[a + 1] are nonzero.
  * Inputs: input_ids [batch, seq_len] int32, loss_mask [batch, seq_len] (nonzero
  * = supervised position), anchors [batch, num_blocks] int32 (the caller's

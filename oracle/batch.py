@@ -2,13 +2,15 @@
 the loss): per sampled anchor, the block's labels, previous-token ids and
 supervision mask.  TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Source: TorchSpec pull request #132, PR description (the dspark-scoped list:
-next-token labels, every block slot supervised; contiguous-prefix eval mask by
-cumprod; anchor-seeded Markov previous token; anchor sampling that needs the
-anchor and its first target to be valid) and the review thread on the label
-offsets (slot j is labelled by the offset j + 1 from the anchor).
+Source: TorchSpec pull request #132, PR description (its list of the pieces
+specific to DSpark: each slot is labelled by the token one past it and all
+slots of a block are supervised; the eval mask is a running product, so it is
+a prefix; the Markov head's previous-token input starts from the anchor; an
+anchor is drawn only where both it and its first label are valid) and the
+review thread on the label offsets (slot j is labelled by the offset j + 1
+from the anchor).
 
-Readings where the pages are silent (the design doc lists them):
+Readings where the pages are silent:
   R22 "valid" for a position is the loss mask: an anchor a may be sampled
       when loss_mask[a] and loss_mask[a + 1] are both nonzero and a + 1 lies
       in the sequence; anchors come from the caller's sampler (random draws
@@ -65,7 +67,7 @@ def build_blocks(input_ids: np.ndarray, loss_mask: np.ndarray, anchors: np.ndarr
             for k in range(K):
                 r = (b * N + n) * K + k
                 pos = a + k + 1                      # slot k predicts anchor + k + 1
-                # anchor-seeded previous token (0 past the end, R23)
+                # previous token, starting from the anchor (0 past the end, R23)
                 prev[r] = ids[b, a + k] if a + k < L else 0
                 if pos < L:
                     target[r] = ids[b, pos]
