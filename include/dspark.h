@@ -3,11 +3,11 @@
  *
  * What is computed (the pages, cited by title and section):
  *   Megatron-Bridge API page "bridge.training.post_training.dspark.loss",
- *   module docstring and `dspark_loss`: the draft is trained with three
- *   position-weighted terms -- cross-entropy against the teacher-forced next
+ *   module docstring and `dspark_loss`: the draft's loss sums three terms,
+ *   each weighted by slot position -- cross-entropy against the teacher-forced next
  *   token, the raw probability L1 ||p_draft - p_target||_1 (no 1/2), and a
- *   confidence BCE against the label 1 - 0.5 * L1 -- each weighted by
- *   exp(-k / loss_decay_gamma); acceptance is accept = 1 - 0.5 * L1 and
+ *   confidence BCE against the label 1 - 0.5 * L1 -- each scaled by the slot
+ *   weight exp(-k / loss_decay_gamma); the acceptance accept = 1 - 0.5 * L1 and
  *   tau = sum_k cumprod(accept)_k + 1.  The loss is an unnormalised numerator,
  *   returned with the supervised token count and [numerator, denominator]
  *   report pairs (section "Return contract").
@@ -102,7 +102,7 @@ enum {
 
 typedef struct {
   int64_t batch;          /* B */
-  int64_t num_blocks;     /* N: sampled anchor blocks per sample */
+  int64_t num_blocks;     /* N: anchor blocks drawn per sequence */
   int64_t block_size;     /* K: draft positions per anchor */
   int64_t draft_vocab;    /* Vd: logits, L1 and target ids live here; multiple of 8 */
   int64_t target_vocab;   /* Vt: rows of markov_w1, range of prev ids (may differ from Vd) */

@@ -33,7 +33,7 @@ Readings where the pages are silent (each is repeated where it is used):
   R9  sign(0) = 0 in the L1 subgradient.
   R11 draft vocab may differ from target vocab; prev ids index W1 (target
       vocab), logits / L1 live in the draft vocab.
-  R13 with no teacher only CE is allowed; the L1 output is then zeros.
+  R13 with no teacher only CE is allowed, and every row's L1 is zero.
 """
 
 from __future__ import annotations
@@ -125,9 +125,9 @@ class Grads:
 def effective_mask(eval_mask, block_keep, B, N, K) -> np.ndarray:
     """Supervision mask of each slot: a contiguous, loss-enabled prefix.
 
-    [API] ``DSparkForwardOutput.eval_mask``: "a block is a contiguous,
-    in-bounds, loss-enabled prefix"; [TS132] scope list: the eval mask is the
-    contiguous prefix, realised as a cumprod.  Reading R3: the kept-anchor mask
+    [API] ``DSparkForwardOutput.eval_mask``: the supervised slots of a block
+    form a prefix (contiguous, inside the sequence, loss-enabled); [TS132]
+    scope list: that prefix is built with a cumulative product.  Reading R3: the kept-anchor mask
     (``block_keep_mask``) multiplies the whole block; a float mask counts as
     supervised where it is nonzero ([API]: "Bool/float").
     """
@@ -141,9 +141,9 @@ def effective_mask(eval_mask, block_keep, B, N, K) -> np.ndarray:
 def decay_weights(K: int, gamma: Optional[float]) -> np.ndarray:
     """Per-slot weight exp(-k / gamma); gamma None (or <= 0) disables decay.
 
-    [API] module docstring ("Each block position k is weighted by
-    exp(-k / loss_decay_gamma)") and ``_loss_weight_mask``.  Reading R2: k is
-    the 0-based slot, slot 0 being the first next-token prediction ([TS132]).
+    [API] module docstring (slot k of a block carries the weight
+    exp(-k / loss_decay_gamma)) and ``_loss_weight_mask``.  Reading R2: k is
+    the 0-based slot; slot 0 predicts the token right after the anchor ([TS132]).
     """
     k = np.arange(K, dtype=F64)
     if gamma is None or gamma <= 0:
@@ -168,8 +168,8 @@ def markov_embedding(inp: Inputs, rows: np.ndarray) -> np.ndarray:
 def draft_logits_corrected(inp: Inputs, rows: np.ndarray, e: np.ndarray) -> np.ndarray:
     """z' = z + W2 e: base logits plus the low-rank previous-token bias.
 
-    [HEADS] "Inputs and Outputs" (the head adds a low-rank previous-token bias
-    to the base logits of valid slots); [TS132] "Testing" (Markov bias ==
+    [HEADS] "Inputs and Outputs" (on a valid slot the head returns the base
+    logits plus a low-rank bias computed from the previous token); [TS132] "Testing" (Markov bias ==
     W2(W1[prev])).  W2 is ``markov_w2.weight [draft_vocab, rank]``.
     """
     z = inp.z[rows].astype(F64)
@@ -181,8 +181,8 @@ def draft_logits_corrected(inp: Inputs, rows: np.ndarray, e: np.ndarray) -> np.n
 def teacher_logits(inp: Inputs, rows: np.ndarray) -> np.ndarray:
     """Target next-token logits: lm_head applied to the target's final hidden.
 
-    [TS132] scope list (L1 distillation "against the target LM head applied to
-    its final hidden state"); [API] ``aligned_target_logits`` (the teacher may
+    [TS132] scope list (the L1 teacher is the target model's LM head on that
+    model's last hidden state); [API] ``aligned_target_logits`` (the teacher may
     also be given directly).
     """
     if inp.aligned is not None:
@@ -213,8 +213,8 @@ def sigmoid(c: np.ndarray) -> np.ndarray:
 def confidence_logit(inp: Inputs, rows: np.ndarray, e: np.ndarray) -> np.ndarray:
     """One confidence logit per slot: proj([h ; e]) + bias.
 
-    [HEADS] "Inputs and Outputs" (hidden states, plus Markov embeddings when
-    with_markov=True) and "Checkpoint Contract" (``proj.weight [1, hidden +
+    [HEADS] "Inputs and Outputs" (the head reads the hidden state, and with
+    with_markov=True also the Markov embedding) and "Checkpoint Contract" (``proj.weight [1, hidden +
     markov_rank]``, ``proj.bias [1]``; ``[1, hidden]`` when with_markov=False).
     Reading R7: the concatenation order is [hidden ; embedding].
     """
@@ -346,11 +346,12 @@ def forward(inp: Inputs, hp: HParams, row_chunk: int = 64) -> Forward:
 def accept_report(accept, eval_mask, block_keep, B, N, K):
     """Analytical acceptance diagnostics as [numerator, denominator] pairs.
 
-    [API] ``_acceptance_report``: accept_rate is the per-position acceptance
-    probability; a draft token survives only if every earlier token of its
-    block is accepted, so tau is the running product over the block plus one
-    for the verified anchor.  Reading R8: masked slots stop the product; the
-    tau pair is summed over kept blocks and counts kept blocks.
+    [API] ``_acceptance_report``: accept_rate is the probability that each
+    slot's token is accepted; a draft token is kept only when all earlier
+    tokens of its block are accepted, so per kept block tau counts the
+    verified anchor plus the cumulative products of the acceptances along the
+    block.  Reading R8: masked slots stop the product; the tau pair is summed
+    over kept blocks and counts kept blocks.
     Returns (accept_num, accept_den, tau_num, tau_den).
     """
     m = effective_mask(eval_mask, block_keep, B, N, K).reshape(B, N, K)

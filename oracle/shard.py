@@ -4,8 +4,9 @@ heads.  TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Source: NeMo-RL design doc "DSpark Auxiliary Heads", "Tensor Parallelism": the
 projection W2 is sharded over the vocabulary (axis 0) while W1 is
-replicated, and the Markov embeddings are summed across tensor-parallel
-ranks where they feed the vocabulary-sharded projection.  The loss over a
+replicated, and where the embeddings enter the projection that is split
+over the vocabulary, their contributions are summed over the tensor-parallel
+ranks.  The loss over a
 vocabulary split needs exactly these exchanges (the plain definitions of
 log-sum-exp, L1 and the gradient, taken column range by column range):
 

@@ -1,7 +1,7 @@
 """GPU parity of the standalone acceptance report (dspark_accept_report,
 through the C ABI) against the oracle's accept_report ([API]
 ``_acceptance_report``: per-slot acceptance summed over supervised slots, and
-per kept block the running product over the block plus one for the anchor).
+per kept block one for the anchor plus the cumulative acceptance products).
 
 Denominators are counts and must match exactly; numerators are fp64 sums in
 another order: 1e-12 relative.
