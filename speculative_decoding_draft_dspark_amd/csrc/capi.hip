@@ -53,8 +53,8 @@ struct Layout {
   size_t total;
 };
 
-constexpr int kRowArrays = 10;
-constexpr int64_t kCUs = 256;  // compute units of an MI355X (sizes the dE split count)  // float row arrays of RowState (w .. dcoef)
+constexpr int kRowArrays = 10;  // float row arrays of RowState (w .. dcoef)
+constexpr int64_t kCUs = 256;   // compute units of an MI355X (sizes the dE split count)
 
 int make_dims(const dspark_shape* sh, Dims* d) {
   if (!sh) return DSPARK_ERR_NULL;
