@@ -722,24 +722,25 @@ BiasGrid bias_grid(int64_t R, int64_t V) {
   constexpr int64_t kCUs = 256;
   BiasGrid gr;
   gr.row_tiles = (R + kRowsPerWG - 1) / kRowsPerWG;
-  const int64_t slices = (V + kSliceV - 1) / kSliceV;
+  const int64_t rt = gr.row_tiles > 0 ? gr.row_tiles : 1;  // callers launch nothing for R <= 0
+  const int64_t slices = V > 0 ? (V + kSliceV - 1) / kSliceV : 1;
   const int64_t maxsp = slices / 8 > 1 ? slices / 8 : 1;
   int64_t per_n[8] = {}, splits_n[8] = {};
   double fill_n[8] = {}, best = 0.0;
   for (int64_t n = 1; n <= 7; ++n) {
-    int64_t sp = n * kCUs / gr.row_tiles;
+    int64_t sp = n * kCUs / rt;
     if (sp > maxsp) sp = maxsp;
     if (sp < 1) sp = 1;
     per_n[n] = (slices + sp - 1) / sp;
     splits_n[n] = (slices + per_n[n] - 1) / per_n[n];
-    const int64_t wg = gr.row_tiles * splits_n[n];
+    const int64_t wg = rt * splits_n[n];
     fill_n[n] = static_cast<double>(wg) / static_cast<double>((wg + kCUs - 1) / kCUs * kCUs);
     if (fill_n[n] > best) best = fill_n[n];
   }
   int64_t n = 1;
   while (n < 7 && fill_n[n] < best - 0.02) ++n;
   gr.vsplit = per_n[n] * kSliceV;
-  gr.splits = (V + gr.vsplit - 1) / gr.vsplit;
+  gr.splits = V > 0 ? (V + gr.vsplit - 1) / gr.vsplit : 0;
   return gr;
 }
 
