@@ -368,15 +368,26 @@ def accept_report(accept, eval_mask, block_keep, B, N, K):
 
 # --------------------------------------------------------------------------- backward
 
-def backward(inp: Inputs, hp: HParams, grad_scale: float = 1.0, row_chunk: int = 64) -> Grads:
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """x rounded to bfloat16 (round to nearest even), back in float64."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
+
+
+def backward(inp: Inputs, hp: HParams, grad_scale: float = 1.0, row_chunk: int = 64,
+             g_bf16: bool = False) -> Grads:
     """Gradient of ``loss`` (upstream gradient ``grad_scale``) by hand.
 
     dCE/dz'_u  = p_u - [u = y]
     dL1/dz'_u  = p_u (s_u - sum_v p_v s_v),  s = sign(p - q)   (q is detached:
-                 [API] ``_ce_and_l1_per_token`` takes the teacher "already
-                 detached by the caller")
+                 [API] ``_ce_and_l1_per_token`` receives the teacher detached)
     dBCE/dc    = sigmoid(c) - accept  (label detached, R6)
     z' = z + W2 e, e = W1[prev], c = W_c [h ; e] + b_c  (chain rule).
+
+    ``g_bf16``: the Markov weight products dE = G W2 and dW2 = G^T e take G
+    rounded to bf16 (round to nearest even), as a bf16 autograd of the loss
+    would when the logit gradient is stored in bf16 (reading R19); dz itself
+    stays exact.
     """
     R, K = inp.R, inp.K
     m = effective_mask(inp.eval_mask, inp.block_keep, inp.B, inp.N, K)
@@ -404,8 +415,9 @@ def backward(inp: Inputs, hp: HParams, grad_scale: float = 1.0, row_chunk: int =
         dz[rows] = G
         dE = np.zeros_like(t["e"])
         if inp.has_markov:
-            dE = G @ inp.W2.astype(F64)
-            dW2 += G.T @ t["e"]
+            Gm = _round_bf16(G) if g_bf16 else G
+            dE = Gm @ inp.W2.astype(F64)
+            dW2 += Gm.T @ t["e"]
         if inp.has_conf:
             acc = np.clip(1.0 - 0.5 * t["l1"], 0.0, 1.0)
             cr = confidence_logit(inp, rows, t["e"])

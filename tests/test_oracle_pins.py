@@ -259,8 +259,22 @@ def test_reduces_to_plain_cross_entropy():
     assert fw.loss == pytest.approx(float(ref), rel=1e-13)
 
 
-def _torch_loss(inp, hp, grad_scale):
-    """The objective assembled from torch float64 library ops, for autograd."""
+class _RoundGradBF16(torch.autograd.Function):
+    """Identity forward; the incoming gradient rounded to bfloat16 on the way back."""
+
+    @staticmethod
+    def forward(ctx, x):
+        return x.view_as(x)
+
+    @staticmethod
+    def backward(ctx, g):
+        return g.to(torch.bfloat16).to(torch.float64)
+
+
+def _torch_loss(inp, hp, grad_scale, round_bias_grad=False):
+    """The objective assembled from torch float64 library ops, for autograd.
+    ``round_bias_grad``: the gradient reaching the Markov bias W2 e is rounded
+    to bf16 (what the weight products see when the logit gradient is bf16)."""
     B, N, K = inp.B, inp.N, inp.K
     m = torch.cumprod(torch.tensor(inp.eval_mask != 0, dtype=torch.float64).view(B, N, K), 2)
     if inp.block_keep is not None:
@@ -269,7 +283,8 @@ def _torch_loss(inp, hp, grad_scale):
     z = _t(inp.z).requires_grad_(); W1 = _t(inp.W1).requires_grad_(); W2 = _t(inp.W2).requires_grad_()
     Wc = _t(inp.W_c).requires_grad_(); bc = _t(inp.b_c).requires_grad_(); hd = _t(inp.h_d).requires_grad_()
     e = W1[torch.tensor(inp.prev_ids.astype(np.int64))]
-    zp = z + F.linear(e, W2)
+    bias = F.linear(e, W2)
+    zp = z + (_RoundGradBF16.apply(bias) if round_bias_grad else bias)
     tl = F.linear(_t(inp.H_t), _t(inp.LM))
     ce = F.cross_entropy(zp, torch.tensor(inp.target_ids.astype(np.int64)), reduction="none")
     l1 = (F.softmax(zp, -1) - F.softmax(tl, -1)).abs().sum(-1)
@@ -292,6 +307,23 @@ def test_gradients_against_torch_autograd():
     for k in ref:
         mine = getattr(gr, k)
         assert np.allclose(mine, ref[k].numpy().reshape(mine.shape), rtol=1e-10, atol=1e-14), k
+
+
+def test_bf16_logit_gradient_in_the_weight_products():
+    """Reading R19: with the logit gradient stored in bf16, the Markov weight
+    products (dE = G W2, dW2 = G^T e) take that rounded G, as torch autograd
+    does when the gradient reaching the bias is bf16; dz and the
+    confidence-head gradients are the exact ones."""
+    inp = tiny_inputs(V=37, N=4, prefix=np.array([1] * 7 + [1, 1, 1, 0, 0, 0, 0] + [1] * 7 + [1] * 7))
+    hp = HParams(ce_alpha=0.4, l1_alpha=0.6, confidence_alpha=0.9)
+    _, ref = _torch_loss(inp, hp, 0.25, round_bias_grad=True)
+    gb = oracle.backward(inp, hp, grad_scale=0.25, g_bf16=True)
+    for k in ref:
+        mine = getattr(gb, k)
+        assert np.allclose(mine, ref[k].numpy().reshape(mine.shape), rtol=1e-10, atol=1e-14), k
+    gr = oracle.backward(inp, hp, grad_scale=0.25)
+    assert np.array_equal(gb.dz, gr.dz) and np.array_equal(gb.dW_c, gr.dW_c)
+    assert not np.allclose(gb.dW2, gr.dW2, rtol=1e-6, atol=0)  # the rounding reaches dW2
 
 
 # ----------------------------------------------------------------- brute force
