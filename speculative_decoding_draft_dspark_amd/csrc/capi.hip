@@ -106,9 +106,13 @@ int make_dims(const dspark_shape* sh, Dims* d) {
       return best;
     };
     sp = pick(nM, (d->g_lo ? 2 : 1) * d->Vd / 32);
-    // dW2: two K splits (the hi and lo halves, or two halves of the rows; more
-    // splits measured slower: the partial-sum traffic outweighs the wave fill)
-    d->dw2_splits = 2 * d->R / 32 >= 16 ? 2 : 1;
+    // dW2: Vd / 256 tiles of 256 x r.  Two K splits (the hi and lo halves, or
+    // two halves of the rows) fill the waves better but add one fp32 Vd x r
+    // partial to write and sum; that pays once each half is at least 2048
+    // long (14336 rows: 1.12 ms against 1.17 ms with one; 1792 rows: 0.25 ms
+    // with one against 0.29 ms with two; three or four splits were slower).
+    const int64_t dw2_k = (d->g_lo ? 2 : 1) * d->R;
+    d->dw2_splits = dw2_k >= 4096 ? 2 : 1;
   }
   d->splits = d->markov ? sp : 0;
   // Sweeps that rebuild z' from z instead of reading a stored fp32 z': always
