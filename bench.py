@@ -82,11 +82,12 @@ def _avg_ms(stages, name, steps):
     return ms / steps if n else None
 
 
-def _traffic(kernel: str):
+def _traffic(kernel: str, workload: str):
     """HBM-side bytes per launch from the committed rocprofv3 counter summary.
 
-    None when no summary exists or the GEMM source changed since the counters
-    were taken (its SHA-256 is recorded with them).
+    None when no summary exists, when it was taken on another workload, or
+    when the GEMM source changed since the counters were taken (its SHA-256
+    is recorded with them).
     """
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
@@ -98,7 +99,9 @@ def _traffic(kernel: str):
             cur = hashlib.sha256(fh.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    return rec.get("bytes_per_launch") if rec.get("gemm_source_sha256") == cur else None
+    if rec.get("workload") != workload or rec.get("gemm_source_sha256") != cur:
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def _cpu_leg(wl, blocks: int):
@@ -400,8 +403,7 @@ def _summary(args, wl, elapsed, stages):
     roofline = {"bound": "mfma", "kernel": kname,
                 "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": (None if stored or wl.name != args.workload
-                            else _traffic("logits_gemm")),
+                "traffic": None if stored else _traffic("logits_gemm", wl.name),
                 "flops_per_launch": gemm_flops, "avg_ms": round(gemm_ms, 4)}
 
     # vocabulary sweeps: algorithmic HBM bytes per (row, column) / average

@@ -253,3 +253,19 @@ def test_vocab_shard_validation_codes(L):
     assert stats(good, lse=FAKE + 8) == E["ERR_ALIGN"]
     assert L.dspark_shard_fwd_terms(C.byref(good), C.byref(hp), C.byref(inp), FAKE, ws, FAKE,
                                     FAKE + 8, None) == E["ERR_ALIGN"]
+
+
+def test_bench_traffic_only_for_the_measured_workload():
+    """The committed HBM byte count is reported only for the workload and GEMM
+    source it was measured on."""
+    import importlib.util
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    with open(os.path.join(root, "profiles", "logits_gemm_traffic.json")) as fh:
+        rec = json.load(fh)
+    got = bench._traffic("logits_gemm", rec["workload"])
+    assert got in (None, rec["bytes_per_launch"])   # None once gemm.hip has changed
+    assert bench._traffic("logits_gemm", "qwen3-8b-r1792-v151936") is None
