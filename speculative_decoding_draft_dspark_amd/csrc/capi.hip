@@ -153,7 +153,9 @@ Layout make_layout(const Dims& d) {
     if (d.gdtype != DSPARK_BF16) { L.ghi = o; o = up(o + RV * 2); }
     if (d.g_lo) { L.glo = o; o = up(o + RV * 2); }
     if (d.markov && d.direct_bwd) {
-      L.dw2part = o; o = up(o + static_cast<size_t>(d.dw2_splits) * d.Vd * d.r * 4);
+      if (d.dw2_splits > 1) {  // one split writes dW2 itself
+        L.dw2part = o; o = up(o + static_cast<size_t>(d.dw2_splits) * d.Vd * d.r * 4);
+      }
     } else if (d.markov) {
       const size_t R32V = static_cast<size_t>(d.R32) * d.Vd;
       L.w2t = o; o = up(o + static_cast<size_t>(d.Vd) * d.r * 2);
@@ -339,6 +341,12 @@ hipError_t dw2_parts_direct(const Dims& d, const void* gA, const void* glo, cons
   B.seg[0] = B.seg[1] = E; B.kseg = d.R; B.kpad = d.R; B.ld = d.r;
   B.layout = LAYOUT_MK; B.nseg = gseg;
   return launch_gemm_w4p(3, d.Vd, d.r, A, B, static_cast<int>(d.dw2_splits), part, d.r, s);
+}
+
+// Where the in-place dW2 product writes: one split writes the fp32 gradient
+// itself; two write their partials to the workspace, summed into it after.
+float* dw2_target(const Dims& d, const Layout& L, char* ws, float* dW2) {
+  return d.dw2_splits > 1 ? reinterpret_cast<float*>(ws + L.dw2part) : dW2;
 }
 
 // Common checks of the vocabulary-shard entry points: the shape must take the
@@ -625,11 +633,12 @@ int dspark_loss_bwd(const dspark_shape* shape, const dspark_hparams* hp, const d
                                                dEpart, rs, d.conf_markov, in->conf_w, d.Hd, g,
                                                c_a, dE, s));
       DSPARK_STAGE(kDw1, dw1_stage(d, L, ws, in->prev_ids, rs.mask, dE, out->d_markov_w1, s));
-      {  // dW2 over row splits, then summed
-        float* part = reinterpret_cast<float*>(ws + L.dw2part);
+      {  // dW2 over row splits (summed when there are two)
+        float* part = dw2_target(d, L, ws, out->d_markov_w2);
         DSPARK_STAGE(kDw2Gemm, dw2_parts_direct(d, gA, glo, E, part, s));
-        DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, static_cast<int>(d.dw2_splits), part,
-                                                out->d_markov_w2, s));
+        if (d.dw2_splits > 1)
+          DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, static_cast<int>(d.dw2_splits),
+                                                  part, out->d_markov_w2, s));
       }
     } else if (d.markov) {
       DSPARK_STAGE(kGradSweep, launch_grad_sweep8(d.gdtype, d.R, rgroups, d.Vd, Zp, T,
@@ -1060,10 +1069,11 @@ int dspark_shard_bwd(const dspark_shape* shape, const dspark_hparams* hp, const 
     DSPARK_STAGE(kDeReduce, launch_de_reduce(d.dtype, d.R, d.r, static_cast<int>(d.splits),
                                              dEpart, rs, 0, nullptr, d.Hd, grad_scale, 0.f,
                                              d_embed, s));
-    float* part = reinterpret_cast<float*>(ws + L.dw2part);
+    float* part = dw2_target(d, L, ws, d_markov_w2);
     DSPARK_STAGE(kDw2Gemm, dw2_parts_direct(d, gA, glo, E, part, s));
-    DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, static_cast<int>(d.dw2_splits), part,
-                                            d_markov_w2, s));
+    if (d.dw2_splits > 1)
+      DSPARK_STAGE(kDw2Gemm, launch_sum_parts(d.Vd * d.r, static_cast<int>(d.dw2_splits), part,
+                                              d_markov_w2, s));
   }
   return DSPARK_OK;
 }

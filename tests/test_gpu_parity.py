@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import oracle
-from speculative_decoding_draft_dspark_amd import (HParams, DSparkBatch, dspark_loss_fwd,
-                                                   dspark_workspace_size)
+from speculative_decoding_draft_dspark_amd import (HParams, DSparkBatch, _capi, dspark_loss_bwd,
+                                                   dspark_loss_fwd, dspark_workspace_size)
 from tests.common import oracle_inputs
 from tests.gpu_common import (TOL, assert_grad, assert_norm, assert_scalar, compare_forward,
                               normwise, ohp, run_gpu, say, to_np)
@@ -138,6 +138,40 @@ def test_shapes_full_parity(shape):
     hp = HParams(ce_alpha=0.2 + 0.01 * N, l1_alpha=0.8, confidence_alpha=0.5 + 0.1 * B,
                  loss_decay_gamma=2.0 + B)
     _full_parity(d, hp, TOL[dtype])
+
+
+# (batch, blocks, grad dtype): the in-place dW2 product splits its row
+# contraction in two (partials summed after) once that contraction, R rows or
+# 2 R with the bf16 high + low parts of an fp32 G, reaches 4096; below, one
+# split writes dW2 directly
+_DW2_SPLIT = [(4, 152, None), (2, 160, torch.float32), (2, 64, None)]
+
+
+@pytest.mark.parametrize("shape", _DW2_SPLIT,
+                         ids=["bf16G-r4256-two", "f32G-r2240-two", "bf16G-r896-one"])
+def test_dw2_row_splits_full_parity(shape):
+    """Both dW2 launch forms of the benchmark's backward path (two row splits
+    plus their sum, or one split straight into dW2) in full against the
+    oracle; the stage's launch count shows which form ran."""
+    B, N, gdt = shape
+    wl = Workload(f"dw2split-r{7 * B * N}", B=B, N=N, K=7, Vd=2048, Vt=2065, H=64, Hd=72, r=64,
+                  dtype="bf16", seed=40 + N, recipe="small")
+    two = (2 if gdt is not None else 1) * wl.R >= 4096
+    say(f"[parity] {wl.name} grad dtype {gdt} two splits {two}")
+    d = make_inputs(wl, DEV)
+    hp = HParams()
+    b = DSparkBatch.from_workload(d)
+    f = dspark_loss_fwd(b, hp, grad_dtype=gdt)
+    torch.cuda.synchronize()
+    _capi.profile_enable(True)
+    dspark_loss_bwd(b, hp, f, GS)
+    torch.cuda.synchronize()
+    launches = _capi.profile_read()["dW2_gemm"][1]
+    _capi.profile_enable(False)
+    assert launches == (2 if two else 1), launches
+    _assert_default_path(d, f, grad_dtype=gdt)
+    tol = TOL["bf16"]
+    _full_parity(d, hp, tol, grad_tol=tol, grad_dtype=gdt)
 
 
 def test_recompute_bias_matches_stored_path():
@@ -382,7 +416,7 @@ def test_full_size_sampled_rows(idx, count, stored):
     assert p[4, 1] == wl.B * wl.N
 
 
-def _assert_default_path(d, f):
+def _assert_default_path(d, f, grad_dtype=None):
     """The launch took the benchmark's path: the Markov bias recomputed in
     every sweep, which the library takes only together with the backward
     products that read G in place.  The stored-logits option then adds the
@@ -393,8 +427,9 @@ def _assert_default_path(d, f):
     assert wl.R % 32 == 0 and wl.Vd % 32 == 0
     ws = f.workspace.numel()
     b = DSparkBatch.from_workload(d)
-    assert ws == dspark_workspace_size(b)
-    assert dspark_workspace_size(b, store_draft_logits=True) - ws >= 3 * wl.R * wl.Vd
+    assert ws == dspark_workspace_size(b, grad_dtype=grad_dtype)
+    assert (dspark_workspace_size(b, grad_dtype=grad_dtype, store_draft_logits=True) - ws
+            >= 3 * wl.R * wl.Vd)
 
 
 @pytest.mark.timeout(900)
