@@ -82,24 +82,36 @@ def _avg_ms(stages, name, steps):
     return ms / steps if n else None
 
 
+def _code_sha256(path: str) -> str:
+    """SHA-256 of a C++ source with its comments and blank lines removed and
+    runs of whitespace collapsed: a comment edit leaves it unchanged, any
+    change to the code does not."""
+    import hashlib
+    import re
+    with open(path) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = (" ".join(l.split()) for l in text.split("\n"))
+    return hashlib.sha256("\n".join(l for l in lines if l).encode()).hexdigest()
+
+
 def _traffic(kernel: str, workload: str):
     """HBM-side bytes per launch from the committed rocprofv3 counter summary.
 
     None when no summary exists, when it was taken on another workload, or
-    when the GEMM source changed since the counters were taken (its SHA-256
-    is recorded with them).
+    when the GEMM code changed since the counters were taken (the hash of
+    gemm.hip's code is recorded with them).
     """
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
     src = os.path.join(ROOT, "speculative_decoding_draft_dspark_amd", "csrc", "gemm.hip")
     try:
         with open(path) as fh:
             rec = json.load(fh)
-        with open(src, "rb") as fh:
-            cur = hashlib.sha256(fh.read()).hexdigest()
+        cur = _code_sha256(src)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("gemm_source_sha256") != cur:
+    if rec.get("workload") != workload or rec.get("gemm_code_sha256") != cur:
         return None
     return rec.get("bytes_per_launch")
 

@@ -1282,12 +1282,13 @@ hipError_t launch_gemm(int dtype, int epi, int tag, int64_t M, int64_t N, const 
                     : launch_t<float>(epi, tag, M, N, A, B, splits, ep, s);
 }
 
-// The logits projections of the forward pass: the corrected draft logits
-// (K = markov rank, memory-bound: the 8-wave kernel, whose epilogue overlaps
-// other workgroups' work) and then the teacher logits (K = hidden: the
-// persistent 4-wave kernel).  Both epilogues compute the tile statistics the
-// same way (maximum; fixed-point exp-sum), so equal rows give equal results.
-// Where the bf16 DMA paths do not apply, both jobs take the generic kernel.
+// The logits projections of the stored-logits forward pass and of the
+// Markov head op: the corrected draft logits (K = markov rank, z as the
+// epilogue addend) and then the teacher logits (K = hidden), each a launch of
+// the persistent 4-wave kernel.  Both epilogues compute the tile statistics
+// the same way (maximum; fixed-point exp-sum), so equal rows give equal
+// results.  Where the bf16 DMA paths do not apply, both jobs take the
+// generic kernel.
 hipError_t launch_logits(int dtype, int64_t M, int64_t N, const Operand* A, const Operand* B,
                          const EpiParams* ep, int njobs, hipStream_t s) {
   if (M <= 0 || N <= 0 || njobs <= 0) return hipSuccess;

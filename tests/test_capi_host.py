@@ -267,5 +267,21 @@ def test_bench_traffic_only_for_the_measured_workload():
     with open(os.path.join(root, "profiles", "logits_gemm_traffic.json")) as fh:
         rec = json.load(fh)
     got = bench._traffic("logits_gemm", rec["workload"])
-    assert got in (None, rec["bytes_per_launch"])   # None once gemm.hip has changed
+    assert got in (None, rec["bytes_per_launch"])   # None once gemm.hip's code has changed
     assert bench._traffic("logits_gemm", "qwen3-8b-r1792-v151936") is None
+
+
+def test_bench_code_hash_ignores_comments_only(tmp_path):
+    """The GEMM code hash behind the byte count: comment and whitespace edits
+    keep it, a code edit changes it."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod2", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text("int f(int x) {\n  return x + 1;  // one\n}\n")
+    b.write_text("/* header */\nint f(int x) {\n\n  // a note\n  return  x + 1;\n}\n")
+    c.write_text("int f(int x) {\n  return x + 2;  // one\n}\n")
+    assert bench._code_sha256(str(a)) == bench._code_sha256(str(b))
+    assert bench._code_sha256(str(a)) != bench._code_sha256(str(c))
