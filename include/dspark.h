@@ -210,7 +210,9 @@ int dspark_accept_report(int64_t batch, int64_t num_blocks, int64_t block_size,
  * _WORKSPACE, _HIP.  Asynchronous on `stream`. */
 
 /* Bytes of workspace dspark_markov_logits needs (the gathered embeddings and
- * per-tile statistics the shared projection kernel writes). */
+ * the per-tile statistics the projection kernel writes where the op takes it
+ * instead of the sweep engine: fp32 inputs, or a rank outside {0, 32, 64,
+ * 128, 256}, or a vocabulary from 2^24 on). */
 size_t dspark_markov_logits_workspace_size(int64_t rows, int64_t draft_vocab,
                                            int64_t markov_rank, int32_t dtype);
 

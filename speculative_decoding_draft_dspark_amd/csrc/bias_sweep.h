@@ -61,6 +61,12 @@ hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, 
                             float l1_a, void* dz, bf16_t* ghi, bf16_t* glo, hipStream_t s,
                             int shard = 0);
 
+// z' = z + E . W2^T into out [R, V] (fp32), zero rows where valid[row] == 0
+// (valid null: every row written): the Markov head op on the sweep path.
+hipError_t launch_bias_store(int64_t R, int64_t V, int64_t rank, const bf16_t* z,
+                             const bf16_t* E, const bf16_t* W2, const uint8_t* valid, float* out,
+                             hipStream_t s);
+
 // Vocabulary shard: part [R, 4] (fp64) = this shard's L1, S and, on the shard
 // that owns the target, z'_y and 1 (0 and 0 on the others and on unsupervised
 // rows).

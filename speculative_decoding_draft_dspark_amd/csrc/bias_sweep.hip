@@ -1,9 +1,10 @@
 // Vocabulary sweeps that recompute the Markov bias of the corrected draft
 // logits z' = z + E . W2^T (NeMo-RL "DSpark Auxiliary Heads", Inputs and
-// Outputs) slice by slice, so z' is never written to memory: the softmax
+// Outputs) slice by slice, so the loss never writes z' to memory: the softmax
 // statistics of z' (the first pass of the loss), the L1 / S / CE pass and the
 // gradient pass (TorchSpec pull request #132, loss section: the fp32 log-softmax,
-// the probability L1 and its gradient) each read z (bf16) and rebuild z'.
+// the probability L1 and its gradient) each read z (bf16) and rebuild z'.  A
+// fourth pass stores z' itself (fp32) for the standalone Markov head op.
 //
 // Work split: a workgroup of 8 waves owns 256 rows and one range of the
 // vocabulary; each wave owns 32 rows (two MFMA row blocks of 16).  The wave
@@ -51,7 +52,7 @@ constexpr int kSliceV = 64;  // vocabulary rows of W2 per slice (4 MFMA blocks o
 static_assert(kSliceV == kStatTile, "a slice is one statistics tile");
 constexpr int kStages = 4;   // W2 slices in LDS: the one in use and three in flight
 
-enum SweepMode { kStats = 0, kL1 = 1, kGrad = 2 };
+enum SweepMode { kStats = 0, kL1 = 1, kGrad = 2, kStore = 3 };
 
 __device__ __forceinline__ void lds_sync() {
   // order LDS accesses only (no wait on outstanding global loads or stores)
@@ -212,6 +213,8 @@ struct SweepParams {
   bf16_t* glo;
   float g, ce_a, l1_a;
   int shard;  // vocabulary shard: a target id outside [0, V) lives in another shard
+  float* zout;           // store pass: z' [R, V] fp32
+  const uint8_t* valid;  // store pass: rows to write (null: all); the others get zeros
 };
 
 // State of one sweep over a workgroup's 256 rows and vocabulary range.
@@ -226,7 +229,8 @@ struct Sweep {
   static constexpr int kZT = 4 + (kLoadT ? 8 : 0) + (kLoadS ? 1 : 0);  // loads per lane per slice
   // stores issued unconditionally per slice: the statistics tile, the sign
   // words, or dz (bf16: one per (h, rb); fp32: two, plus G hi)
-  static constexpr int kST = MODE == kStats ? 1 : (MODE == kL1 ? 1 : (sizeof(GT) == 2 ? 4 : 12));
+  static constexpr int kST = MODE == kStats || MODE == kL1 ? 1
+                             : (MODE == kStore ? 8 : (sizeof(GT) == 2 ? 4 : 12));
   // slices of z / T in flight ahead of the one in use: 2 without T, 1 with T
   // (three register sets of z and T would not fit two waves per SIMD)
   static constexpr int kLead = kLoadT ? 1 : 2;
@@ -278,10 +282,13 @@ struct Sweep {
     for (int rb = 0; rb < 2; ++rb) {
       const int64_t row = r0 + 16 * rb + cl;
       rowok[rb] = row < P.R;
-      sup[rb] = MODE != kStats && rowok[rb] && P.rs.mask[row] != 0;
+      if (MODE == kStore)
+        sup[rb] = rowok[rb] && (P.valid == nullptr || P.valid[row] != 0);
+      else
+        sup[rb] = MODE != kStats && rowok[rb] && P.rs.mask[row] != 0;
       lz[rb] = lt[rb] = Sr[rb] = cc[rb] = cl1[rb] = c0[rb] = 0.f;
       int64_t y = -1;
-      if (MODE != kStats && sup[rb]) {
+      if (MODE != kStats && MODE != kStore && sup[rb]) {
         // exp(x - lse) as exp2(x log2 e - lse log2 e): one fma per element
         lz[rb] = P.rs.lse_z[row] * kLog2e;
         lt[rb] = P.rs.lse_t[row] * kLog2e;
@@ -393,6 +400,7 @@ struct Sweep {
         for (int i = 0; i < 8; ++i) zp[h][rb][i] = acc[i >> 2][rb][i & 3];
       if (MODE == kL1) l1_work(cs, h, cur, zp[h]);
       if (MODE == kGrad) grad_work(cs, h, cur, zp[h]);
+      if (MODE == kStore) store_work(cs, h, zp[h]);
     }
     if (MODE == kStats) stats_work(cs, zp);
     if (MODE == kL1) {  // every slice's words, stored unconditionally
@@ -532,6 +540,26 @@ struct Sweep {
           __builtin_amdgcn_raw_buffer_store_b128(lv, slice_rsrc(P.glo, cs), bo<2>(eo) + 64 * h, 0,
                                                  0);
         }
+      }
+    }
+  }
+
+  // Store pass on block pair h: z' of the lane's 8 columns as fp32 (zeros on
+  // rows the caller marks invalid); columns past the range belong to another
+  // workgroup and rows past R to no one: never written.
+  __device__ __forceinline__ void store_work(int cs, int h, const float (&zh)[2][8]) {
+    const __amdgpu_buffer_rsrc_t ro = slice_rsrc(P.zout, cs);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int col = cs + 32 * h + 8 * g;  // within the range
+      const uint32_t eo = col < vlen ? eoff[rb] : kFar;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4 v = {sup[rb] ? __float_as_uint(zh[rb][4 * q]) : 0u,
+                         sup[rb] ? __float_as_uint(zh[rb][4 * q + 1]) : 0u,
+                         sup[rb] ? __float_as_uint(zh[rb][4 * q + 2]) : 0u,
+                         sup[rb] ? __float_as_uint(zh[rb][4 * q + 3]) : 0u};
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, bo<4>(eo) + 128 * h + 16 * q, 0, 0);
       }
     }
   }
@@ -786,6 +814,16 @@ hipError_t launch_bias_l1_shard(int64_t R, int64_t V, int64_t rank, int splits, 
                      dim3(kFinishWaves * kWave), 0,
                      s, R, V, rank, splits, has_teacher, part_l1, part_s, z, E, W2, tid, rs, part);
   return hipGetLastError();
+}
+
+hipError_t launch_bias_store(int64_t R, int64_t V, int64_t rank, const bf16_t* z,
+                             const bf16_t* E, const bf16_t* W2, const uint8_t* valid, float* out,
+                             hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  SweepParams P = base_params(R, V, z, E, W2);
+  P.zout = out;
+  P.valid = valid;
+  return launch_mode<kStore, false, float>(rank, bias_grid(R, V), P, s);
 }
 
 hipError_t launch_bias_grad(int grad_dtype, int64_t R, int64_t V, int64_t rank, const bf16_t* z,

@@ -809,8 +809,18 @@ int dspark_markov_logits(int64_t rows, int64_t draft_vocab, int64_t target_vocab
     DSPARK_TRY(launch_gather_embed(dtype, rows, markov_rank, target_vocab, prev_ids, mask,
                                    markov_w1, ws + L.E, s));
   }
-  // z' = z + E W2^T: the loss's logits projection with z as the epilogue
-  // addend (K = 0 without a Markov head: z' = z)
+  if (dtype == DSPARK_BF16 && bias_sweep_ok(draft_vocab, markov_rank)) {
+    // the loss's sweep engine in its store pass: the bias rebuilt slice by
+    // slice on the rows' E, z' written in fp32 and invalid rows as zeros
+    DSPARK_TRY(launch_bias_store(rows, draft_vocab, markov_rank,
+                                 static_cast<const bf16_t*>(draft_logits),
+                                 markov_rank > 0 ? reinterpret_cast<const bf16_t*>(ws + L.E)
+                                                 : nullptr,
+                                 static_cast<const bf16_t*>(markov_w2), valid_mask, out, s));
+    return DSPARK_OK;
+  }
+  // elsewhere z' = z + E W2^T is the loss's logits projection with z as the
+  // epilogue addend (K = 0 without a Markov head: z' = z)
   Operand A{}, B{};
   A.seg[0] = A.seg[1] = ws + L.E; A.kseg = markov_rank;
   A.kpad = gemm_kpad(markov_rank, esize); A.ld = markov_rank; A.layout = LAYOUT_KC; A.nseg = 1;

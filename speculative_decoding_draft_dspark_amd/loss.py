@@ -266,7 +266,8 @@ def markov_logits(draft_logits: torch.Tensor, prev_ids: Optional[torch.Tensor] =
                   markov_w2: Optional[torch.Tensor] = None,
                   valid_mask: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """``dspark_markov_logits``: the Markov head's corrected logits (fp32)
-    z + W2 W1[prev] on valid slots, z elsewhere; no head (W1 None): z."""
+    z + W2 W1[prev] on valid slots, zero rows on the others; no head (W1
+    None): z on valid slots."""
     z = draft_logits.reshape(-1, draft_logits.shape[-1])
     rows, V = z.shape
     r = 0 if markov_w1 is None else markov_w1.shape[1]

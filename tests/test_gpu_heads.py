@@ -37,21 +37,25 @@ def _f64(t):
     return t.to(torch.float64).numpy()
 
 
-@pytest.mark.parametrize("dtype,rank", [("bf16", 64), ("bf16", 24), ("f32", 32), ("bf16", 0),
-                                        ("f32", 0)])
-def test_markov_logits_parity(dtype, rank):
-    # rows and vocabulary not multiples of the 256 x 256 tiles (ragged tails);
-    # rank 64 takes the LDS-DMA projection kernel, 24 and fp32 the generic one
-    R, V, Vt = 200, 1000, 777
-    g = torch.Generator().manual_seed(11 + rank)
-    say(f"[heads] markov logits {dtype} R={R} V={V} rank={rank}")
+@pytest.mark.parametrize("dtype,rank,masked,R", [
+    ("bf16", 64, True, 200), ("bf16", 24, True, 200), ("f32", 32, True, 200),
+    ("bf16", 0, True, 200), ("f32", 0, True, 200), ("bf16", 256, True, 600),
+    ("bf16", 128, False, 200), ("bf16", 96, True, 200), ("bf16", 32, False, 300)])
+def test_markov_logits_parity(dtype, rank, masked, R):
+    # rows and vocabulary not multiples of the 256-row workgroups or the
+    # 64-column slices (ragged tails); bf16 with rank 0, 32, 64, 128 or 256
+    # takes the sweep engine's store pass, bf16 rank 96 the LDS-DMA projection
+    # kernel, rank 24 and fp32 the generic one; without a mask every row is valid
+    V, Vt = 1000, 777
+    g = torch.Generator().manual_seed(11 + rank + R)
+    say(f"[heads] markov logits {dtype} R={R} V={V} rank={rank} masked={masked}")
     z = _rand((R, V), 2.0, dtype, g)
     prev = torch.randint(0, Vt, (R,), generator=g, dtype=torch.int32)
-    valid = (torch.rand(R, generator=g) > 0.25).to(torch.uint8)
+    valid = ((torch.rand(R, generator=g) > 0.25) if masked else torch.ones(R, dtype=torch.bool)).to(torch.uint8)
     W1 = _rand((Vt, rank), 0.5, dtype, g) if rank else None
     W2 = _rand((V, rank), 0.5, dtype, g) if rank else None
     out = markov_logits(z.to(DEV), prev.to(DEV), None if W1 is None else W1.to(DEV),
-                        None if W2 is None else W2.to(DEV), valid.to(DEV))
+                        None if W2 is None else W2.to(DEV), valid.to(DEV) if masked else None)
     got = to_np(out)
     inp = oracle.Inputs(B=1, N=1, K=R, z=_f64(z), target_ids=np.zeros(R, np.int32),
                         eval_mask=valid.numpy(), prev_ids=prev.numpy(),
