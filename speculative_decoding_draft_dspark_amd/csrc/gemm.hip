@@ -7,22 +7,30 @@
 //     "DSpark Auxiliary Heads", Inputs and Outputs),
 //   - the backward products dE = G . W2 and dW2 = G^T . E.
 //
-// Two main loops share one tile order and one epilogue:
-//   * gemm_dma_kernel (bf16, both operands K-contiguous, K a multiple of 32):
-//     operand tiles go global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
-//     staging), through a 4-stage ring of BK = 32 slices prefetched 3 slices
-//     ahead, one barrier per slice.  This is the lm_head / logits path.
+// Four kernels share the tile order (XCD-aware groups: each of the 8 XCDs
+// works a contiguous range of 256 x 256 tiles, so operand slices are shared
+// through its own L2) and XOR-swizzled LDS rows of 16-byte chunks:
+//   * gemm_w4_kernel (bf16, K-contiguous operands, K a multiple of 32): the
+//     logits projections, persistent, 4 waves of 128 x 128 built from
+//     v_mfma_f32_32x32x16_bf16; operands go global -> LDS with
+//     buffer_load_dwordx4 ... lds through a 4-stage ring of BK = 32 slices;
+//     the epilogue stages the tile through two free ring stages and computes
+//     the per-row softmax statistics of every 64-column tile.
+//   * gemm_w4p_kernel (bf16): the same main loop for the backward products
+//     that read G, W2 and E in place (K-contiguous or M-contiguous operands,
+//     the latter transposed by ds_read_b64_tr_b16), split-K partial output.
+//   * gemm_dma_kernel (bf16, both operands K-contiguous or k-blocked, K a
+//     multiple of 32): 8 waves of 128 x 64 built from
+//     v_mfma_f32_16x16x32_bf16 over an LDS-DMA ring; the split-K backward
+//     products where G is not read in place (rows or draft vocabulary not
+//     multiples of 32).
 //   * gemm_kernel (fp32 or bf16, any operand layout): register-staged,
-//     double-buffered LDS; operands may be K-contiguous, M-contiguous
+//     double-buffered LDS, 8 waves of 128 x 64 (v_mfma_f32_16x16x32_bf16 or
+//     v_mfma_f32_16x16x4_f32); operands K-contiguous, M-contiguous
 //     (transposed on the way into LDS) or k-blocked ([K/c][M][c] with c
-//     elements per 16-byte chunk).
-// Both: 256 x 256 output tiles, 8 waves of 128 x 64 each built from
-// v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32; in this
-// loss the 32x32x16 form measured slower in the full GEMM); LDS rows
-// of 16-byte chunks XOR-swizzled so MFMA operand reads are conflict-free; an
-// XCD-aware grouped tile order (each of the 8 XCDs works a contiguous range so
-// operand slices are shared through its own L2).  Operands may consist of two
-// K segments (used for hi/lo splits of a bf16 gradient).
+//     elements per 16-byte chunk).  Everything the others do not take.
+// Operands may consist of two K segments (used for hi/lo splits of a bf16
+// gradient).
 #include "common.h"
 #include "internal.h"
 
@@ -581,9 +589,8 @@ __device__ __forceinline__ void dma_job(const GemmJob& J, int64_t M, int64_t N, 
 }
 
 // Up to two GEMM jobs over the same output tile grid, run back to back per
-// tile (the corrected draft logits and the teacher logits share M and N, so a
-// workgroup's memory-heavy draft epilogue overlaps other workgroups' MFMA
-// phases).  A job with K = 0 is its epilogue alone (C = X).
+// tile (launched here with one: the split-K backward partials).  A job with
+// K = 0 is its epilogue alone (C = X).
 template <int BM, int BN, int WM, int WN, int EPI, int AL, int BL, int TAG>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int64_t N,
                                                                   int64_t kper, GemmJob j0,
@@ -604,9 +611,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_dma_kernel(int64_t M, int
 // per LDS byte read of the 8-wave loop.  The MFMA takes the vocab (B)
 // fragment as its first operand, so for block (j, i) lane (h, r) = (l / 32,
 // l % 32) holds row 32 i + r of the wave tile at columns 32 j + 8 q + 4 h ..
-// + 3 in elements 4 q .. 4 q + 3: 16-byte stores straight from the
-// accumulators, and a row's softmax statistics need one shuffle and one
-// exchange between the two waves that share the row.  Operands stream
+// + 3 in elements 4 q .. 4 q + 3 (16-byte pieces of 4 columns; the logits
+// epilogue regroups them by row through LDS, the backward partials store
+// them as they are).  Operands stream
 // through an LDS-DMA ring (4 stages of 32-wide K slices); each wave reads the
 // next slice's fragments into a second register set while its MFMAs run,
 // since with one wave per SIMD no other wave hides LDS latency.
