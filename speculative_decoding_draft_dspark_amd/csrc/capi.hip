@@ -26,7 +26,7 @@ inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Dims {
   int64_t B, N, K, R, Vd, Vt, H, Hd, r, nstat, splits, conf_chunks, F;
   int64_t R32;  // R rounded up to a multiple of 32 (k-blocked row operands)
-  int64_t dw2_splits;  // K splits of the in-place dW2 product (hi and lo rows)
+  int64_t dw2_splits;  // K splits of the in-place dW2 product: 1, or 2 (hi and lo, or row halves)
   int dtype, gdtype, esize;
   bool markov, conf, conf_markov;
   // bf16 backward products read G, W2 and E in place (row counts and the
