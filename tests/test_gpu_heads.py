@@ -112,3 +112,39 @@ def test_confidence_head_matches_the_loss_logits():
     terms = f.row_terms
     assert terms is not None
     assert np.array_equal(c.cpu().numpy(), terms[:, 3].cpu().numpy())
+
+
+@pytest.mark.timeout(600)
+def test_markov_logits_full_size_sampled_rows():
+    """The Markov head op at the large-batch shapes (14336 rows, vocabulary
+    151936, rank 256, bf16: every row tile and vocabulary range of the sweep
+    grid) on sampled rows against the oracle, with a mask; invalid rows exactly
+    zero everywhere."""
+    wl = get_workload(3)
+    R, V, Vt, r = wl.R, wl.Vd, wl.Vt, wl.r
+    say(f"[heads] markov logits full size R={R} V={V} rank={r}")
+    d = make_inputs(wl, DEV)
+    g = torch.Generator().manual_seed(7)
+    p = d["prev_ids"].cpu()
+    # valid slots hold in-range previous tokens (the loss's masked rows may not)
+    valid = ((torch.rand(R, generator=g) > 0.2) & (p >= 0) & (p < Vt)).to(torch.uint8)
+    out = markov_logits(d["z"], d["prev_ids"], d["W1"], d["W2"], valid.to(DEV))
+    torch.cuda.synchronize()
+    v = valid.numpy().astype(bool)
+    inval = torch.from_numpy(~v).to(DEV)
+    assert not bool(out[inval].any().item())
+    # first and last rows of the batch, both sides of each 256-row tile edge,
+    # and random rows
+    rows = sorted(set([0, 1, R - 1, R - 2, 255, 256, 4095, 4096, 8191, 8192]
+                      + torch.randint(0, R, (22,), generator=g).tolist()))
+    idx = torch.tensor(rows, dtype=torch.long)
+    got = out[idx.to(DEV)].double().cpu().numpy()
+    z = d["z"][idx.to(DEV)].double().cpu().numpy()
+    prev = d["prev_ids"][idx.to(DEV)].cpu().numpy()
+    inp = oracle.Inputs(B=1, N=1, K=len(rows), z=z, target_ids=np.zeros(len(rows), np.int32),
+                        eval_mask=valid.numpy()[rows], prev_ids=prev,
+                        W1=d["W1"].double().cpu().numpy(), W2=d["W2"].double().cpu().numpy())
+    ref = oracle.markov_head_logits(inp, valid.numpy()[rows])
+    err = normwise(got, ref)
+    assert err <= HEAD_TOL, f"z' normwise rel err {err:.3e} on rows {rows}"
+    assert np.all(np.abs(got - ref) <= HEAD_TOL * (1.0 + np.abs(ref)))
