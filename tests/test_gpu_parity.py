@@ -174,6 +174,22 @@ def test_dw2_row_splits_full_parity(shape):
     _full_parity(d, hp, tol, grad_tol=tol, grad_dtype=gdt)
 
 
+@pytest.mark.timeout(900)
+def test_max_vocabulary_full_parity():
+    """A draft vocabulary of 2^22 (4194304; the sweeps take vocabularies below
+    2^24, each wave's 32 rows of fp32 teacher logits then span 512 MB of
+    32-bit buffer offsets) over 32 rows, on the benchmark's launch path, in
+    full against the oracle: 256 vocabulary ranges of 256 slices for the
+    sweeps, 16384 vocabulary tiles for the projection and dW2, the largest
+    split count for dE."""
+    wl = Workload("maxvocab-v4194304", B=1, N=8, K=4, Vd=1 << 22, Vt=(1 << 22) + 17, H=64, Hd=72,
+                  r=32, dtype="bf16", seed=77, recipe="small")
+    say(f"[parity] {wl.name} R={wl.R}")
+    d = make_inputs(wl, DEV)
+    f, _, _, _ = _full_parity(d, HParams(), TOL["bf16"], row_chunk=8)
+    _assert_default_path(d, f)
+
+
 def test_recompute_bias_matches_stored_path():
     """The two draft-logit paths agree with each other (beyond both meeting the oracle):
     same token count, loss within bf16 tolerance, identical flags."""
@@ -419,17 +435,21 @@ def test_full_size_sampled_rows(idx, count, stored):
 def _assert_default_path(d, f, grad_dtype=None):
     """The launch took the benchmark's path: the Markov bias recomputed in
     every sweep, which the library takes only together with the backward
-    products that read G in place.  The stored-logits option then adds the
-    4 R Vd bytes of fp32 corrected logits to the workspace (less the R Vd / 4
-    of sign bits it does not need); where it does not apply it changes
-    nothing, so a smaller default workspace shows the path."""
+    products that read G in place.  That path has a z' statistics stage
+    (bias_stats) the stored-logits path does not have: a forward on the same
+    default-sized workspace under the stage timers must run it once."""
     wl = d["workload"]
     assert wl.R % 32 == 0 and wl.Vd % 32 == 0
-    ws = f.workspace.numel()
     b = DSparkBatch.from_workload(d)
-    assert ws == dspark_workspace_size(b, grad_dtype=grad_dtype)
-    assert (dspark_workspace_size(b, grad_dtype=grad_dtype, store_draft_logits=True) - ws
-            >= 3 * wl.R * wl.Vd)
+    assert f.workspace.numel() == dspark_workspace_size(b, grad_dtype=grad_dtype)
+    _capi.profile_enable(True)
+    try:
+        dspark_loss_fwd(b, HParams(), grad_dtype=grad_dtype, workspace=f.workspace)
+        torch.cuda.synchronize()
+        st = _capi.profile_read()
+    finally:
+        _capi.profile_enable(False)
+    assert st["bias_stats"][1] == 1 and st["logits_gemm"][1] == 1, st
 
 
 @pytest.mark.timeout(900)
