@@ -174,6 +174,19 @@ def test_dw2_row_splits_full_parity(shape):
     _full_parity(d, hp, tol, grad_tol=tol, grad_dtype=gdt)
 
 
+@pytest.mark.parametrize("K,N", [(1, 64), (2, 48), (16, 8)], ids=["k1", "k2", "k16"])
+def test_block_sizes_full_parity(K, N):
+    """Block sizes other than 7: single-token blocks (decay weight 1 and tau
+    accept + 1 on every block), two tokens, and 16 (long decay tails and
+    prefix masks); rows a multiple of 32, so the benchmark's launch path."""
+    wl = Workload(f"blk{K}-bf16-v2048", B=2, N=N, K=K, Vd=2048, Vt=2065, H=64, Hd=72, r=64,
+                  dtype="bf16", seed=50 + K, recipe="small")
+    say(f"[parity] {wl.name} R={wl.R}")
+    d = make_inputs(wl, DEV)
+    f, _, _, _ = _full_parity(d, HParams(loss_decay_gamma=3.0), TOL["bf16"])
+    _assert_default_path(d, f)
+
+
 @pytest.mark.timeout(900)
 def test_max_vocabulary_full_parity():
     """A draft vocabulary of 2^22 (4194304; the sweeps take vocabularies below
