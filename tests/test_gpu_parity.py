@@ -187,6 +187,19 @@ def test_block_sizes_full_parity(K, N):
     _assert_default_path(d, f)
 
 
+@pytest.mark.parametrize("V", [32, 64, 96])
+def test_smallest_vocabularies_full_parity(V):
+    """Draft vocabularies of half a slice, one slice and one and a half
+    (32, 64, 96 columns: one vocabulary range, a single statistics tile or a
+    ragged second one) on the benchmark's launch path."""
+    wl = Workload(f"tinyvocab-bf16-v{V}", B=1, N=32, K=7, Vd=V, Vt=V + 9, H=64, Hd=72, r=32,
+                  dtype="bf16", seed=60 + V, recipe="small")
+    say(f"[parity] {wl.name} R={wl.R}")
+    d = make_inputs(wl, DEV)
+    f, _, _, _ = _full_parity(d, HParams(), TOL["bf16"])
+    _assert_default_path(d, f)
+
+
 @pytest.mark.timeout(900)
 def test_max_vocabulary_full_parity():
     """A draft vocabulary of 2^22 (4194304; the sweeps take vocabularies below
