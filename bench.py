@@ -99,7 +99,7 @@ def _code_sha256(path: str) -> str:
 def _traffic(kernel: str, workload: str):
     """HBM-side bytes per launch from the committed rocprofv3 counter summary.
 
-    None when no summary exists, when it was taken on another workload, or
+    None when no summary exists, when none was taken on this workload, or
     when the GEMM code changed since the counters were taken (the hash of
     gemm.hip's code is recorded with them).
     """
@@ -111,9 +111,9 @@ def _traffic(kernel: str, workload: str):
         cur = _code_sha256(src)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("gemm_code_sha256") != cur:
+    if rec.get("gemm_code_sha256") != cur:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_launch", {}).get(workload)
 
 
 def _cpu_leg(wl, blocks: int):

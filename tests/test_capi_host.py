@@ -256,8 +256,8 @@ def test_vocab_shard_validation_codes(L):
 
 
 def test_bench_traffic_only_for_the_measured_workload():
-    """The committed HBM byte count is reported only for the workload and GEMM
-    source it was measured on."""
+    """The committed HBM byte counts are reported only for the workloads and
+    GEMM code they were measured on."""
     import importlib.util
     import json
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -266,9 +266,10 @@ def test_bench_traffic_only_for_the_measured_workload():
     spec.loader.exec_module(bench)
     with open(os.path.join(root, "profiles", "logits_gemm_traffic.json")) as fh:
         rec = json.load(fh)
-    got = bench._traffic("logits_gemm", rec["workload"])
-    assert got in (None, rec["bytes_per_launch"])   # None once gemm.hip's code has changed
-    assert bench._traffic("logits_gemm", "qwen3-8b-r1792-v151936") is None
+    for name, n in rec["bytes_per_launch"].items():
+        got = bench._traffic("logits_gemm", name)
+        assert got in (None, n)   # None once gemm.hip's code has changed
+    assert bench._traffic("logits_gemm", "tiny-fp32-r28-v1024") is None
 
 
 def test_bench_code_hash_ignores_comments_only(tmp_path):
