@@ -15,8 +15,9 @@
 // over the rank, with the W2 fragment as the first operand, so each fragment
 // read from LDS feeds two MFMAs.  The W2 rows of a block are permuted so that
 // lane (g, cl) ends up with the 8 consecutive columns 32 h + 8 g .. + 7 of
-// its row for each block pair h: z (bf16) arrives as one 16-byte load per
-// (h, row block), T (fp32) as two.  z, widened to fp32, is the initial
+// its row for each block pair h: z (bf16) is one 16-byte chunk per
+// (h, row block), loaded in whole lines and moved to its lane by a row
+// rotation outside the L1 pass, and T (fp32) two.  z, widened to fp32, is the initial
 // accumulator of the MFMA chains, so they end at z' itself.  Every sweep
 // computes z' with the same instruction sequence, so all three see the same
 // values.  A slice is one softmax-statistics tile (64 columns).
@@ -179,7 +180,8 @@ struct BiasEngine {
 };
 
 // The lane's z (bf16), T (fp32, L1 pass) and sign bits (gradient pass) of
-// one slice: per block pair h and row block rb, the 8 columns 32 h + 8 g .. + 7.
+// one slice: per block pair h and row block rb, the 8 columns 32 h + 8 g .. + 7
+// (z as loaded in whole lines until Sweep::fix() has run).
 template <bool LOADT, bool LOADS>
 struct SliceData {
   u32x4 z[2][2];
@@ -234,6 +236,7 @@ struct Sweep {
   // slices of z / T in flight ahead of the one in use: 2 without T, 1 with T
   // (three register sets of z and T would not fit two waves per SIMD)
   static constexpr int kLead = kLoadT ? 1 : 2;
+  static constexpr bool kWholeLines = MODE != kL1;  // z loads in whole lines
   const SweepParams& P;
   u32x4* ring;  // kStages x Eng::kStageCh
   Eng eng;
@@ -252,6 +255,10 @@ struct Sweep {
   // per-element address arithmetic; a resource ends at the end of the wave's
   // 32 rows, so no access leaves them.
   uint32_t eoff[2];
+  // whole-line z loads: byte offset of load p of row block rb from a slice's
+  // origin; hi = lane bit 3 (the second half of the lane's 16-lane row)
+  uint32_t zoff[2][2];
+  bool hi;
   uint32_t span;      // elements from row r0 to the end of the wave's rows below R
   uint32_t stoff;     // statistics pass: byte offset of the lane's tile store (lanes g = rb < 2)
   int64_t orig;       // element offset of the range's origin (row r0, column vb)
@@ -264,6 +271,7 @@ struct Sweep {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     g = lane >> 4;
     cl = lane & 15;
+    hi = (lane & 8) != 0;
     // wave-uniform, so the buffer resources built from it are scalar and no
     // load or store needs a waterfall loop
     r0 = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + wave * kRowsPerWave;
@@ -305,6 +313,14 @@ struct Sweep {
       }
       yl[rb] = (y >= vb && y < ve) ? static_cast<int>(y - vb) : -1;
       eoff[rb] = rowok[rb] ? static_cast<uint32_t>((16 * rb + cl) * P.V + 8 * g) : kFar;
+      {
+        // lane 16 g + 8 k + r: load 0 brings row r of the block, chunk
+        // 4 k + g; load 1 row 8 + r, chunk 4 (1 - k) + g.  Rows past R lie
+        // past the slice's buffer resource and read zero.
+        const int r = lane & 7, k = (lane >> 3) & 1;
+        zoff[0][rb] = static_cast<uint32_t>(((16 * rb + r) * P.V + 8 * (4 * k + g)) * 2);
+        zoff[1][rb] = static_cast<uint32_t>(((16 * rb + 8 + r) * P.V + 8 * (4 * (1 - k) + g)) * 2);
+      }
       a_l1[rb] = a_s[rb] = 0.0;
     }
   }
@@ -330,13 +346,19 @@ struct Sweep {
   // read zero; columns past the range read the neighbouring range's values
   // (or zero past the wave's rows), which the work on the slice masks out.
   __device__ __forceinline__ void load(SD& d, int cs) const {
+    // Outside the L1 pass z comes in whole 128-byte lines (8 rows x 8
+    // chunks of 16 bytes per load; load p of row block rb covers its rows
+    // 8 p .. 8 p + 7) and fix() moves each chunk to the lane that computes on
+    // it; the L1 pass, whose T loads dominate and whose registers are full,
+    // loads each lane's own chunks (16 rows x 64 bytes per load).
     const __amdgpu_buffer_rsrc_t rzs = slice_rsrc(P.z, cs);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        d.z[h][rb] = __builtin_amdgcn_raw_buffer_load_b128(rzs, bo<2>(eoff[rb]) + 64 * h, 0,
-                                                           MODE == kStats ? kStream : 0);
+        d.z[p][rb] = __builtin_amdgcn_raw_buffer_load_b128(
+            rzs, kWholeLines ? zoff[p][rb] : bo<2>(eoff[rb]) + 64 * p, 0,
+            MODE == kStats ? kStream : 0);
     if (kLoadT) {
       const __amdgpu_buffer_rsrc_t rts = slice_rsrc(P.T, cs);
 #pragma unroll
@@ -368,7 +390,29 @@ struct Sweep {
   // wait on loads still in flight.  Loads past the range read zeros and are
   // always issued, and the per-element conditions are selects, so every wait
   // count is static.
-  __device__ __forceinline__ void step(int s, const SD& cur, SD& nxt) {
+  // The two whole-line loads of a row block into each lane's own chunks
+  // (block pair 0 in a, 1 in b).  The low half of a 16-lane row holds its own
+  // pair-0 chunk in a, the high half in b; each half's other load holds the
+  // pair-1 chunk of the lane 8 away in the same row (row_ror:8).
+  __device__ __forceinline__ void fix_pair(u32x4& a, u32x4& b) const {
+    u32x4 own, other;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      own[j] = hi ? b[j] : a[j];
+      const uint32_t x = hi ? a[j] : b[j];
+      other[j] = static_cast<uint32_t>(
+          __builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x128, 0xf, 0xf, false));
+    }
+    a = own;
+    b = other;
+  }
+  __device__ __forceinline__ void fix(SD& d) const {
+    if (!kWholeLines) return;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) fix_pair(d.z[0][rb], d.z[1][rb]);
+  }
+
+  __device__ __forceinline__ void step(int s, SD& cur, SD& nxt) {
     // W2 of slice s landed: it was queued in step s - 3 (the prologue drains
     // its own), followed by that step's z / T loads and stores and two more
     // steps' DMA, loads and stores.  The vector memory counter retires loads
@@ -386,6 +430,7 @@ struct Sweep {
     int cs = __builtin_amdgcn_readfirstlane(s * kSliceV);
     asm volatile("" : "+s"(cs));
     load(nxt, cs + kLead * kSliceV);
+    fix(cur);
     float zp[2][2][8];  // [h][rb][column]
     wsg[0] = wsg[1] = 0u;
 #pragma unroll
