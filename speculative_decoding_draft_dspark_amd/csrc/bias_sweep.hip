@@ -265,6 +265,7 @@ struct Sweep {
   double a_l1[2], a_s[2];  // L1 pass accumulators
   uint32_t wsg[2];         // L1 pass: sign words of the slice in progress
   float c0[2];             // gradient: g w (ce_a - l1_a S); + / - g w l1_a for sign +1 / -1
+  u32x4 dzv[2][2];         // gradient, bf16 dz: the lane's chunk per (block pair, row block)
 
   __device__ __forceinline__ Sweep(const SweepParams& p, u32x4* rg) : P(p), ring(rg) {
     const int lane = threadIdx.x & 63;
@@ -406,6 +407,37 @@ struct Sweep {
     a = own;
     b = other;
   }
+  // The inverse of fix_pair: the lanes' own chunks a (block pair 0) and b
+  // (block pair 1) of a row block into the two whole-line stores (rows 0..7
+  // and 8..15 of the block, as loaded).
+  __device__ __forceinline__ void unfix_pair(const u32x4& a, const u32x4& b, u32x4& lo,
+                                             u32x4& up) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t y = static_cast<uint32_t>(
+          __builtin_amdgcn_update_dpp(0, static_cast<int>(b[j]), 0x128, 0xf, 0xf, false));
+      lo[j] = hi ? y : a[j];
+      up[j] = hi ? a[j] : y;
+    }
+  }
+  // bf16 dz of the slice in whole 128-byte lines (the layout of the whole-line
+  // z loads); a chunk whose columns lie past the range belongs to another
+  // workgroup and is not written, rows past R lie past the buffer.
+  __device__ __forceinline__ void store_dz(int cs) {
+    const __amdgpu_buffer_rsrc_t rd = slice_rsrc(static_cast<bf16_t*>(P.dz), cs);
+    const int k = hi ? 1 : 0;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      u32x4 v[2];
+      unfix_pair(dzv[0][rb], dzv[1][rb], v[0], v[1]);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int c = p == 0 ? 4 * k + g : 4 * (1 - k) + g;  // the chunk this lane stores
+        __builtin_amdgcn_raw_buffer_store_b128(v[p], rd, cs + 8 * c < vlen ? zoff[p][rb] : kFar,
+                                               0, 0);
+      }
+    }
+  }
   __device__ __forceinline__ void fix(SD& d) const {
     if (!kWholeLines) return;
 #pragma unroll
@@ -448,6 +480,7 @@ struct Sweep {
       if (MODE == kStore) store_work(cs, h, zp[h]);
     }
     if (MODE == kStats) stats_work(cs, zp);
+    if (MODE == kGrad && sizeof(GT) == 2) store_dz(cs);
     if (MODE == kL1) {  // every slice's words, stored unconditionally
       const int tn = (static_cast<int>(vb) + cs) / kSliceV;
       const int lane = threadIdx.x & 63;
@@ -564,8 +597,7 @@ struct Sweep {
       // columns past the range belong to another workgroup: never written
       const uint32_t eo = col < vlen ? eoff[rb] : kFar;
       if (sizeof(GT) == 2) {
-        __builtin_amdgcn_raw_buffer_store_b128(hv, slice_rsrc(static_cast<GT*>(P.dz), cs),
-                                               bo<2>(eo) + 64 * h, 0, 0);
+        dzv[h][rb] = hv;  // stored in whole lines once both block pairs are done
       } else {
         const __amdgpu_buffer_rsrc_t rds = slice_rsrc(static_cast<GT*>(P.dz), cs);
 #pragma unroll
