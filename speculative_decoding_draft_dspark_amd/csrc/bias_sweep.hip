@@ -622,21 +622,31 @@ struct Sweep {
   }
 
   // Store pass on block pair h: z' of the lane's 8 columns as fp32 (zeros on
-  // rows the caller marks invalid); columns past the range belong to another
-  // workgroup and rows past R to no one: never written.
+  // rows the caller marks invalid), in whole 128-byte lines: the lane's two
+  // 16-byte chunks go through the inverse row rotation, so each store covers
+  // 8 rows x the pair's 32 columns.  A chunk whose columns lie past the range
+  // belongs to another workgroup and is not written; rows past R lie past
+  // the buffer.
   __device__ __forceinline__ void store_work(int cs, int h, const float (&zh)[2][8]) {
     const __amdgpu_buffer_rsrc_t ro = slice_rsrc(P.zout, cs);
+    const int lane = threadIdx.x & 63, r = lane & 7, k = hi ? 1 : 0;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const int col = cs + 32 * h + 8 * g;  // within the range
-      const uint32_t eo = col < vlen ? eoff[rb] : kFar;
+      u32x4 own[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const u32x4 v = {sup[rb] ? __float_as_uint(zh[rb][4 * q]) : 0u,
-                         sup[rb] ? __float_as_uint(zh[rb][4 * q + 1]) : 0u,
-                         sup[rb] ? __float_as_uint(zh[rb][4 * q + 2]) : 0u,
-                         sup[rb] ? __float_as_uint(zh[rb][4 * q + 3]) : 0u};
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, bo<4>(eo) + 128 * h + 16 * q, 0, 0);
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) own[q][j] = sup[rb] ? __float_as_uint(zh[rb][4 * q + j]) : 0u;
+      u32x4 v[2];
+      unfix_pair(own[0], own[1], v[0], v[1]);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int c = p == 0 ? 2 * g + k : 2 * g + 1 - k;  // chunk of the pair's line
+        const int row = 16 * rb + 8 * p + r;
+        const uint32_t off = cs + 32 * h + 4 * c < vlen
+                                 ? static_cast<uint32_t>((row * P.V + 32 * h + 4 * c) * 4)
+                                 : kFar;
+        __builtin_amdgcn_raw_buffer_store_b128(v[p], ro, off, 0, 0);
       }
     }
   }
